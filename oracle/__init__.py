@@ -1,0 +1,230 @@
+"""CPU oracle for the NVFP4 "Four-Over-Six" KV-cache smooth-quantize path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.  It is
+a thin numpy/ctypes wrapper over oracle.c (plain C, built with gcc), which
+states what each function computes and the page passage it follows.  Inputs
+are numpy arrays; bf16 tensors travel as uint16 bit patterns.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+MODE_4OVER6, MODE_FIXED6, MODE_FIXED4 = 0, 1, 2
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it with gcc first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        i, l, f, u32 = ctypes.c_int, ctypes.c_long, ctypes.c_float, ctypes.c_uint32
+        sig = {
+            "ora_e2m1_encode": (ctypes.c_uint8, [f]),
+            "ora_e2m1_decode": (f, [ctypes.c_uint8]),
+            "ora_e4m3_encode": (ctypes.c_uint8, [f]),
+            "ora_e4m3_decode": (f, [ctypes.c_uint8]),
+            "ora_float_to_bf16": (ctypes.c_uint16, [f]),
+            "ora_bf16_to_float": (f, [ctypes.c_uint16]),
+            "ora_kv_mean": (i, [P, i, i, i, i, P, i]),
+            "ora_rht16": (None, [P, l, u32, P]),
+            "ora_quantize_chunks": (i, [P, i, i, i, i, i, P, i, u32, P, P, P, P, P, P, i]),
+            "ora_quantize_2d": (i, [P, i, i, i, P, P, P, P, P, P, i]),
+            "ora_dequantize": (i, [P, P, P, P, i, i, i, i, P, i]),
+            "ora_dequantize_2d": (i, [P, P, P, i, i, P]),
+            "ora_e2m1_encode_array": (None, [P, l, P, i]),
+            "ora_e4m3_encode_array": (None, [P, l, P, i]),
+            "ora_float_to_bf16_array": (None, [P, l, P, i]),
+            "ora_e2m1_decode_array": (None, [P, l, P, i]),
+            "ora_e4m3_decode_array": (None, [P, l, P, i]),
+            "ora_candidate_codes": (None, [P, l, f, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+# ---- codecs --------------------------------------------------------------
+
+def e2m1_encode(y, nthreads=0):
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().ora_e2m1_encode_array(_ptr(y), y.size, _ptr(out), nthreads)
+    return out
+
+
+def e2m1_decode(q, nthreads=0):
+    q = _c(q, np.uint8)
+    out = np.empty(q.shape, np.float32)
+    lib().ora_e2m1_decode_array(_ptr(q), q.size, _ptr(out), nthreads)
+    return out
+
+
+def e4m3_encode(r, nthreads=0):
+    r = _c(r, np.float32)
+    out = np.empty(r.shape, np.uint8)
+    lib().ora_e4m3_encode_array(_ptr(r), r.size, _ptr(out), nthreads)
+    return out
+
+
+def e4m3_decode(s, nthreads=0):
+    s = _c(s, np.uint8)
+    out = np.empty(s.shape, np.float32)
+    lib().ora_e4m3_decode_array(_ptr(s), s.size, _ptr(out), nthreads)
+    return out
+
+
+def float_to_bf16(x, nthreads=0):
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().ora_float_to_bf16_array(_ptr(x), x.size, _ptr(out), nthreads)
+    return out
+
+
+def bf16_to_float(h):
+    h = _c(h, np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def candidate_codes(t, c):
+    """E4M3 code of t / c (IEEE fp32 division), as the quantizer forms a candidate."""
+    t = _c(t, np.float32)
+    out = np.empty(t.shape, np.uint8)
+    lib().ora_candidate_codes(_ptr(t), t.size, float(c), _ptr(out))
+    return out
+
+
+def rht16(x, sign_mask):
+    """16-point random-sign Hadamard transform of each row of x [n, 16] (fp32)."""
+    x = _c(x, np.float32).reshape(-1, 16)
+    out = np.empty_like(x)
+    lib().ora_rht16(_ptr(x), x.shape[0], int(sign_mask) & 0xFFFF, _ptr(out))
+    return out
+
+
+# ---- the path ------------------------------------------------------------
+
+def kv_mean(x, chunk_len, nthreads=0):
+    """Per-chunk channel mean of x [H, T, D] (bf16 bits) -> float32 [T/L, H, D]."""
+    x = _c(x, np.uint16)
+    H, T, D = x.shape
+    out = np.empty((T // chunk_len, H, D), np.float32)
+    _check(lib().ora_kv_mean(_ptr(x), H, T, D, chunk_len, _ptr(out), nthreads), "kv_mean")
+    return out
+
+
+def quantize_chunks(x, chunk_len, mode=MODE_4OVER6, mean=None, hadamard=False, sign_mask=0,
+                    want_errors=False, nthreads=0):
+    """Quantize x [H, T, D] (bf16 bits) chunk by chunk; see ora_quantize_chunks."""
+    x = _c(x, np.uint16)
+    H, T, D = x.shape
+    nc = T // chunk_len
+    codes = np.empty((H, T, D // 2), np.uint8)
+    scales = np.empty((H, T, D // 16), np.uint8)
+    ts = np.empty((nc,), np.float32)
+    e6 = np.empty((H, T, D // 16), np.float32) if want_errors else None
+    e4 = np.empty((H, T, D // 16), np.float32) if want_errors else None
+    n4 = ctypes.c_longlong(0)
+    m = None if mean is None else _c(mean, np.float32)
+    rc = lib().ora_quantize_chunks(_ptr(x), H, T, D, chunk_len, mode, _ptr(m), int(bool(hadamard)),
+                                   int(sign_mask) & 0xFFFF, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(e6),
+                                   _ptr(e4), ctypes.byref(n4), nthreads)
+    _check(rc, "quantize_chunks")
+    out = {"codes": codes, "scales": scales, "tensor_scale": ts, "use4": int(n4.value)}
+    if want_errors:
+        out["err6"], out["err4"] = e6, e4
+    return out
+
+
+def smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, k_mean=None, want_errors=False, nthreads=0):
+    """The KV step: per-chunk K mean (or the given one), smoothed K and raw V
+    quantized per chunk.  Returns the same outputs as the GPU entry point."""
+    if k_mean is None:
+        k_mean = kv_mean(k, chunk_len, nthreads)
+    qk = quantize_chunks(k, chunk_len, mode, mean=k_mean, want_errors=want_errors, nthreads=nthreads)
+    qv = quantize_chunks(v, chunk_len, mode, mean=None, want_errors=want_errors, nthreads=nthreads)
+    out = {"k_codes": qk["codes"], "v_codes": qv["codes"], "k_scales": qk["scales"], "v_scales": qv["scales"],
+           "k_tensor_scale": qk["tensor_scale"], "v_tensor_scale": qv["tensor_scale"],
+           "k_mean": np.asarray(k_mean, np.float32), "k_use4": qk["use4"], "v_use4": qv["use4"]}
+    if want_errors:
+        out.update(k_err6=qk["err6"], k_err4=qk["err4"], v_err6=qv["err6"], v_err4=qv["err4"])
+    return out
+
+
+def dequantize(codes, scales, tensor_scale, mean, chunk_len, nthreads=0):
+    """codes [H, T, D/2], scales [H, T, D/16] -> bf16 bits [H, T, D]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    ts = _c(tensor_scale, np.float32)
+    m = None if mean is None else _c(mean, np.float32)
+    H, T, D2 = codes.shape
+    D = 2 * D2
+    out = np.empty((H, T, D), np.uint16)
+    _check(lib().ora_dequantize(_ptr(codes), _ptr(scales), _ptr(ts), _ptr(m), H, T, D, chunk_len, _ptr(out),
+                                nthreads), "dequantize")
+    return out
+
+
+def quantize_1d(x, mode=MODE_4OVER6, hadamard=False, sign_mask=0, want_errors=False, nthreads=0):
+    """Activation path: x [rows, cols] (bf16 bits), 1D blocks along cols, one
+    tensor scale, optional RHT first.  codes [rows, cols/2], scales [rows, cols/16]."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    r = quantize_chunks(x.reshape(1, rows, cols), rows, mode, None, hadamard, sign_mask, want_errors, nthreads)
+    out = {"codes": r["codes"][0], "scales": r["scales"][0], "tensor_scale": r["tensor_scale"], "use4": r["use4"]}
+    if want_errors:
+        out["err6"], out["err4"] = r["err6"][0], r["err4"][0]
+    return out
+
+
+def quantize_2d(w, mode=MODE_4OVER6, want_errors=False, nthreads=0):
+    """Weight path: w [rows, cols] (bf16 bits), 16x16 tiles.  codes [rows, cols/2],
+    scales [rows/16, cols/16], tensor_scale [1]."""
+    w = _c(w, np.uint16)
+    rows, cols = w.shape
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows // 16, cols // 16), np.uint8)
+    ts = np.empty((1,), np.float32)
+    e6 = np.empty((rows // 16, cols // 16), np.float32) if want_errors else None
+    e4 = np.empty((rows // 16, cols // 16), np.float32) if want_errors else None
+    n4 = ctypes.c_longlong(0)
+    _check(lib().ora_quantize_2d(_ptr(w), rows, cols, mode, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(e6), _ptr(e4),
+                                 ctypes.byref(n4), nthreads), "quantize_2d")
+    out = {"codes": codes, "scales": scales, "tensor_scale": ts, "use4": int(n4.value)}
+    if want_errors:
+        out["err6"], out["err4"] = e6, e4
+    return out
+
+
+def dequantize_2d(codes, scales, tensor_scale):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    ts = _c(tensor_scale, np.float32)
+    rows, c2 = codes.shape
+    out = np.empty((rows, 2 * c2), np.uint16)
+    _check(lib().ora_dequantize_2d(_ptr(codes), _ptr(scales), _ptr(ts), rows, 2 * c2, _ptr(out)), "dequantize_2d")
+    return out

@@ -1,0 +1,443 @@
+"""Pins of the oracle's quantizer, smoothing, RHT and dequant against what the
+page and the mathematics fix: hand-derived worked examples of the 4/6 rule,
+exact-arithmetic brute force of the best-of-two choice, closed forms,
+invariants, and library routines (torch's fp8 / bf16 casts, scipy's Hadamard
+matrix)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(x):
+    return W.bf16_bits(torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16))
+
+
+def _torch_e4m3(r):
+    return torch.from_numpy(np.ascontiguousarray(r, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _unpack(codes):
+    lo, hi = codes & 15, codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+
+
+# ------------------------------------------------------- worked examples ----
+
+def test_worked_examples_from_the_75_percent_claim():
+    ex = json.load(open(os.path.join(GOLDEN, "four_over_six_examples.json")))
+    row = np.array(ex["row"], np.float32)
+    x = _bits(row).reshape(1, 1, -1)
+    q = O.quantize_chunks(x, 1, O.MODE_4OVER6, want_errors=True)
+    assert q["tensor_scale"][0] == ex["tensor_scale"]
+    for b, blk in enumerate(ex["blocks"]):
+        assert q["scales"][0, 0, b] == blk["scale"], blk["why"]
+        assert list(q["codes"][0, 0, 8 * b:8 * b + 8]) == blk["codes"], blk["why"]
+        assert q["err6"][0, 0, b] == blk["err6"] and q["err4"][0, 0, b] == blk["err4"], blk["why"]
+    assert q["use4"] == sum(blk["choice"] == 4 for blk in ex["blocks"])
+    deq = O.dequantize(q["codes"], q["scales"], q["tensor_scale"], None, 1)
+    assert np.array_equal(O.bf16_to_float(deq).ravel(), np.array(ex["dequantized"], np.float32))
+
+
+# ----------------------------------------------- exact-arithmetic helpers ----
+
+E4M3_VALS = np.array([O.lib().ora_e4m3_decode(c) for c in range(127)], np.float64)
+E4M3_MIDS = (E4M3_VALS[:-1] + E4M3_VALS[1:]) / 2
+E2M1_MAG = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float64)
+E2M1_MIDS = (E2M1_MAG[:-1] + E2M1_MAG[1:]) / 2
+
+
+def _nearest_even(val, mids, scale):
+    """Index of the nearest grid point to val/scale (grid given by its
+    midpoints mids), ties to the even index; exact because val and
+    scale*mids are exact float64 products of short mantissas."""
+    thr = scale[..., None] * mids
+    below = (val[..., None] > thr).sum(-1)
+    tie = (val[..., None] == thr)
+    tie_idx = tie.argmax(-1)
+    has_tie = tie.any(-1)
+    # at a tie between k and k+1 pick the even one
+    even = np.where(tie_idx % 2 == 0, tie_idx, tie_idx + 1)
+    return np.where(has_tie, even, below)
+
+
+def exact_candidate(z, c, scale_int=2 ** 16):
+    """Exact candidate c for blocks z [n, m] (m = 16 for 1D, 256 for a tile):
+    E4M3 scale index nearest to t_b / c, codes nearest to z / S, and the exact
+    squared error times scale_int^2 as an int64 (z * scale_int and v * S *
+    scale_int are integers for the inputs used here)."""
+    z = z.astype(np.float64)
+    t = np.abs(z).max(-1)
+    sidx = _nearest_even(t, E4M3_MIDS, np.full_like(t, float(c)))
+    sidx = np.minimum(sidx, 126)
+    S = E4M3_VALS[sidx]
+    mag = _nearest_even(np.abs(z), E2M1_MIDS, np.broadcast_to(S[:, None], z.shape))
+    v = np.where(np.signbit(z), -E2M1_MAG[mag], E2M1_MAG[mag])
+    zi = np.rint(z * scale_int).astype(np.int64)
+    vi = np.rint(v * S[:, None] * scale_int).astype(np.int64)
+    assert np.array_equal(zi.astype(np.float64), z * scale_int)
+    assert np.array_equal(vi.astype(np.float64), v * S[:, None] * scale_int)
+    err = ((zi - vi) ** 2).sum(-1)
+    code = (mag | (np.signbit(z).astype(np.int64) << 3)).astype(np.uint8)
+    return sidx.astype(np.uint8), code, err
+
+
+def _random_bf16_blocks(rng, n, width=16, emin=-6, emax=3):
+    sign = rng.integers(0, 2, (n, width))
+    e = rng.integers(emin, emax + 1, (n, width))
+    m = rng.integers(0, 128, (n, width))
+    vals = (1 + m / 128.0) * 2.0 ** e * np.where(sign, -1, 1)
+    # structured blocks: a maximum with companions near 75 % of it, and
+    # half-empty blocks
+    k = n // 4
+    top = vals[:k, :1]
+    vals[:k, 1:6] = top * 0.75 * (1 + rng.uniform(-0.02, 0.02, (k, 5)))
+    vals[k:2 * k, 8:] = 0.0
+    return torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _rounding_sensitive(z, sidx):
+    """Blocks where y = fl(z * fl(1/S)) and the exact z / S fall on different
+    E2M1 codes (a quotient within an fp32 rounding of a midpoint)."""
+    S = E4M3_VALS[sidx].astype(np.float32)
+    R = np.where(S > 0, np.float32(1) / np.where(S > 0, S, 1), 0).astype(np.float32)
+    y = (z * R[:, None]).astype(np.float32)
+    fl_codes = O.e2m1_encode(y) & 7
+    mag_exact = _nearest_even(np.abs(z.astype(np.float64)), E2M1_MIDS,
+                              np.broadcast_to(E4M3_VALS[sidx][:, None], z.shape))
+    return (fl_codes != mag_exact).any(-1)
+
+
+def test_best_of_two_matches_exact_arithmetic_1d():
+    rng = np.random.default_rng(20)
+    n = 120_000 - 1  # plus the anchor block: 7500 rows of 16 blocks
+    z = _random_bf16_blocks(rng, n)
+    # row layout: one anchor block holding 1792 so that g_enc = g_dec = 1
+    anchor = np.zeros((1, 16), np.float32)
+    anchor[0, 0] = 1792.0
+    allz = np.concatenate([anchor, z])
+    assert np.array_equal(O.bf16_to_float(_bits(allz)), allz)  # inputs are bf16-exact
+    x = _bits(allz).reshape(1, -1, 256)  # 16 blocks per row
+    T = x.shape[1]
+    q = O.quantize_chunks(x, T, O.MODE_4OVER6, want_errors=True)
+    assert q["tensor_scale"][0] == 1.0
+    scales = q["scales"].reshape(-1)[1:]
+    codes = _unpack(q["codes"].reshape(-1, 8))[1:]
+    e6o, e4o = q["err6"].reshape(-1)[1:], q["err4"].reshape(-1)[1:]
+
+    s6, c6, e6 = exact_candidate(z, 6)
+    s4, c4, e4 = exact_candidate(z, 4)
+    choose4 = e4 < e6
+    want_s = np.where(choose4, s4, s6)
+    want_c = np.where(choose4[:, None], c4, c6)
+
+    sens = _rounding_sensitive(z, s6) | _rounding_sensitive(z, s4)
+    # Excused: (a) y = fl(z * fl(1/S)) and the exact z / S round to different
+    # codes (bf16 inputs often sit exactly on an E2M1 midpoint of z / S);
+    # (b) exact errors (equal or not) closer than the fp32 accumulation can
+    # resolve: the choice is made on the fp32 errors.
+    close = np.abs(e6 - e4) <= (np.maximum(e6, e4) >> 18) + 1
+    excused = sens | close
+    bad = (scales != want_s) | (codes != want_c).any(-1)
+    assert not (bad & ~excused).any(), np.nonzero(bad & ~excused)[0][:10]
+    assert excused.mean() < 2e-2 and bad.mean() < 5e-3, (excused.mean(), bad.mean())
+    # the tie rule on the fp32 errors: equal errors keep +-6
+    tie32 = (e6o == e4o) & ~sens
+    assert tie32.sum() > 100 and np.array_equal(scales[tie32], s6[tie32])
+    # the oracle's fp32 errors agree with the exact errors within the
+    # accumulated rounding bound (17 roundings of <= 2^-24 each)
+    ok = ~sens
+    scale2 = float(2 ** 32)
+    for eo, ee in ((e6o, e6), (e4o, e4)):
+        rel = np.abs(eo[ok].astype(np.float64) * scale2 - ee[ok]) / np.maximum(ee[ok], 1)
+        assert rel.max() <= 20 * 2.0 ** -24
+    # both candidates are real choices in this sample
+    assert 0.05 < choose4.mean() < 0.95
+
+
+def test_best_of_two_matches_exact_arithmetic_2d():
+    rng = np.random.default_rng(21)
+    nt = 3000
+    tiles = _random_bf16_blocks(rng, nt, width=256)
+    rows_t = 30  # tile grid 30 x 100 plus an anchor tile row
+    grid = tiles.reshape(rows_t, nt // rows_t, 16, 16).transpose(0, 2, 1, 3).reshape(rows_t * 16, -1)
+    anchor = np.zeros((16, grid.shape[1]), np.float32)
+    anchor[0, 0] = 1792.0
+    w = np.concatenate([anchor, grid])
+    q = O.quantize_2d(_bits(w), O.MODE_4OVER6, want_errors=True)
+    assert q["tensor_scale"][0] == 1.0
+    sc = q["scales"][1:].reshape(-1)
+    codes = _unpack(q["codes"][16:]).reshape(rows_t, 16, nt // rows_t, 16).transpose(0, 2, 1, 3).reshape(nt, 256)
+    s6, c6, e6 = exact_candidate(tiles, 6)
+    s4, c4, e4 = exact_candidate(tiles, 4)
+    choose4 = e4 < e6
+    sens = _rounding_sensitive(tiles, s6) | _rounding_sensitive(tiles, s4)
+    close = np.abs(e6 - e4) <= (np.maximum(e6, e4) >> 17) + 1
+    bad = (sc != np.where(choose4, s4, s6)) | (codes != np.where(choose4[:, None], c4, c6)).any(-1)
+    assert not (bad & ~(sens | close)).any()
+    assert (sens | close).mean() < 0.15 and bad.mean() < 0.05, ((sens | close).mean(), bad.mean())
+    assert 0.01 < choose4.mean() < 0.99
+
+
+# ------------------------------------------- realistic-data consistency ----
+
+def _prepared(x_bits, mean):
+    x = O.bf16_to_float(x_bits)
+    return (x - mean[0][:, None, :]).astype(np.float32) if mean is not None else x
+
+
+@pytest.mark.parametrize("which", ["gaussian", "heavy"])
+def test_choice_scale_and_code_consistency(which):
+    shape = W.KVShape(3, 512, 128, 256)
+    k, v = (W.gaussian_kv if which == "gaussian" else W.heavy_tail_kv)(shape, 31)
+    kb, vb = W.bf16_bits(k), W.bf16_bits(v)
+    r = O.smooth_quantize(kb, vb, 256, want_errors=True)
+    for name, xb, mean in (("k", kb, r["k_mean"]), ("v", vb, None)):
+        for ch in range(2):
+            sl = slice(256 * ch, 256 * (ch + 1))
+            xp = O.bf16_to_float(xb[:, sl])
+            if mean is not None:
+                xp = (xp - mean[ch][:, None, :]).astype(np.float32)
+            A = np.abs(xp).max()
+            g_enc = np.float32(1792.0) / np.float32(A)
+            assert r[f"{name}_tensor_scale"][ch] == np.float32(A) / np.float32(1792.0)
+            z = (xp * g_enc).astype(np.float32).reshape(-1, 16)
+            t = np.abs(z).max(-1)
+            s6 = _torch_e4m3((t / np.float32(6)).astype(np.float32))
+            s4 = _torch_e4m3((t / np.float32(4)).astype(np.float32))
+            sc = r[f"{name}_scales"][:, sl].reshape(-1)
+            e6 = r[f"{name}_err6"][:, sl].reshape(-1)
+            e4 = r[f"{name}_err4"][:, sl].reshape(-1)
+            use4 = e4 < e6
+            assert np.array_equal(sc, np.where(use4, s4, s6))
+            # chosen error <= other error; errors are finite and >= 0
+            chosen = np.where(use4, e4, e6)
+            assert np.all(chosen <= np.maximum(e6, e4)) and np.all(np.isfinite(e6)) and np.all(e4 >= 0)
+            # max-magnitude rule: the block maximum lands on 6 (+-6) or 4 (+-4)
+            # whenever the scale is a normal E4M3 value
+            S = O.e4m3_decode(sc)
+            codes = _unpack(r[f"{name}_codes"][:, sl].reshape(-1, 8))
+            mx = (codes & 7).max(-1)
+            normal = S >= 2.0 ** -6
+            assert np.all(mx[normal & use4] == 6) and np.all(mx[normal & ~use4] == 7)
+    assert r["k_use4"] + r["v_use4"] > 0
+
+
+def test_fixed_modes_are_single_candidate_nvfp4():
+    shape = W.KVShape(2, 256, 64, 256)
+    _, v = W.gaussian_kv(shape, 32)
+    vb = W.bf16_bits(v)
+    x = O.bf16_to_float(vb)
+    A = np.abs(x).max()
+    for mode, C, c in ((O.MODE_FIXED6, 2688.0, 6), (O.MODE_FIXED4, 1792.0, 4)):
+        q = O.quantize_chunks(vb, 256, mode, want_errors=True)
+        g = np.float32(C) / np.float32(A)
+        z = (x * g).astype(np.float32)
+        t = np.abs(z).reshape(-1, 16).max(-1)
+        s = _torch_e4m3((t / np.float32(c)).astype(np.float32))
+        assert np.array_equal(q["scales"].reshape(-1), s)
+        S = O.e4m3_decode(s)
+        R = np.where(S > 0, np.float32(1) / np.where(S > 0, S, 1), 0).astype(np.float32)
+        y = (z.reshape(-1, 16) * R[:, None]).astype(np.float32)
+        # low nibble = even element, blocks of 16 consecutive channels
+        assert np.array_equal(_unpack(q["codes"].reshape(-1, 8)), O.e2m1_encode(y))
+        assert q["use4"] == (q["scales"].size if mode == O.MODE_FIXED4 else 0)
+        other = q["err4"] if mode == O.MODE_FIXED6 else q["err6"]
+        assert np.isnan(other).all()
+
+
+# -------------------------------------------------------------- invariants ----
+
+def test_power_of_two_scaling_equivariance():
+    shape = W.KVShape(2, 512, 128, 256)
+    k, v = W.gaussian_kv(shape, 33)
+    base = O.smooth_quantize(W.bf16_bits(k), W.bf16_bits(v), 256)
+    for p in (-3, 5):
+        f = 2.0 ** p
+        sk = W.bf16_bits((k.float() * f).to(torch.bfloat16))  # exact: a power of two
+        sv = W.bf16_bits((v.float() * f).to(torch.bfloat16))
+        r = O.smooth_quantize(sk, sv, 256)
+        for key in ("k_codes", "v_codes", "k_scales", "v_scales"):
+            assert np.array_equal(r[key], base[key]), (p, key)
+        assert np.array_equal(r["k_tensor_scale"], base["k_tensor_scale"] * np.float32(f))
+        assert np.array_equal(r["v_tensor_scale"], base["v_tensor_scale"] * np.float32(f))
+        assert np.array_equal(r["k_mean"], base["k_mean"] * np.float32(f))
+
+
+def test_sign_symmetry():
+    shape = W.KVShape(2, 256, 128, 256)
+    _, v = W.gaussian_kv(shape, 34)
+    a = O.quantize_chunks(W.bf16_bits(v), 256)
+    b = O.quantize_chunks(W.bf16_bits(-v), 256)
+    assert np.array_equal(a["scales"], b["scales"])
+    assert np.array_equal(a["codes"] ^ 0x88, b["codes"])
+    assert np.array_equal(a["tensor_scale"], b["tensor_scale"])
+
+
+def test_grid_values_roundtrip_exactly():
+    rng = np.random.default_rng(35)
+    # every block: values v * 2^e (v on the E2M1 grid) with a maximum of 6 * 2^e
+    n = 2000
+    e = rng.integers(-4, 4, n).astype(np.float64)
+    mags = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    v = mags[rng.integers(0, 8, (n, 16))] * np.where(rng.integers(0, 2, (n, 16)), -1, 1)
+    v[:, 0] = 6.0
+    vals = (v * 2.0 ** e[:, None]).astype(np.float32)
+    anchor = np.zeros((1, 16), np.float32)
+    anchor[0, 0] = 1792.0
+    allv = np.concatenate([anchor, vals])
+    x = _bits(allv).reshape(1, -1, 16)
+    q = O.quantize_chunks(x, x.shape[1], O.MODE_4OVER6)
+    assert q["tensor_scale"][0] == 1.0
+    deq = O.dequantize(q["codes"], q["scales"], q["tensor_scale"], None, x.shape[1])
+    assert np.array_equal(O.bf16_to_float(deq).reshape(-1, 16), allv)
+
+
+# --------------------------------------------------------------- smoothing ----
+
+def test_mean_is_exact_for_power_of_two_chunks():
+    rng = np.random.default_rng(36)
+    x = rng.integers(-255, 256, (3, 1024, 32)).astype(np.float32)  # |int| < 256: exact in bf16 and in the sum
+    m = O.kv_mean(_bits(x), 256)
+    want = x.reshape(3, 4, 256, 32).sum(2, dtype=np.float64) / 256  # exact: power-of-two divisor
+    assert np.array_equal(m, want.transpose(1, 0, 2).astype(np.float32))
+
+
+def test_mean_matches_fp64_and_smoothed_mean_is_zero():
+    shape = W.KVShape(4, 1536, 64, 512)
+    k, _ = W.gaussian_kv(shape, 37)
+    kb = W.bf16_bits(k)
+    kf = O.bf16_to_float(kb).astype(np.float64)
+    m = O.kv_mean(kb, 512)
+    ref = kf.reshape(4, 3, 512, 64).mean(2).transpose(1, 0, 2)
+    assert np.all(np.abs(m - ref) <= np.abs(ref) * 2.0 ** -24 + 1e-30)
+    for c in range(3):
+        seg = O.bf16_to_float(kb[:, 512 * c:512 * (c + 1)])
+        kp = (seg - m[c][:, None, :]).astype(np.float32).astype(np.float64)
+        resid = np.abs(kp.mean(1))
+        bound = 2.0 ** -23 * (np.abs(m[c]) + np.abs(seg - m[c][:, None, :]).mean(1))
+        assert np.all(resid <= bound)
+
+
+def test_smoothing_removes_the_channel_offset_before_quantizing():
+    shape = W.KVShape(2, 256, 128, 256)
+    k, _ = W.gaussian_kv(shape, 38)
+    kb = W.bf16_bits(k)
+    m = O.kv_mean(kb, 256)
+    smoothed = O.quantize_chunks(kb, 256, mean=m)
+    unsmoothed = O.quantize_chunks(kb, 256, mean=None)
+    ds = O.bf16_to_float(O.dequantize(smoothed["codes"], smoothed["scales"], smoothed["tensor_scale"], m, 256))
+    du = O.bf16_to_float(O.dequantize(unsmoothed["codes"], unsmoothed["scales"], unsmoothed["tensor_scale"], None,
+                                      256))
+    x = O.bf16_to_float(kb).astype(np.float64)
+    assert ((ds - x) ** 2).mean() < ((du - x) ** 2).mean()
+
+
+# -------------------------------------------------------------------- RHT ----
+
+def test_rht_matches_dense_hadamard_on_integers():
+    rng = np.random.default_rng(40)
+    H16 = scipy.linalg.hadamard(16).astype(np.float64)  # Sylvester, natural order
+    x = rng.integers(-64, 64, (5000, 16)).astype(np.float32)
+    for mask in (0, 0xFFFF, 0x8421, int(rng.integers(0, 1 << 16))):
+        s = np.array([-1.0 if (mask >> j) & 1 else 1.0 for j in range(16)])
+        want = (x.astype(np.float64) * s) @ H16.T * 0.25
+        assert np.array_equal(O.rht16(x, mask).astype(np.float64), want), hex(mask)
+
+
+def test_rht_inverse_and_norm():
+    rng = np.random.default_rng(41)
+    mask = 0x5A3C
+    s = np.array([-1.0 if (mask >> j) & 1 else 1.0 for j in range(16)], np.float32)
+    x = rng.integers(-50, 50, (2000, 16)).astype(np.float32)
+    y = O.rht16(x, mask)
+    back = O.rht16(y, 0) * s  # (H/4)^-1 = H/4, then undo the signs
+    assert np.array_equal(back, x)
+    xr = rng.standard_normal((2000, 16)).astype(np.float32)
+    yr = O.rht16(xr, mask)
+    n0, n1 = np.linalg.norm(xr, axis=1), np.linalg.norm(yr, axis=1)
+    assert np.allclose(n0, n1, rtol=1e-6)
+    # one-hot inputs select a signed, scaled Hadamard column
+    H16 = scipy.linalg.hadamard(16)
+    for j in range(16):
+        e = np.zeros((1, 16), np.float32)
+        e[0, j] = 4.0
+        assert np.array_equal(O.rht16(e, mask)[0], (H16[:, j] * s[j]).astype(np.float32))
+
+
+def test_activation_path_uses_rotated_values():
+    x, mask, _ = W.act_weight(act_rows=64, act_cols=256, w_rows=16, w_cols=16)
+    xb = W.bf16_bits(x)
+    q = O.quantize_1d(xb, hadamard=True, sign_mask=mask)
+    rot = O.rht16(O.bf16_to_float(xb).reshape(-1, 16), mask).reshape(64, 256)
+    assert q["tensor_scale"][0] == np.abs(rot).max() / np.float32(1792)
+    # the same as quantizing the rotated tensor without RHT: quantize the
+    # rotated values through an exactly representable route (bf16 would round),
+    # so compare the scale bytes' candidates instead
+    g = np.float32(1792) / np.abs(rot).max()
+    t = np.abs((rot * g).astype(np.float32)).reshape(-1, 16).max(-1)
+    s6 = _torch_e4m3((t / np.float32(6)).astype(np.float32))
+    s4 = _torch_e4m3((t / np.float32(4)).astype(np.float32))
+    sc = q["scales"].reshape(-1)
+    assert np.all((sc == s6) | (sc == s4))
+    plain = O.quantize_1d(xb)
+    assert not np.array_equal(plain["scales"], q["scales"])
+
+
+# ----------------------------------------------------------------- dequant ----
+
+def test_dequant_formula_via_numpy_and_torch():
+    rng = np.random.default_rng(50)
+    H, T, D, L = 2, 64, 64, 32
+    codes = rng.integers(0, 256, (H, T, D // 2)).astype(np.uint8)
+    scales = rng.integers(0, 0x7F, (H, T, D // 16)).astype(np.uint8)
+    ts = np.array([0.37, 2.5e-3], np.float32)
+    mean = rng.standard_normal((T // L, H, D)).astype(np.float32)
+    got = O.dequantize(codes, scales, ts, mean, L)
+    v = O.e2m1_decode(_unpack(codes))
+    S = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    S = np.repeat(S, 16, axis=-1)
+    g = np.repeat(ts, L)[None, :, None]
+    m = np.repeat(mean, L, axis=0).transpose(1, 0, 2)
+    xh = ((v * S).astype(np.float32) * g).astype(np.float32)
+    xh = (xh + m).astype(np.float32)
+    want = torch.from_numpy(xh).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    got2 = O.dequantize(codes, scales, ts, None, L)
+    want2 = torch.from_numpy(((v * S).astype(np.float32) * g).astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(got2, want2.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_dequant_2d_layout():
+    rng = np.random.default_rng(51)
+    codes = rng.integers(0, 256, (32, 24)).astype(np.uint8)
+    scales = rng.integers(0, 0x7F, (2, 3)).astype(np.uint8)
+    ts = np.array([0.125], np.float32)
+    got = O.bf16_to_float(O.dequantize_2d(codes, scales, ts))
+    v = O.e2m1_decode(_unpack(codes))
+    S = O.e4m3_decode(scales)
+    want = v * np.kron(S, np.ones((16, 16), np.float32)) * np.float32(0.125)
+    assert np.array_equal(got, want.astype(np.float32))  # exact: short mantissas
+
+
+# ---------------------------------------------------------------- golden ----
+
+def test_tiny_config_golden_regression():
+    path = os.path.join(GOLDEN, "tiny_kv_oracle.npz")
+    g = np.load(path)
+    k, v = W.gaussian_kv(W.TINY, W.SEED_TINY)
+    kb, vb = W.bf16_bits(k), W.bf16_bits(v)
+    assert np.array_equal(kb, g["k"]) and np.array_equal(vb, g["v"])
+    r = O.smooth_quantize(kb, vb, W.TINY.chunk_len)
+    for key in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tensor_scale", "v_tensor_scale", "k_mean"):
+        assert np.array_equal(r[key], g[key]), key
+    deq = O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], r["k_mean"], W.TINY.chunk_len)
+    assert np.array_equal(deq, g["k_dequant"])
