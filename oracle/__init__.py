@@ -55,6 +55,19 @@ def lib():
     return _lib
 
 
+def default_threads():
+    """Worker threads for the oracle: OMP_NUM_THREADS when set (the GPU hosts
+    set it to their CPU share), else the CPU count capped at 16."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _nt(n):
+    return default_threads() if not n or n <= 0 else int(n)
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -73,35 +86,35 @@ def _check(rc, what):
 def e2m1_encode(y, nthreads=0):
     y = _c(y, np.float32)
     out = np.empty(y.shape, np.uint8)
-    lib().ora_e2m1_encode_array(_ptr(y), y.size, _ptr(out), nthreads)
+    lib().ora_e2m1_encode_array(_ptr(y), y.size, _ptr(out), _nt(nthreads))
     return out
 
 
 def e2m1_decode(q, nthreads=0):
     q = _c(q, np.uint8)
     out = np.empty(q.shape, np.float32)
-    lib().ora_e2m1_decode_array(_ptr(q), q.size, _ptr(out), nthreads)
+    lib().ora_e2m1_decode_array(_ptr(q), q.size, _ptr(out), _nt(nthreads))
     return out
 
 
 def e4m3_encode(r, nthreads=0):
     r = _c(r, np.float32)
     out = np.empty(r.shape, np.uint8)
-    lib().ora_e4m3_encode_array(_ptr(r), r.size, _ptr(out), nthreads)
+    lib().ora_e4m3_encode_array(_ptr(r), r.size, _ptr(out), _nt(nthreads))
     return out
 
 
 def e4m3_decode(s, nthreads=0):
     s = _c(s, np.uint8)
     out = np.empty(s.shape, np.float32)
-    lib().ora_e4m3_decode_array(_ptr(s), s.size, _ptr(out), nthreads)
+    lib().ora_e4m3_decode_array(_ptr(s), s.size, _ptr(out), _nt(nthreads))
     return out
 
 
 def float_to_bf16(x, nthreads=0):
     x = _c(x, np.float32)
     out = np.empty(x.shape, np.uint16)
-    lib().ora_float_to_bf16_array(_ptr(x), x.size, _ptr(out), nthreads)
+    lib().ora_float_to_bf16_array(_ptr(x), x.size, _ptr(out), _nt(nthreads))
     return out
 
 
@@ -133,7 +146,7 @@ def kv_mean(x, chunk_len, nthreads=0):
     x = _c(x, np.uint16)
     H, T, D = x.shape
     out = np.empty((T // chunk_len, H, D), np.float32)
-    _check(lib().ora_kv_mean(_ptr(x), H, T, D, chunk_len, _ptr(out), nthreads), "kv_mean")
+    _check(lib().ora_kv_mean(_ptr(x), H, T, D, chunk_len, _ptr(out), _nt(nthreads)), "kv_mean")
     return out
 
 
@@ -152,7 +165,7 @@ def quantize_chunks(x, chunk_len, mode=MODE_4OVER6, mean=None, hadamard=False, s
     m = None if mean is None else _c(mean, np.float32)
     rc = lib().ora_quantize_chunks(_ptr(x), H, T, D, chunk_len, mode, _ptr(m), int(bool(hadamard)),
                                    int(sign_mask) & 0xFFFF, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(e6),
-                                   _ptr(e4), ctypes.byref(n4), nthreads)
+                                   _ptr(e4), ctypes.byref(n4), _nt(nthreads))
     _check(rc, "quantize_chunks")
     out = {"codes": codes, "scales": scales, "tensor_scale": ts, "use4": int(n4.value)}
     if want_errors:
@@ -185,7 +198,7 @@ def dequantize(codes, scales, tensor_scale, mean, chunk_len, nthreads=0):
     D = 2 * D2
     out = np.empty((H, T, D), np.uint16)
     _check(lib().ora_dequantize(_ptr(codes), _ptr(scales), _ptr(ts), _ptr(m), H, T, D, chunk_len, _ptr(out),
-                                nthreads), "dequantize")
+                                _nt(nthreads)), "dequantize")
     return out
 
 
@@ -213,7 +226,7 @@ def quantize_2d(w, mode=MODE_4OVER6, want_errors=False, nthreads=0):
     e4 = np.empty((rows // 16, cols // 16), np.float32) if want_errors else None
     n4 = ctypes.c_longlong(0)
     _check(lib().ora_quantize_2d(_ptr(w), rows, cols, mode, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(e6), _ptr(e4),
-                                 ctypes.byref(n4), nthreads), "quantize_2d")
+                                 ctypes.byref(n4), _nt(nthreads)), "quantize_2d")
     out = {"codes": codes, "scales": scales, "tensor_scale": ts, "use4": int(n4.value)}
     if want_errors:
         out["err6"], out["err4"] = e6, e4

@@ -1,0 +1,221 @@
+"""NVFP4 "Four-Over-Six" KV-cache quantizer for MI355X (gfx950).
+
+Thin ctypes binding over libnvfp4kv.so (HIP kernels + C ABI, declared in
+include/nvfp4kv.h).  Same names as the C entry points; this module only
+marshals arguments: it allocates output tensors with torch (device memory),
+passes their pointers and torch's current HIP stream, and turns a non-zero
+status into an exception.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  A missing or unloadable library raises.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "Nvfp4Error", "lib", "nvfp4_status_string",
+    "nvfp4_kv_workspace_bytes", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
+    "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
+    "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
+]
+
+MODE_4OVER6, MODE_FIXED6, MODE_FIXED4 = 0, 1, 2
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4kv.so")
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {nvfp4_status_string(status)} ({status})")
+
+
+def lib():
+    """The loaded C library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library missing: {LIB_PATH}; build it with "
+                               "`python precision_kv_cache_amd/build.py` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i, ll, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_size_t, ctypes.c_uint32
+        sig = {
+            "nvfp4_status_string": (ctypes.c_char_p, [i]),
+            "nvfp4_kv_workspace_bytes": (sz, [i, i, i, i]),
+            "nvfp4_kv_smooth_quantize": (i, [P, P, i, i, i, i, i, P, P, P, P, P, P, P, P, P, sz, P]),
+            "nvfp4_dequantize": (i, [P, P, P, P, i, i, i, i, P, P]),
+            "nvfp4_quantize_1d_workspace_bytes": (sz, [i, i]),
+            "nvfp4_quantize_2d_workspace_bytes": (sz, [i, i]),
+            "nvfp4_quantize_1d": (i, [P, i, i, i, i, u32, P, P, P, P, sz, P]),
+            "nvfp4_quantize_2d": (i, [P, i, i, i, P, P, P, P, sz, P]),
+            "nvfp4_dequantize_2d": (i, [P, P, P, i, i, P, P]),
+            "nvfp4_diag_e2m1_encode": (i, [P, ll, P, P]),
+            "nvfp4_diag_candidates": (i, [P, ll, P, P, P]),
+            "nvfp4_diag_reciprocal": (i, [P, ll, P, P]),
+            "nvfp4_diag_bf16_round": (i, [P, ll, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def nvfp4_status_string(status):
+    return lib().nvfp4_status_string(int(status)).decode()
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise Nvfp4Error(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bf16_dev(t, name):
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    return t
+
+
+def nvfp4_kv_workspace_bytes(H, T, D, chunk_len):
+    return int(lib().nvfp4_kv_workspace_bytes(H, T, D, chunk_len))
+
+
+def nvfp4_kv_smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, choice_counts=False, out=None, workspace=None,
+                             stream=None):
+    """K smoothing + 4/6 NVFP4 quantization of K, V bf16 [H, T, D].
+
+    Returns a dict with k_codes, v_codes [H, T, D/2] uint8, k_scales, v_scales
+    [H, T, D/16] uint8 (E4M3FN bits), k_tensor_scale, v_tensor_scale [T/L]
+    float32, k_mean [T/L, H, D] float32 and, if requested, choice_counts [2, 2]
+    int64 ({K, V} x {kept +-6, kept +-4}).  ``out`` may supply these tensors
+    (and ``workspace`` a uint8 device buffer) to avoid allocation.
+    """
+    _bf16_dev(k, "k"); _bf16_dev(v, "v")
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [H, T, D]")
+    H, T, D = k.shape
+    dev = k.device
+    nc = T // chunk_len if chunk_len > 0 else 0
+    if out is None:
+        out = {
+            "k_codes": torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
+            "v_codes": torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
+            "k_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
+            "v_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
+            "k_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
+            "v_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
+            "k_mean": torch.empty(nc, H, D, dtype=torch.float32, device=dev),
+        }
+        if choice_counts:
+            out["choice_counts"] = torch.empty(2, 2, dtype=torch.int64, device=dev)
+    ws_bytes = nvfp4_kv_workspace_bytes(H, T, D, chunk_len)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = lib().nvfp4_kv_smooth_quantize(
+        _ptr(k), _ptr(v), H, T, D, chunk_len, mode, _ptr(out["k_codes"]), _ptr(out["v_codes"]),
+        _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
+        _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(rc, "nvfp4_kv_smooth_quantize")
+    return out
+
+
+def nvfp4_dequantize(codes, scales, tensor_scale, mean, chunk_len, out=None, stream=None):
+    """codes [H, T, D/2], scales [H, T, D/16], tensor_scale [T/L], mean
+    [T/L, H, D] or None -> bf16 [H, T, D]."""
+    H, T, D2 = codes.shape
+    D = 2 * D2
+    if out is None:
+        out = torch.empty(H, T, D, dtype=torch.bfloat16, device=codes.device)
+    rc = lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(mean), H, T, D, chunk_len,
+                                _ptr(out), _stream(stream))
+    _check(rc, "nvfp4_dequantize")
+    return out
+
+
+def nvfp4_quantize_1d(x, mode=MODE_4OVER6, hadamard=False, sign_mask=0, out=None, workspace=None, stream=None):
+    """Activation x bf16 [rows, cols] -> codes [rows, cols/2], scales
+    [rows, cols/16], tensor_scale [1]; optional 16-point RHT first."""
+    _bf16_dev(x, "x")
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        out = {"codes": torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
+               "scales": torch.empty(rows, cols // 16, dtype=torch.uint8, device=dev),
+               "tensor_scale": torch.empty(1, dtype=torch.float32, device=dev)}
+    nws = int(lib().nvfp4_quantize_1d_workspace_bytes(rows, cols))
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    rc = lib().nvfp4_quantize_1d(_ptr(x), rows, cols, mode, int(bool(hadamard)), int(sign_mask) & 0xFFFF,
+                                 _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["tensor_scale"]),
+                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "nvfp4_quantize_1d")
+    return out
+
+
+def nvfp4_quantize_2d(w, mode=MODE_4OVER6, out=None, workspace=None, stream=None):
+    """Weight w bf16 [rows, cols] -> codes [rows, cols/2], scales
+    [rows/16, cols/16], tensor_scale [1] (16x16 tiles)."""
+    _bf16_dev(w, "w")
+    rows, cols = w.shape
+    dev = w.device
+    if out is None:
+        out = {"codes": torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
+               "scales": torch.empty(rows // 16, cols // 16, dtype=torch.uint8, device=dev),
+               "tensor_scale": torch.empty(1, dtype=torch.float32, device=dev)}
+    nws = int(lib().nvfp4_quantize_2d_workspace_bytes(rows, cols))
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    rc = lib().nvfp4_quantize_2d(_ptr(w), rows, cols, mode, _ptr(out["codes"]), _ptr(out["scales"]),
+                                 _ptr(out["tensor_scale"]), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "nvfp4_quantize_2d")
+    return out
+
+
+def nvfp4_dequantize_2d(codes, scales, tensor_scale, out=None, stream=None):
+    rows, c2 = codes.shape
+    if out is None:
+        out = torch.empty(rows, 2 * c2, dtype=torch.bfloat16, device=codes.device)
+    rc = lib().nvfp4_dequantize_2d(_ptr(codes), _ptr(scales), _ptr(tensor_scale), rows, 2 * c2, _ptr(out),
+                                   _stream(stream))
+    _check(rc, "nvfp4_dequantize_2d")
+    return out
+
+
+# ---- codec probes (test support) -----------------------------------------
+
+def nvfp4_diag_e2m1_encode(y, stream=None):
+    out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
+    _check(lib().nvfp4_diag_e2m1_encode(_ptr(y), y.numel(), _ptr(out), _stream(stream)), "nvfp4_diag_e2m1_encode")
+    return out
+
+
+def nvfp4_diag_candidates(t, stream=None):
+    s6 = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+    s4 = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+    _check(lib().nvfp4_diag_candidates(_ptr(t), t.numel(), _ptr(s6), _ptr(s4), _stream(stream)),
+           "nvfp4_diag_candidates")
+    return s6, s4
+
+
+def nvfp4_diag_reciprocal(s, stream=None):
+    out = torch.empty(s.shape, dtype=torch.float32, device=s.device)
+    _check(lib().nvfp4_diag_reciprocal(_ptr(s), s.numel(), _ptr(out), _stream(stream)), "nvfp4_diag_reciprocal")
+    return out
+
+
+def nvfp4_diag_bf16_round(x, stream=None):
+    out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
+    _check(lib().nvfp4_diag_bf16_round(_ptr(x), x.numel(), _ptr(out), _stream(stream)), "nvfp4_diag_bf16_round")
+    return out

@@ -1,0 +1,311 @@
+// act_weight.hip -- NVFP4 4/6 quantizers for the GEMM operands that the
+// LongLive-2.0 summary page lists for its NVFP4 path (training pipeline,
+// step 4): activations with 1D 16-element blocks after a 16-point
+// random-sign Hadamard transform, and weights with 2D 16x16 tiles.
+//
+// Both need the tensor's largest magnitude before any block can be encoded,
+// so each is two passes: an amax pass (order-free, merged with an integer
+// atomic max on the non-negative fp32 bit pattern) and the quantize pass,
+// which recomputes the rotation in registers instead of storing it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "host_common.hpp"
+#include "nvfp4_device.hpp"
+#include "nvfp4kv.h"
+
+namespace nvfp4 {
+
+constexpr int kAWThreads = 256;
+
+// 16-point random-sign Hadamard transform of one block, in place:
+// u = s * x (exact sign flips), fast Walsh-Hadamard butterflies with strides
+// 1, 2, 4, 8 turning (a, b) into (a + b, a - b), then times 1/4 (exact).
+// flip[j] is 0x80000000 where bit j of the sign mask is set.
+__device__ __forceinline__ void rht16(float (&u)[16], const uint32_t (&flip)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) u[j] = __uint_as_float(__float_as_uint(u[j]) ^ flip[j]);
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = u[i], b = u[i + h];
+      u[i] = a + b;
+      u[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) u[j] = u[j] * 0.25f;
+}
+
+__device__ __forceinline__ void sign_flips(uint32_t mask, uint32_t (&flip)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) flip[j] = ((mask >> j) & 1u) << 31;
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Largest |value| over nseg 16-element segments (optionally rotated).
+template <bool RHT>
+__global__ __launch_bounds__(kAWThreads) void amax16_kernel(const uint16_t* x, long long nseg, uint32_t sign_mask,
+                                                            uint32_t* amax_bits) {
+  __shared__ float shw[kAWThreads / 64];
+  uint32_t flip[16];
+  sign_flips(sign_mask, flip);
+  float am = 0.0f;
+  for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nseg;
+       f += (long long)gridDim.x * blockDim.x) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + f * 16);
+    const uint4 a = src[0], b = src[1];
+    float u[16];
+    unpack16(a, b, u);
+    if (RHT) rht16(u, flip);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
+  }
+  am = wave_max(am);
+  if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x / 64); ++w) m = fmaxf(m, shw[w]);
+    atomicMax(amax_bits, __float_as_uint(m));  // non-negative floats order as integers
+  }
+}
+
+// 1D quantize pass: one lane per 16-element block of the row-major tensor.
+template <int MODE, bool RHT>
+__global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, long long nblk, uint32_t sign_mask,
+                                                             const uint32_t* amax_bits, uint8_t* codes,
+                                                             uint8_t* scales, float* tensor_scale) {
+  const float A = __uint_as_float(*amax_bits);
+  const float C = mode_constant(MODE);
+  const float g = A > 0.0f ? C / A : 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = A / C;
+  uint32_t flip[16];
+  sign_flips(sign_mask, flip);
+  for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nblk;
+       f += (long long)gridDim.x * blockDim.x) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + f * 16);
+    const uint4 a = src[0], b = src[1];
+    float z[16];
+    unpack16(a, b, z);
+    if (RHT) rht16(z, flip);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = z[i] * g;
+    const Block46 q = quant_block16<MODE>(z);
+    *reinterpret_cast<uint2*>(codes + f * 8) = make_uint2(q.lo, q.hi);
+    scales[f] = (uint8_t)q.scale;
+  }
+}
+
+// 2D quantize pass: 16 lanes per 16x16 tile (lane = tile row), 4 tiles per
+// wave; the tile maximum and the tile error are butterfly reductions inside
+// the 16-lane group, the error one pairwise tree over the tile rows.
+template <int MODE>
+__global__ __launch_bounds__(kAWThreads) void quant2d_kernel(const uint16_t* w, int rows, int cols,
+                                                             const uint32_t* amax_bits, uint8_t* codes,
+                                                             uint8_t* scales, float* tensor_scale) {
+  const float A = __uint_as_float(*amax_bits);
+  const float C = mode_constant(MODE);
+  const float g = A > 0.0f ? C / A : 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = A / C;
+  const int ntc = cols / 16;
+  const long long ntiles = (long long)(rows / 16) * ntc;
+  const int lane = threadIdx.x & 63, r = lane & 15;
+  const long long waves_total = (long long)gridDim.x * (blockDim.x / 64);
+  for (long long wv = blockIdx.x * (long long)(blockDim.x / 64) + (threadIdx.x >> 6); wv * 4 < ntiles;
+       wv += waves_total) {
+    const long long tile = wv * 4 + (lane >> 4);
+    const bool active = tile < ntiles;
+    const long long tr = active ? tile / ntc : 0, tc = active ? tile % ntc : 0;
+    const size_t row = (size_t)tr * 16 + r;
+    float z[16];
+    if (active) {
+      const uint4* src = reinterpret_cast<const uint4*>(w + row * cols + tc * 16);
+      const uint4 a = src[0], b = src[1];
+      unpack16(a, b, z);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = z[i] * g;
+    float t = block_absmax(z);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) t = fmaxf(t, __shfl_xor(t, o, 64));
+    const uint32_t s = candidate_codes(t);
+    uint32_t lo, hi, scale, use4;
+    if (MODE == kModeFixed6 || MODE == kModeFixed4) {
+      const float S = MODE == kModeFixed6 ? e4m3_byte<0>(s) : e4m3_byte<1>(s);
+      const Encoded16 e = encode16(z, S, recip_e4m3(S));
+      lo = e.lo; hi = e.hi;
+      scale = MODE == kModeFixed6 ? (s & 0xffu) : (s >> 8);
+      use4 = MODE == kModeFixed4;
+    } else {
+      const float S6 = e4m3_byte<0>(s), S4 = e4m3_byte<1>(s);
+      const Encoded16 e6 = encode16(z, S6, recip_e4m3(S6));
+      const Encoded16 e4 = encode16(z, S4, recip_e4m3(S4));
+      float err6 = e6.err_lo + e6.err_hi, err4 = e4.err_lo + e4.err_hi;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {  // pairwise tree over the 16 tile rows
+        err6 = err6 + __shfl_xor(err6, o, 64);
+        err4 = err4 + __shfl_xor(err4, o, 64);
+      }
+      const bool u4 = err4 < err6;
+      lo = u4 ? e4.lo : e6.lo;
+      hi = u4 ? e4.hi : e6.hi;
+      scale = u4 ? (s >> 8) : (s & 0xffu);
+      use4 = u4;
+    }
+    (void)use4;
+    if (active) {
+      *reinterpret_cast<uint2*>(codes + row * (cols / 2) + tc * 8) = make_uint2(lo, hi);
+      if (r == 0) scales[tr * ntc + tc] = (uint8_t)scale;
+    }
+  }
+}
+
+// Dequantize 2D tiles: one lane per 16-element row segment.
+__global__ __launch_bounds__(kAWThreads) void dequant2d_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                               const float* tensor_scale, int rows, int cols,
+                                                               uint16_t* out) {
+  const int ntc = cols / 16;
+  const long long nseg = (long long)rows * ntc;
+  const float g = tensor_scale[0];
+  for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nseg;
+       f += (long long)gridDim.x * blockDim.x) {
+    const long long row = f / ntc, cb = f % ntc;
+    const uint2 q = *reinterpret_cast<const uint2*>(codes + f * 8);
+    const float S = __builtin_amdgcn_cvt_f32_fp8((int)scales[(row / 16) * ntc + cb], 0);
+    uint32_t wds[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t wq = half ? q.y : q.x;
+      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq, 1.0f, 0);
+      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq, 1.0f, 1);
+      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq, 1.0f, 2);
+      const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq, 1.0f, 3);
+      wds[4 * half + 0] = pack_bf16x2((v0[0] * S) * g, (v0[1] * S) * g);
+      wds[4 * half + 1] = pack_bf16x2((v1[0] * S) * g, (v1[1] * S) * g);
+      wds[4 * half + 2] = pack_bf16x2((v2[0] * S) * g, (v2[1] * S) * g);
+      wds[4 * half + 3] = pack_bf16x2((v3[0] * S) * g, (v3[1] * S) * g);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out + f * 16);
+    dst[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    dst[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+  }
+}
+
+static unsigned grid_for(long long n, int per_thread_items) {
+  long long b = (n + (long long)kAWThreads * per_thread_items - 1) / ((long long)kAWThreads * per_thread_items);
+  return (unsigned)(b < 1 ? 1 : (b > (1 << 20) ? (1 << 20) : b));
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+static bool aw_shape_ok(int rows, int cols, bool tiles) {
+  if (rows < 0 || cols <= 0 || cols % 16) return false;
+  if (tiles && rows % 16) return false;
+  return (long long)rows * cols < (1LL << 40);
+}
+
+extern "C" NVFP4KV_API size_t nvfp4_quantize_1d_workspace_bytes(int rows, int cols) noexcept {
+  return aw_shape_ok(rows, cols, false) ? 256 : 0;
+}
+
+extern "C" NVFP4KV_API size_t nvfp4_quantize_2d_workspace_bytes(int rows, int cols) noexcept {
+  return aw_shape_ok(rows, cols, true) ? 256 : 0;
+}
+
+extern "C" NVFP4KV_API int nvfp4_quantize_1d(const uint16_t* x, int rows, int cols, int mode, int hadamard,
+                                             uint32_t sign_mask, uint8_t* codes, uint8_t* scales,
+                                             float* tensor_scale, void* workspace, size_t workspace_bytes,
+                                             void* stream) noexcept {
+  if (!aw_shape_ok(rows, cols, false)) return NVFP4_ERR_SHAPE;
+  if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !scales || !tensor_scale) return NVFP4_ERR_NULL;
+  if (!workspace || workspace_bytes < 256) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(workspace, 256))
+    return NVFP4_ERR_ALIGN;
+  const size_t n = (size_t)rows * cols;
+  const Range in[1] = {range_of(x, n * 2)};
+  const Range out[4] = {range_of(codes, n / 2), range_of(scales, n / 16), range_of(tensor_scale, 4),
+                        range_of(workspace, 256)};
+  if (any_alias(in, 1, out, 4)) return NVFP4_ERR_ALIAS;
+  hipStream_t s = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  const long long nblk = (long long)(n / 16);
+  (void)hipGetLastError();
+  zero_u32_kernel<<<1, 64, 0, s>>>(amax, 1);
+  const unsigned ga = grid_for(nblk, 4), gq = grid_for(nblk, 2);
+  if (hadamard)
+    amax16_kernel<true><<<ga, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax);
+  else
+    amax16_kernel<false><<<ga, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax);
+#define NVFP4_Q1D(MODE)                                                                                   \
+  (hadamard ? quant1d_kernel<MODE, true><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax, codes, scales, \
+                                                                   tensor_scale)                          \
+            : quant1d_kernel<MODE, false><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax, codes, scales, \
+                                                                    tensor_scale))
+  switch (mode) {
+    case NVFP4_MODE_FIXED6: NVFP4_Q1D(kModeFixed6); break;
+    case NVFP4_MODE_FIXED4: NVFP4_Q1D(kModeFixed4); break;
+    default: NVFP4_Q1D(kMode4over6); break;
+  }
+#undef NVFP4_Q1D
+  return launch_status();
+}
+
+extern "C" NVFP4KV_API int nvfp4_quantize_2d(const uint16_t* w, int rows, int cols, int mode, uint8_t* codes,
+                                             uint8_t* scales, float* tensor_scale, void* workspace,
+                                             size_t workspace_bytes, void* stream) noexcept {
+  if (!aw_shape_ok(rows, cols, true)) return NVFP4_ERR_SHAPE;
+  if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
+  if (rows == 0) return NVFP4_OK;
+  if (!w || !codes || !scales || !tensor_scale) return NVFP4_ERR_NULL;
+  if (!workspace || workspace_bytes < 256) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(w, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(workspace, 256))
+    return NVFP4_ERR_ALIGN;
+  const size_t n = (size_t)rows * cols;
+  const Range in[1] = {range_of(w, n * 2)};
+  const Range out[4] = {range_of(codes, n / 2), range_of(scales, n / 256), range_of(tensor_scale, 4),
+                        range_of(workspace, 256)};
+  if (any_alias(in, 1, out, 4)) return NVFP4_ERR_ALIAS;
+  hipStream_t s = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  (void)hipGetLastError();
+  zero_u32_kernel<<<1, 64, 0, s>>>(amax, 1);
+  amax16_kernel<false><<<grid_for((long long)(n / 16), 4), kAWThreads, 0, s>>>(w, (long long)(n / 16), 0u, amax);
+  const long long ntiles = (long long)(rows / 16) * (cols / 16);
+  const unsigned gq = grid_for((ntiles + 3) / 4 * 64, 1);
+  switch (mode) {
+    case NVFP4_MODE_FIXED6: quant2d_kernel<kModeFixed6><<<gq, kAWThreads, 0, s>>>(w, rows, cols, amax, codes, scales, tensor_scale); break;
+    case NVFP4_MODE_FIXED4: quant2d_kernel<kModeFixed4><<<gq, kAWThreads, 0, s>>>(w, rows, cols, amax, codes, scales, tensor_scale); break;
+    default: quant2d_kernel<kMode4over6><<<gq, kAWThreads, 0, s>>>(w, rows, cols, amax, codes, scales, tensor_scale); break;
+  }
+  return launch_status();
+}
+
+extern "C" NVFP4KV_API int nvfp4_dequantize_2d(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                               int rows, int cols, uint16_t* out, void* stream) noexcept {
+  if (!aw_shape_ok(rows, cols, true)) return NVFP4_ERR_SHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!codes || !scales || !tensor_scale || !out) return NVFP4_ERR_NULL;
+  if (!aligned(codes, 8) || !aligned(out, 16) || !aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGN;
+  const size_t n = (size_t)rows * cols;
+  const Range in[3] = {range_of(codes, n / 2), range_of(scales, n / 256), range_of(tensor_scale, 4)};
+  const Range outr[1] = {range_of(out, n * 2)};
+  if (any_alias(in, 3, outr, 1)) return NVFP4_ERR_ALIAS;
+  (void)hipGetLastError();
+  dequant2d_kernel<<<grid_for((long long)(n / 16), 2), kAWThreads, 0, as_stream(stream)>>>(codes, scales,
+                                                                                        tensor_scale, rows, cols, out);
+  return launch_status();
+}

@@ -1,0 +1,189 @@
+// nvfp4_device.hpp -- gfx950 device building blocks of the NVFP4 4/6
+// quantizer: bf16 unpacking, the two candidate block scales, the exact
+// reciprocal, the 16-element E2M1 encode with its fp32 error, and the 4/6
+// choice (full-stack NVFP4 section of the LongLive-2.0 summary page).
+//
+// Every conversion uses a CDNA4 hardware instruction whose rounding matches
+// the format definitions (round to nearest even, E2M1 saturating at 6 with
+// the sign kept, E4M3FN with subnormals); the test suite sweeps them against
+// the CPU reference.  All arithmetic is fp32, one rounding per operation;
+// the fused multiply-adds below are written out where the result is
+// identical to the unfused form (an exact product) or where the error sum
+// is defined as fused.  Built with -ffp-contract=off so that the compiler
+// adds no other contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum { kMode4over6 = 0, kModeFixed6 = 1, kModeFixed4 = 2 };
+
+// Tensor-scale constant: the encode scale maps the largest magnitude to C, so
+// a block's candidate scale t_b / c stays within the E4M3 range (448) for
+// every candidate the mode uses.
+__host__ __device__ constexpr float mode_constant(int mode) { return mode == kModeFixed6 ? 2688.0f : 1792.0f; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 16 bf16 values (two 16-byte loads) -> fp32.
+__device__ __forceinline__ void unpack16(const uint4& a, const uint4& b, float (&x)[16]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[2 * j] = bf16_lo(w[j]);
+    x[2 * j + 1] = bf16_hi(w[j]);
+  }
+}
+
+// fl(t / 6) for t >= 0 without a division: the product with fl(1/6), its
+// exact residual by a fused multiply-add, and one correction.  Equal to the
+// IEEE quotient for every normal t; for subnormal t (t / 6 < 2^-126) it may
+// differ by an ulp, but both round to the E4M3 code 0.
+__device__ __forceinline__ float div6(float t) {
+  const float inv6 = 0x1.555556p-3f;  // fl(1/6)
+  const float q = t * inv6;
+  const float r = __builtin_fmaf(-q, 6.0f, t);
+  return __builtin_fmaf(r, inv6, q);
+}
+
+// fl(1 / S) for an E4M3 value S, 0 for S = 0: the hardware reciprocal (1 ulp)
+// plus one Newton step whose residual is exact; equal to the IEEE quotient
+// for all 126 positive finite E4M3 values.
+__device__ __forceinline__ float recip_e4m3(float S) {
+  const float r = __builtin_amdgcn_rcpf(S);
+  const float e = __builtin_fmaf(-S, r, 1.0f);
+  const float r2 = __builtin_fmaf(e, r, r);
+  return S > 0.0f ? r2 : 0.0f;
+}
+
+// Both candidate scales of a block with largest |z| = t: byte 0 = E4M3(t/6),
+// byte 1 = E4M3(t/4).
+__device__ __forceinline__ uint32_t candidate_codes(float t) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(div6(t), t * 0.25f, 0, false) & 0xffffu;
+}
+
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte(uint32_t packed) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
+}
+
+// Encode 8 values z[0..7] (already in the encode domain) with reciprocal R:
+// one word of 8 E2M1 codes, element 2j in the low nibble of byte j.
+__device__ __forceinline__ uint32_t encode8(const float* z, float R) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[0] * R, z[1] * R, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[2] * R, z[3] * R, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[4] * R, z[5] * R, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[6] * R, z[7] * R, 1.0f, 3);
+  return w;
+}
+
+// Sum over the 8 elements of (z - v * S)^2, sequential fused accumulation
+// from 0 in element order; v * S is exact, so fma(-v, S, z) is the rounded
+// difference.
+__device__ __forceinline__ float half_error(const float* z, uint32_t w, float S) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2 v;
+    switch (j) {  // the byte selector is an instruction immediate
+      case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+      case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+      case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+      default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+    const float e0 = __builtin_fmaf(-v[0], S, z[2 * j]);
+    acc = __builtin_fmaf(e0, e0, acc);
+    const float e1 = __builtin_fmaf(-v[1], S, z[2 * j + 1]);
+    acc = __builtin_fmaf(e1, e1, acc);
+  }
+  return acc;
+}
+
+struct Encoded16 {
+  uint32_t lo, hi;  // codes of elements 0..7 and 8..15
+  float err_lo, err_hi;
+};
+
+__device__ __forceinline__ Encoded16 encode16(const float (&z)[16], float S, float R) {
+  Encoded16 r;
+  r.lo = encode8(z, R);
+  r.hi = encode8(z + 8, R);
+  r.err_lo = half_error(z, r.lo, S);
+  r.err_hi = half_error(z + 8, r.hi, S);
+  return r;
+}
+
+__device__ __forceinline__ float block_absmax(const float (&z)[16]) {
+  float t = fabsf(z[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) t = fmaxf(t, fabsf(z[i]));
+  return t;
+}
+
+struct Block46 {
+  uint32_t lo, hi;  // 16 packed codes
+  uint32_t scale;   // E4M3 byte
+  uint32_t use4;    // 1 when the +-4 candidate was kept
+};
+
+// Four-Over-Six on one 16-element block in the encode domain: both
+// candidates, each block's fp32 error (two halves added), keep +-4 only when
+// its error is strictly lower.  The fixed modes evaluate one candidate.
+template <int MODE>
+__device__ __forceinline__ Block46 quant_block16(const float (&z)[16]) {
+  const float t = block_absmax(z);
+  const uint32_t s = candidate_codes(t);
+  Block46 out;
+  if (MODE == kModeFixed6) {
+    const float S = e4m3_byte<0>(s);
+    const Encoded16 e = encode16(z, S, recip_e4m3(S));
+    out.lo = e.lo; out.hi = e.hi; out.scale = s & 0xffu; out.use4 = 0;
+  } else if (MODE == kModeFixed4) {
+    const float S = e4m3_byte<1>(s);
+    const Encoded16 e = encode16(z, S, recip_e4m3(S));
+    out.lo = e.lo; out.hi = e.hi; out.scale = s >> 8; out.use4 = 1;
+  } else {
+    const float S6 = e4m3_byte<0>(s), S4 = e4m3_byte<1>(s);
+    const Encoded16 e6 = encode16(z, S6, recip_e4m3(S6));
+    const Encoded16 e4 = encode16(z, S4, recip_e4m3(S4));
+    const float err6 = e6.err_lo + e6.err_hi;
+    const float err4 = e4.err_lo + e4.err_hi;
+    const bool use4 = err4 < err6;
+    out.lo = use4 ? e4.lo : e6.lo;
+    out.hi = use4 ? e4.hi : e6.hi;
+    out.scale = use4 ? (s >> 8) : (s & 0xffu);
+    out.use4 = use4 ? 1u : 0u;
+  }
+  return out;
+}
+
+// Two fp32 -> packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  f2 v = {a, b};
+  b2 h = __builtin_convertvector(v, b2);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
+// Wave-level reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ unsigned wave_sum_u32(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,75 @@
+"""Shared GPU-test plumbing: run the HIP path through the binding, pull the
+results to numpy, and compare them with the CPU oracle on the same inputs."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+import precision_kv_cache_amd as P
+import workloads as W
+
+MEAN_RTOL = 1e-6
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    if t.dtype == torch.bfloat16:
+        return W.bf16_bits(t)
+    return t.detach().cpu().numpy()
+
+
+def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True):
+    """K, V given as numpy bf16 bits [H, T, D] -> GPU outputs as numpy."""
+    k = W.from_bits(kb, "cuda")
+    v = W.from_bits(vb, "cuda")
+    out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts)
+    torch.cuda.synchronize()
+    return {key: t.cpu().numpy() for key, t in out.items()}, out
+
+
+def mean_rule(kb, L, gpu_mean):
+    """Acceptance of the K mean: |m_gpu - m_ref| <= 1e-6 * max(|m_ref|,
+    mean_t |K|) per channel, m_ref the fp64 mean.  Returns the worst ratio."""
+    H, T, D = kb.shape
+    nc = T // L
+    x = O.bf16_to_float(kb).astype(np.float64).reshape(H, nc, L, D)
+    ref = x.mean(2).transpose(1, 0, 2)
+    scale = np.maximum(np.abs(ref), np.abs(x).mean(2).transpose(1, 0, 2))
+    err = np.abs(gpu_mean.astype(np.float64) - ref)
+    ok = err <= MEAN_RTOL * scale
+    ratio = np.where(scale > 0, err / np.where(scale > 0, scale, 1), np.where(err > 0, np.inf, 0))
+    return bool(ok.all()), float(ratio.max())
+
+
+def check_kv(kb, vb, L, mode, res, dev_out=None, nthreads=0, check_dequant=True):
+    """Full parity of one GPU KV call against the oracle fed with the GPU
+    mean: codes, scales, tensor scales and choice counts bit-exact; the
+    dequantized K (mean restored) and V bit-exact."""
+    ok, worst = mean_rule(kb, L, res["k_mean"])
+    assert ok, f"K mean outside 1e-6 rule (worst ratio {worst:.3g})"
+    ref = O.smooth_quantize(kb, vb, L, mode, k_mean=res["k_mean"], nthreads=nthreads)
+    for key in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        a, b = res[key], ref[key]
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            raise AssertionError(f"{key}: {len(bad)} mismatches, first at {bad[:5].tolist()}")
+    for key in ("k_tensor_scale", "v_tensor_scale"):
+        assert np.array_equal(res[key].view(np.uint32), ref[key].view(np.uint32)), key
+    if "choice_counts" in res:
+        n = res["k_codes"].size // 8
+        assert res["choice_counts"].tolist() == [[n - ref["k_use4"], ref["k_use4"]], [n - ref["v_use4"], ref["v_use4"]]]
+    if check_dequant and dev_out is not None:
+        dk = P.nvfp4_dequantize(dev_out["k_codes"], dev_out["k_scales"], dev_out["k_tensor_scale"],
+                                dev_out["k_mean"], L)
+        dv = P.nvfp4_dequantize(dev_out["v_codes"], dev_out["v_scales"], dev_out["v_tensor_scale"], None, L)
+        torch.cuda.synchronize()
+        rk = O.dequantize(ref["k_codes"], ref["k_scales"], ref["k_tensor_scale"], res["k_mean"], L, nthreads)
+        rv = O.dequantize(ref["v_codes"], ref["v_scales"], ref["v_tensor_scale"], None, L, nthreads)
+        assert np.array_equal(to_np(dk), rk), "dequantized K differs"
+        assert np.array_equal(to_np(dv), rv), "dequantized V differs"
+    return ref

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+headers declare, and rejects bad arguments with the documented status before
+any HIP call (so these run on a machine with no GPU, with fake pointers that
+are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import precision_kv_cache_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("nvfp4kv.h", "nvfp4kv_diag.h")]
+
+OK, NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, MODE, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        txt = open(h).read()
+        names += re.findall(r"NVFP4KV_API\s+[\w\s\*]+?\b(nvfp4_\w+)\s*\(", txt)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 13
+    L = P.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (nvfp4_\w+)", nm))
+    assert set(names) <= exported, set(names) - exported
+    # nothing else leaks out under the nvfp4_ prefix
+    assert exported == set(names), exported - set(names)
+
+
+def test_status_strings():
+    for code in (OK, NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, MODE, HIP):
+        s = P.nvfp4_status_string(code)
+        assert s.startswith("NVFP4")
+    assert "unknown" in P.nvfp4_status_string(12345)
+
+
+def test_workspace_sizes():
+    assert P.nvfp4_kv_workspace_bytes(24, 7040, 128, 7040) > 0
+    assert P.nvfp4_kv_workspace_bytes(24, 7040, 128, 7040) % 256 == 0
+    assert P.nvfp4_kv_workspace_bytes(24, 56320, 128, 7040) > P.nvfp4_kv_workspace_bytes(24, 7040, 128, 7040)
+    for bad in ((24, 7040, 100, 7040), (24, 7041, 128, 7040), (-1, 10, 16, 10), (1, 16, 8192, 16), (1, 16, 16, 0)):
+        assert P.nvfp4_kv_workspace_bytes(*bad) == 0, bad
+    assert P.lib().nvfp4_quantize_1d_workspace_bytes(16, 48) > 0
+    assert P.lib().nvfp4_quantize_2d_workspace_bytes(24, 48) == 0  # rows % 16
+
+
+FAKE = 0x7f0000000000  # 256-byte aligned, never dereferenced
+
+
+def _kvq(k=FAKE, v=FAKE + (1 << 30), H=2, T=64, D=32, L=32, mode=0, kc=FAKE + (2 << 30), vc=FAKE + (3 << 30),
+         ks=FAKE + (4 << 30), vs=FAKE + (5 << 30), kt=FAKE + (6 << 30), vt=FAKE + (7 << 30), km=FAKE + (8 << 30),
+         cc=None, ws=FAKE + (9 << 30), wsb=1 << 20):
+    V = ctypes.c_void_p
+    return P.lib().nvfp4_kv_smooth_quantize(V(k), V(v), H, T, D, L, mode, V(kc), V(vc), V(ks), V(vs), V(kt), V(vt),
+                                            V(km), V(cc), V(ws), wsb, None)
+
+
+def test_kv_quantize_argument_errors():
+    assert _kvq(k=None) == NULL
+    assert _kvq(km=None) == NULL
+    assert _kvq(D=40) == SHAPE
+    assert _kvq(T=65) == SHAPE
+    assert _kvq(L=0) == SHAPE
+    assert _kvq(H=-1) == SHAPE
+    assert _kvq(D=8192) == SHAPE
+    assert _kvq(mode=3) == MODE
+    assert _kvq(k=FAKE + 8) == ALIGN
+    assert _kvq(kc=(FAKE + (2 << 30)) + 4) == ALIGN
+    assert _kvq(km=(FAKE + (8 << 30)) + 4) == ALIGN
+    assert _kvq(ws=(FAKE + (9 << 30)) + 128) == ALIGN
+    assert _kvq(ws=None) == WORKSPACE
+    assert _kvq(wsb=16) == WORKSPACE
+    assert _kvq(vc=FAKE + 64) == ALIAS            # output inside input K
+    assert _kvq(vc=FAKE + (2 << 30) + 256) == ALIAS  # two outputs overlap
+    assert _kvq(ws=FAKE + (1 << 30)) == ALIAS     # workspace inside V
+    assert _kvq(cc=FAKE + (5 << 30)) == ALIAS     # counts inside v_scales
+
+
+def test_empty_calls_are_no_ops():
+    assert _kvq(H=0, k=None, v=None) == OK
+    assert _kvq(T=0, k=None) == OK
+    assert P.lib().nvfp4_dequantize(None, None, None, None, 0, 64, 32, 32, None, None) == OK
+    assert P.lib().nvfp4_quantize_1d(None, 0, 32, 0, 1, 0, None, None, None, None, 0, None) == OK
+    assert P.lib().nvfp4_quantize_2d(None, 0, 32, 0, None, None, None, None, 0, None) == OK
+
+
+def test_dequant_and_1d_2d_argument_errors():
+    V = ctypes.c_void_p
+    L = P.lib()
+    assert L.nvfp4_dequantize(None, V(FAKE), V(FAKE), None, 1, 32, 32, 32, V(FAKE), None) == NULL
+    assert L.nvfp4_dequantize(V(FAKE), V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), None, 1, 32, 40, 32,
+                              V(FAKE + (3 << 30)), None) == SHAPE
+    assert L.nvfp4_dequantize(V(FAKE), V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), None, 1, 32, 32, 32,
+                              V(FAKE + 16), None) == ALIAS
+    assert L.nvfp4_dequantize(V(FAKE), V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), V(FAKE + (4 << 30) + 4), 1, 32,
+                              32, 32, V(FAKE + (3 << 30)), None) == ALIGN
+    args1d = [V(FAKE), 16, 32, 0, 1, 0, V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), V(FAKE + (3 << 30)),
+              V(FAKE + (4 << 30)), 256, None]
+    a = list(args1d); a[2] = 33
+    assert L.nvfp4_quantize_1d(*a) == SHAPE
+    a = list(args1d); a[3] = 7
+    assert L.nvfp4_quantize_1d(*a) == MODE
+    a = list(args1d); a[10] = 8
+    assert L.nvfp4_quantize_1d(*a) == WORKSPACE
+    a = list(args1d); a[6] = V(FAKE + 32)
+    assert L.nvfp4_quantize_1d(*a) == ALIAS
+    assert L.nvfp4_quantize_2d(V(FAKE), 24, 32, 0, V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), V(FAKE + (3 << 30)),
+                               V(FAKE + (4 << 30)), 256, None) == SHAPE
+    assert L.nvfp4_dequantize_2d(V(FAKE), V(FAKE + (1 << 30)), None, 32, 32, V(FAKE + (2 << 30)), None) == NULL
+    assert L.nvfp4_diag_e2m1_encode(None, 10, None, None) == NULL
+    assert L.nvfp4_diag_candidates(None, -1, None, None, None) == SHAPE
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(P, "_lib", None)
+    monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="HIP library missing"):
+        P.lib()

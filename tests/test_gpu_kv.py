@@ -1,0 +1,169 @@
+"""GPU parity of the KV path (nvfp4_kv_smooth_quantize / nvfp4_dequantize)
+against the CPU oracle, through the C ABI, on the seeded workloads and on
+ragged and degenerate shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import precision_kv_cache_amd as P
+import workloads as W
+from gpu_helpers import check_kv, gpu_kv, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    P.lib()  # raises if the HIP library is missing
+
+
+@pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
+def test_tiny_workload(mode):
+    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode)
+    k, v = W.gaussian_kv(W.TINY, W.SEED_TINY)
+    kb, vb = W.bf16_bits(k), W.bf16_bits(v)
+    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode)
+    check_kv(kb, vb, W.TINY.chunk_len, mode, res, dev)
+
+
+def test_tiny_matches_golden_fixture():
+    say("tiny KV vs golden fixture")
+    g = np.load(__import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "tiny_kv_oracle.npz"))
+    res, _ = gpu_kv(g["k"], g["v"], W.TINY.chunk_len)
+    if np.array_equal(res["k_mean"], g["k_mean"]):  # same mean -> same bytes as the stored oracle run
+        for key in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tensor_scale", "v_tensor_scale"):
+            assert np.array_equal(res[key], g[key]), key
+
+
+def test_one_chunk_workload():
+    s = W.ONE_CHUNK
+    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK)
+    k, v = W.gaussian_kv(s, W.SEED_ONE_CHUNK)
+    kb, vb = W.bf16_bits(k), W.bf16_bits(v)
+    res, dev = gpu_kv(kb, vb, s.chunk_len)
+    ref = check_kv(kb, vb, s.chunk_len, O.MODE_4OVER6, res, dev)
+    assert 0 < ref["k_use4"] < res["k_codes"].size // 8
+
+
+def test_heavy_tail_workload():
+    s = W.ONE_CHUNK
+    say("heavy-tail KV", s, "seed", W.SEED_HEAVY)
+    k, v = W.heavy_tail_kv(s, W.SEED_HEAVY)
+    kb, vb = W.bf16_bits(k), W.bf16_bits(v)
+    for mode in (O.MODE_4OVER6, O.MODE_FIXED6):
+        say("  mode", mode)
+        res, dev = gpu_kv(kb, vb, s.chunk_len, mode)
+        check_kv(kb, vb, s.chunk_len, mode, res, dev)
+
+
+@pytest.mark.parametrize("layer", [0, 29])
+def test_full_cache_layer_sampled(layer):
+    """A full-size layer of the 8-chunk cache ([24, 56320, 128], the launch
+    configuration the benchmark times), drawn on the GPU; chunks 0, 3 and 7
+    are checked completely against the oracle, and the whole layer's outputs
+    against properties that hold at any size."""
+    s = W.CACHE_LAYER
+    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer))
+    k, v = W.gaussian_kv(s, W.cache_layer_seed(layer), device="cuda")
+    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True)
+    dk = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len)
+    dv = P.nvfp4_dequantize(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, s.chunk_len)
+    torch.cuda.synchronize()
+    L = s.chunk_len
+    for c in (0, 3, 7):
+        say("  chunk", c)
+        sl = slice(c * L, (c + 1) * L)
+        kb, vb = W.bf16_bits(k[:, sl]), W.bf16_bits(v[:, sl])
+        res = {"k_mean": out["k_mean"][c:c + 1].cpu().numpy()}
+        for key in ("k_codes", "v_codes", "k_scales", "v_scales"):
+            res[key] = out[key][:, sl].cpu().numpy()
+        res["k_tensor_scale"] = out["k_tensor_scale"][c:c + 1].cpu().numpy()
+        res["v_tensor_scale"] = out["v_tensor_scale"][c:c + 1].cpu().numpy()
+        ref = check_kv(kb, vb, L, O.MODE_4OVER6, res)
+        rk = O.dequantize(ref["k_codes"], ref["k_scales"], ref["k_tensor_scale"], res["k_mean"], L)
+        rv = O.dequantize(ref["v_codes"], ref["v_scales"], ref["v_tensor_scale"], None, L)
+        assert np.array_equal(to_np(dk[:, sl]), rk)
+        assert np.array_equal(to_np(dv[:, sl]), rv)
+    # any-size properties: counts cover every block; reconstruction is close
+    cc = out["choice_counts"].cpu()
+    nblk = k.numel() // 16
+    assert cc.sum(1).tolist() == [nblk, nblk]
+    for x, xh, name in ((k, dk, "K"), (v, dv, "V")):
+        xf, xhf = x.float(), xh.float()
+        rel = ((xf - xhf) ** 2).mean() / (xf ** 2).mean()
+        say("  relative MSE", name, float(rel))
+        assert float(rel) < 0.02
+
+
+@pytest.mark.parametrize("H,T,D,L", [
+    (3, 300, 64, 100),   # ragged tiles: 100-row chunks, 3 chunks
+    (2, 96, 48, 32),     # 3 blocks per row: 255-thread workgroups
+    (1, 64, 80, 64),     # 5 blocks per row
+    (5, 513, 16, 513),   # one block per row, odd length
+    (2, 130, 256, 65),   # 16 blocks per row
+    (1, 40, 4096, 8),    # widest rows
+    (2, 7, 32, 1),       # one token per chunk: K' = 0 everywhere
+])
+def test_ragged_and_odd_shapes(H, T, D, L):
+    say("shape", (H, T, D, L))
+    shape = W.KVShape(H, T, D, L)
+    k, v = W.gaussian_kv(shape, 4242 + H * T + D)
+    kb, vb = W.bf16_bits(k), W.bf16_bits(v)
+    res, dev = gpu_kv(kb, vb, L)
+    check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
+    if L == 1:
+        assert not res["k_codes"].any() and not res["k_scales"].any() and not res["k_tensor_scale"].any()
+
+
+def _bits(a):
+    return W.bf16_bits(torch.as_tensor(np.asarray(a, np.float32)).to(torch.bfloat16))
+
+
+def test_degenerate_values():
+    rng = np.random.default_rng(77)
+    H, T, D, L = 2, 64, 32, 32
+    cases = {
+        "zeros": (np.zeros((H, T, D)), np.zeros((H, T, D))),
+        "signed zeros": (-np.zeros((H, T, D)), -np.zeros((H, T, D))),
+        "constant channels": (np.broadcast_to(rng.standard_normal((H, 1, D)), (H, T, D)),
+                              np.full((H, T, D), -3.5)),
+        "subnormal elements": (np.where(rng.random((H, T, D)) < 0.2, 3e-39, rng.standard_normal((H, T, D))),
+                               np.where(rng.random((H, T, D)) < 0.3, -5e-39, rng.standard_normal((H, T, D)) * 1e-3)),
+        "huge": (rng.standard_normal((H, T, D)) * 1e30, rng.standard_normal((H, T, D)) * 3e37),
+        "tiny": (rng.standard_normal((H, T, D)) * 1e-20, rng.standard_normal((H, T, D)) * 1e-30),
+        "one spike": (np.where(rng.random((H, T, D)) < 1e-3, 1e4, 0.0), np.eye(T, D)[None].repeat(H, 0)),
+    }
+    for name, (k, v) in cases.items():
+        say("degenerate:", name)
+        kb, vb = _bits(k), _bits(v)
+        res, dev = gpu_kv(kb, vb, L)
+        check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
+
+
+def test_deterministic_and_stream_ordered():
+    s = W.KVShape(4, 2048, 128, 1024)
+    say("determinism", s)
+    k, v = W.gaussian_kv(s, 99, device="cuda")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        a = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True)
+        b = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True)
+    side.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_dequant_without_mean_and_empty():
+    s = W.KVShape(2, 128, 64, 64)
+    say("dequant paths", s)
+    k, v = W.gaussian_kv(s, 5, device="cuda")
+    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len)
+    d0 = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], None, s.chunk_len)
+    torch.cuda.synchronize()
+    ref = O.dequantize(out["k_codes"].cpu().numpy(), out["k_scales"].cpu().numpy(),
+                       out["k_tensor_scale"].cpu().numpy(), None, s.chunk_len)
+    assert np.array_equal(to_np(d0), ref)
+    e = torch.empty(0, 64, 32, dtype=torch.bfloat16, device="cuda")
+    r = P.nvfp4_kv_smooth_quantize(e, e.clone(), 64)
+    assert r["k_codes"].numel() == 0
