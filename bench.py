@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 4/6 KV-cache path on one MI355X.
+
+Workload (one step): the full cache of 30 layers, K and V bf16 [24, 56320,
+128] per layer (8 chunks of 8 frames x 880 tokens): every layer is
+smooth-quantized chunk by chunk (nvfp4_kv_smooth_quantize), then the whole
+cache is dequantized back to bf16 (nvfp4_dequantize, K with its means).
+Inputs are resident in HBM before the timed region; they are drawn once on
+the GPU from seeded generators (workloads/).  The cache (20.8 GB of bf16) is
+far larger than the 256 MB Infinity Cache, so every step is a cold pass.
+
+value = algorithmic bytes per step / time per step: every bf16 element read
+once and written once, codes (0.5 B) and E4M3 scales (1/16 B) written once
+and read once, plus the per-chunk means and tensor scales.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "NVFP4 4/6 KV quantize GB/s (bytes in+out) and % of MI355X HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=30, help="cache layers (the workload has 30)")
+    ap.add_argument("--mode", type=int, default=0, help="0 = 4/6, 1 = fixed 6, 2 = fixed 4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
+    return ap.parse_args()
+
+
+def kv_bytes(H, T, D, L, with_mean):
+    """Algorithmic bytes of one tensor's quantize (or dequantize): bf16 in,
+    codes and scales out (or the reverse), plus tensor scales and means."""
+    n = H * T * D
+    nc = T // L
+    b = 2 * n + n // 2 + n // 16 + 4 * nc
+    if with_mean:
+        b += 4 * nc * H * D
+    return b
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this path runs on a single MI355X "
+              f"(asked for --gpus {a.gpus}, WORLD_SIZE {world}); run it with --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()  # fail loudly without the HIP library
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.CACHE_LAYER
+    H, T, D, L = s.H, s.T, s.D, s.chunk_len
+    nlayers = a.layers
+
+    t0 = time.time()
+    ks, vs = [], []
+    for l in range(nlayers):
+        k, v = W.gaussian_kv(s, W.cache_layer_seed(l), device=dev)
+        ks.append(k)
+        vs.append(v)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    nc = T // L
+    outs, deq = [], []
+    for l in range(nlayers):
+        outs.append({
+            "k_codes": torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
+            "v_codes": torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
+            "k_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
+            "v_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
+            "k_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
+            "v_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
+            "k_mean": torch.empty(nc, H, D, dtype=torch.float32, device=dev),
+        })
+        deq.append((torch.empty(H, T, D, dtype=torch.bfloat16, device=dev),
+                    torch.empty(H, T, D, dtype=torch.bfloat16, device=dev)))
+    counts = torch.zeros(2, 2, dtype=torch.int64, device=dev)
+    ws = torch.empty(P.nvfp4_kv_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def quant(l, ev=None):
+        o = outs[l]
+        if ev is not None:
+            ev[0].record(stream)
+        P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def dequant(l, ev=None):
+        o = outs[l]
+        if ev is not None:
+            ev[0].record(stream)
+        P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, out=deq[l][0],
+                           stream=stream)
+        P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, out=deq[l][1],
+                           stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def step(qev=None, dev_ev=None):
+        for l in range(nlayers):
+            quant(l, None if qev is None else qev[l])
+        for l in range(nlayers):
+            dequant(l, None if dev_ev is None else dev_ev[l])
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: one event pair around the whole run, plus an event pair
+    # around every library call of the last step (same stream) for the
+    # per-call durations the roofline uses
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    qev = [(E(), E()) for _ in range(nlayers)]
+    dev_ev = [(E(), E()) for _ in range(nlayers)]
+    start, stop = E(), E()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(a.steps):
+        last = i == a.steps - 1
+        step(qev if last else None, dev_ev if last else None)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / a.steps
+    q_ms = sum(e0.elapsed_time(e1) for e0, e1 in qev) / nlayers    # one layer's quantize call (K and V)
+    d_ms = sum(e0.elapsed_time(e1) for e0, e1 in dev_ev) / nlayers  # one layer's dequantize calls (K and V)
+
+    qbytes_layer = kv_bytes(H, T, D, L, True) + kv_bytes(H, T, D, L, False)
+    dbytes_layer = qbytes_layer
+    step_bytes = nlayers * (qbytes_layer + dbytes_layer)
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    q_gbps = qbytes_layer / (q_ms * 1e-3) / 1e9
+    d_gbps = dbytes_layer / (d_ms * 1e-3) / 1e9
+
+    # 4/6 choice histogram on one layer (outside the timed region)
+    o = P.nvfp4_kv_smooth_quantize(ks[0], vs[0], L, a.mode, choice_counts=True)
+    torch.cuda.synchronize()
+    cc = o["choice_counts"].cpu().tolist()
+
+    # device copy bandwidth of a 4 GiB buffer, for context
+    src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = E(), E()
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    dominant = "quantize" if q_ms >= d_ms else "dequantize"
+    ach = q_gbps if dominant == "quantize" else d_gbps
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "full 8-chunk KV cache: 30 layers x K,V bf16 [24 heads, 56320 tokens, 128], "
+                        "chunks of 7040 tokens; 4/6 smooth-quantize every layer, then dequantize the cache",
+            "layers": nlayers, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
+            "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": step_bytes,
+        },
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "quantize_GBps": round(q_gbps, 1),
+        "dequantize_GBps": round(d_gbps, 1),
+        "quantize_call_ms": round(q_ms, 4),
+        "dequantize_call_ms": round(d_ms, 4),
+        "choice_counts_layer0": {"K": {"kept6": cc[0][0], "kept4": cc[0][1]},
+                                 "V": {"kept6": cc[1][0], "kept4": cc[1][1]}},
+        "d2d_copy_GBps": round(copy_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "nvfp4_kv_smooth_quantize (one layer, K and V)" if dominant == "quantize"
+            else "nvfp4_dequantize (one layer, K and V)",
+            "achieved": round(ach, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": qbytes_layer,
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(ks, vs, L, mode, target_s):
+    """The oracle as it stands, on the host cores: K and V smooth-quantize +
+    dequantize of whole chunks, layer 0 chunk 0 onwards, until about
+    target_s seconds of work."""
+    import oracle as O
+    import workloads as W
+
+    nt = O.default_threads()
+    H, T, D = ks[0].shape
+    done, t_total, nbytes, last = 0, 0.0, 0, (0, 0)
+    for l in range(len(ks)):
+        for c in range(T // L):
+            kb = W.bf16_bits(ks[l][:, c * L:(c + 1) * L])
+            vb = W.bf16_bits(vs[l][:, c * L:(c + 1) * L])
+            t0 = time.perf_counter()
+            r = O.smooth_quantize(kb, vb, L, mode, nthreads=nt)
+            O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], r["k_mean"], L, nthreads=nt)
+            O.dequantize(r["v_codes"], r["v_scales"], r["v_tensor_scale"], None, L, nthreads=nt)
+            t_total += time.perf_counter() - t0
+            done += 1
+            last = (l, c)
+            nbytes += 2 * (kv_bytes(H, L, D, L, True) + kv_bytes(H, L, D, L, False))
+            if t_total >= target_s:
+                break
+        if t_total >= target_s:
+            break
+    return {"value": round(nbytes / t_total / 1e9, 3), "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "sample": f"{done} chunks of [24, 7040, 128] K and V (layer 0 chunk 0 to layer {last[0]} chunk "
+                      f"{last[1]}): smooth-quantize + dequantize",
+            "seconds": round(t_total, 2)}
+
+
+if __name__ == "__main__":
+    main()

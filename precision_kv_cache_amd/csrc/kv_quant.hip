@@ -1,6 +1,6 @@
 // kv_quant.hip -- per-chunk K smoothing + NVFP4 4/6 quantization of a KV
-// cache layer, and its dequantize (LongLive-2.0 summary page: inference
-// pipeline, step 7; full-stack NVFP4).
+// cache layer (two-pass form), and its dequantize (LongLive-2.0 summary
+// page: inference pipeline, step 7; full-stack NVFP4).
 //
 // Data layout (all row-major):
 //   K, V        bf16 [H, T, D]; chunk c of head h = rows c*L .. c*L+L-1 of
@@ -9,25 +9,29 @@
 //               (h, t, D/16 column); one lane of a workgroup owns one block.
 //   k_mean      [nc, H, D] fp32; tensor scales [nc] fp32 per tensor.
 //
-// Three kernels per group of chunks (the group is sized so that its K and V
-// stay in the 256 MB Infinity Cache between the first and the last pass):
-//   kv_stats    per (chunk, head, row tile): K channel sum (fp64), max, min;
-//               V largest magnitude.                      -> workspace
-//   kv_finalize per (chunk, head): channel mean m = fp32(sum / L) and the
-//               head's largest |fl(K - m)| = max(fl(max - m), fl(m - min))
-//               (exact: rounded subtraction is monotone); V head maximum.
-//   kv_quant    per (chunk, head, row tile): tensor scale from the heads'
-//               maxima, then smoothing, the 4/6 block quantizer, stores.
+// Two passes over each group of chunks (the group is sized so that its K
+// and V could stay in the Infinity Cache between the passes):
+//   kv_stats    per (chunk, tensor, head, row tile): K channel sum (fp64),
+//               max, min, or V largest magnitude -> workspace; the last tile
+//               of a head (atomic counter) reduces the head: mean
+//               m = fp32(sum / L) and the head's largest |fl(K - m)| =
+//               max(fl(max - m), fl(m - min)) (exact: rounded subtraction is
+//               monotone), or the V head maximum.
+//   kv_quant    per (chunk, tensor, head, row tile): tensor scale from the
+//               heads' maxima, smoothing, the 4/6 block quantizer, stores.
+// The two run as separate kernels so that the VALU-heavy quantize kernel
+// keeps its own (small) register and LDS footprint and high occupancy.
 // Thread mapping: NB * RP working threads (NB = D/16 blocks per row,
 // RP = 256/NB rows per pass), rounded up to whole waves (the extra lanes
-// only contribute identity values to the wave reductions); thread t owns
-// column t % NB for all its rows, so its 16 channel means stay in
-// registers, and consecutive threads read consecutive 32-byte blocks (2 KB
-// contiguous per wave and pass).
+// only contribute identity values to the reductions); thread t owns column
+// t % NB for all its rows, so its 16 channel means stay in registers, and
+// consecutive threads read consecutive 32-byte blocks (2 KB contiguous per
+// wave and pass).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "host_common.hpp"
+#include "kv_fused.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4kv.h"
 
@@ -36,7 +40,8 @@ namespace nvfp4 {
 constexpr int kMaxThreads = 256;
 constexpr int kStatsPasses = 16;  // rows per stats tile = RP * kStatsPasses
 constexpr int kQuantPasses = 4;   // rows per quant / dequant tile = RP * kQuantPasses
-constexpr size_t kGroupBytes = size_t(96) << 20;  // K+V bytes per launch group
+constexpr int kBatch = 4;         // rows whose loads are issued together
+constexpr size_t kGroupBytes = size_t(96) << 20;  // K+V bytes per chunk group
 
 struct KVGeom {
   int H, T, D, L, nc;
@@ -59,7 +64,8 @@ static KVGeom kv_geom(int H, int T, int D, int L) {
 }
 
 struct KVWorkspace {
-  size_t psum, pmax, pmin, pvabs, hamax, total;  // byte offsets
+  size_t psum, pmax, pmin, pvabs, hamax, counters, total;  // byte offsets
+  int n_counters;
 };
 
 static KVWorkspace kv_workspace_layout(const KVGeom& g) {
@@ -71,6 +77,9 @@ static KVWorkspace kv_workspace_layout(const KVGeom& g) {
   w.pmin = off;  off = align_up(off + nch * sizeof(float), 256);
   w.pvabs = off; off = align_up(off + (size_t)g.nc * g.H * g.nst * sizeof(float), 256);
   w.hamax = off; off = align_up(off + (size_t)2 * g.nc * g.H * sizeof(float), 256);
+  w.counters = off;  // one per (chunk, tensor, head)
+  w.n_counters = 2 * g.nc * g.H;
+  off = align_up(off + (size_t)w.n_counters * sizeof(unsigned), 256);
   w.total = off;
   return w;
 }
@@ -81,49 +90,61 @@ struct KVParams {
   uint8_t* scales[2];
   float* tscale[2];
   float* kmean;
-  double* psum;
-  float* pmax;
-  float* pmin;
-  float* pvabs;
-  float* hamax;  // [2][nc][H]
+  double* psum;   // [nc][H][nst][D]
+  float* pmax;    // [nc][H][nst][D]
+  float* pmin;    // [nc][H][nst][D]
+  float* pvabs;   // [nc][H][nst]
+  float* hamax;   // [2][nc][H]
+  unsigned* cnt;  // [nc][2][H]
   unsigned long long* choice;
-  int H, T, D, L, nc, NB, RP, rows_s, rows_q, nst;
-  int chunk0;
+  int H, T, D, L, nc, NB, RP, rows_s, rows_q, nst, nqt;
+  int s0, s1;  // chunks whose statistics this launch computes
+  int q0, q1;  // chunks this launch quantizes
 };
 
 // ---------------------------------------------------------------- stats ---
 
-__global__ __launch_bounds__(kMaxThreads) void kv_stats_kernel(KVParams p) {
-  // LDS for the cross-thread reduction: 16 channel slots x up to 256 threads,
-  // transposed ([slot][thread], +1 pad) so both phases avoid bank conflicts.
-  __shared__ double sh[16 * (kMaxThreads + 1)];
-  const int ts = blockIdx.x, h = blockIdx.y, tau = blockIdx.z & 1, c = p.chunk0 + (int)(blockIdx.z >> 1);
+__device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, double* sh, float* shw,
+                              unsigned* sh_flag) {
   const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
   const bool active = roff < p.RP;
   const int r0 = ts * p.rows_s;
   const int r1 = active ? min(r0 + p.rows_s, p.L) : r0;  // idle lanes take no rows
   const uint16_t* base = p.x[tau] + ((size_t)h * p.T + (size_t)c * p.L) * p.D + (size_t)col * 16;
+  const size_t hb = ((size_t)c * p.H + h) * p.nst;
+  uint32_t done = 0;  // completion of this thread's published partials
 
   if (tau == 0) {
     double s[16];
     float mx[16], mn[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) { s[i] = 0.0; mx[i] = -INFINITY; mn[i] = INFINITY; }
-    for (int r = r0 + roff; r < r1; r += p.RP) {
-      const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)r * p.D);
-      const uint4 a = src[0], b = src[1];
-      float x[16];
-      unpack16(a, b, x);
+    for (int rb = r0 + roff; rb < r1; rb += kBatch * p.RP) {
+      uint4 a[kBatch], b[kBatch];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] += (double)x[i];
-        mx[i] = fmaxf(mx[i], x[i]);
-        mn[i] = fminf(mn[i], x[i]);
+      for (int q = 0; q < kBatch; ++q) {
+        const int r = rb + q * p.RP;
+        if (r < r1) {
+          a[q] = load_nt(base + (size_t)r * p.D);
+          b[q] = load_nt(base + (size_t)r * p.D + 8);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (rb + q * p.RP >= r1) continue;
+        float x[16];
+        unpack16(a[q], b[q], x);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[i] += (double)x[i];
+          mx[i] = fmaxf(mx[i], x[i]);
+          mn[i] = fminf(mn[i], x[i]);
+        }
       }
     }
+    // cross-thread reduction through LDS ([slot][thread] + pad)
     const int stride = kMaxThreads + 1;
-    const size_t pbase = (((size_t)c * p.H + h) * p.nst + ts) * p.D;
-    // sums: thread d reduces channel d over the RP row groups, in order
+    const size_t pbase = (hb + ts) * p.D;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sh[i * stride + tid] = s[i];
     __syncthreads();
@@ -131,83 +152,126 @@ __global__ __launch_bounds__(kMaxThreads) void kv_stats_kernel(KVParams p) {
       const int cc = d >> 4, i = d & 15;
       double acc = 0.0;
       for (int q = 0; q < p.RP; ++q) acc += sh[i * stride + q * p.NB + cc];
-      p.psum[pbase + d] = acc;
+      publish(&p.psum[pbase + d], acc, done);
     }
     __syncthreads();
     float* shf = reinterpret_cast<float*>(sh);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) shf[i * stride + tid] = mx[i];
-    __syncthreads();
-    for (int d = tid; d < p.D; d += blockDim.x) {
-      const int cc = d >> 4, i = d & 15;
-      float acc = -INFINITY;
-      for (int q = 0; q < p.RP; ++q) acc = fmaxf(acc, shf[i * stride + q * p.NB + cc]);
-      p.pmax[pbase + d] = acc;
+    for (int i = 0; i < 16; ++i) {
+      shf[i * stride + tid] = mx[i];
+      shf[(16 + i) * stride + tid] = mn[i];
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) shf[i * stride + tid] = mn[i];
-    __syncthreads();
     for (int d = tid; d < p.D; d += blockDim.x) {
       const int cc = d >> 4, i = d & 15;
-      float acc = INFINITY;
-      for (int q = 0; q < p.RP; ++q) acc = fminf(acc, shf[i * stride + q * p.NB + cc]);
-      p.pmin[pbase + d] = acc;
+      float a = -INFINITY, b = INFINITY;
+      for (int q = 0; q < p.RP; ++q) {
+        a = fmaxf(a, shf[i * stride + q * p.NB + cc]);
+        b = fminf(b, shf[(16 + i) * stride + q * p.NB + cc]);
+      }
+      publish(&p.pmax[pbase + d], a, done);
+      publish(&p.pmin[pbase + d], b, done);
     }
   } else {
     float am = 0.0f;
-    for (int r = r0 + roff; r < r1; r += p.RP) {
-      const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)r * p.D);
-      const uint4 a = src[0], b = src[1];
-      float x[16];
-      unpack16(a, b, x);
+    for (int rb = r0 + roff; rb < r1; rb += kBatch * p.RP) {
+      uint4 a[kBatch], b[kBatch];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+      for (int q = 0; q < kBatch; ++q) {
+        const int r = rb + q * p.RP;
+        if (r < r1) {
+          a[q] = load_nt(base + (size_t)r * p.D);
+          b[q] = load_nt(base + (size_t)r * p.D + 8);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (rb + q * p.RP >= r1) continue;
+        float x[16];
+        unpack16(a[q], b[q], x);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+      }
     }
     am = wave_max(am);
-    float* shf = reinterpret_cast<float*>(sh);
-    if ((tid & 63) == 0) shf[tid >> 6] = am;
+    if ((tid & 63) == 0) shw[tid >> 6] = am;
     __syncthreads();
     if (tid == 0) {
       float a = 0.0f;
-      for (int w = 0; w < (int)((blockDim.x + 63) / 64); ++w) a = fmaxf(a, shf[w]);
-      p.pvabs[((size_t)c * p.H + h) * p.nst + ts] = a;
+      for (int w = 0; w < (int)(blockDim.x / 64); ++w) a = fmaxf(a, shw[w]);
+      publish(&p.pvabs[hb + ts], a, done);
     }
   }
-}
 
-// ------------------------------------------------------------- finalize ---
-
-__global__ __launch_bounds__(kMaxThreads) void kv_finalize_kernel(KVParams p) {
-  __shared__ float shw[kMaxThreads / 64];
-  const int h = blockIdx.x, c = p.chunk0 + (int)blockIdx.y, tau = blockIdx.z;
-  const int tid = threadIdx.x;
+  // The last tile of (chunk, tensor, head) reduces the head.
+  wait_published(done);
+  __syncthreads();  // every thread's exchanges completed before thread 0 counts
+  if (tid == 0) *sh_flag = add_agent(&p.cnt[((size_t)c * 2 + tau) * p.H + h], 1u) == (unsigned)(p.nst - 1);
+  __syncthreads();
+  if (!*sh_flag) return;
   float a = 0.0f;
   if (tau == 0) {
-    for (int d = tid; d < p.D; d += blockDim.x) {
-      double s = 0.0;
-      float mx = -INFINITY, mn = INFINITY;
-      for (int ts = 0; ts < p.nst; ++ts) {
-        const size_t i = (((size_t)c * p.H + h) * p.nst + ts) * p.D + d;
-        s += p.psum[i];
-        mx = fmaxf(mx, p.pmax[i]);
-        mn = fminf(mn, p.pmin[i]);
+    // thread t reduces channel t % D over tiles t / D, t / D + NSPLIT, ...
+    // (loads issued in batches), then the parts are combined in order
+    const int nsplit = (int)blockDim.x >= p.D ? (int)blockDim.x / p.D : 1;
+    const int stride = kMaxThreads + 1;
+    float* shf = reinterpret_cast<float*>(sh + 2 * stride);
+    for (int d0 = 0; d0 < p.D; d0 += (int)blockDim.x) {
+      const int d = d0 + tid % (p.D < (int)blockDim.x ? p.D : (int)blockDim.x);
+      const int part = p.D < (int)blockDim.x ? tid / p.D : 0;
+      double sum = 0.0;
+      float mxv = -INFINITY, mnv = INFINITY;
+      if (part < nsplit && d < p.D) {
+        for (int jb = part; jb < p.nst; jb += nsplit * 8) {
+          double ps[8];
+          float px[8], pn[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int jj = jb + q * nsplit;
+            if (jj < p.nst) {
+              const size_t i = (hb + jj) * p.D + d;
+              ps[q] = fetch(&p.psum[i]); px[q] = fetch(&p.pmax[i]); pn[q] = fetch(&p.pmin[i]);
+            } else {
+              ps[q] = 0.0; px[q] = -INFINITY; pn[q] = INFINITY;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) { sum += ps[q]; mxv = fmaxf(mxv, px[q]); mnv = fminf(mnv, pn[q]); }
+        }
       }
-      const float m = (float)(s / (double)p.L);
-      p.kmean[((size_t)c * p.H + h) * p.D + d] = m;
-      const float up = mx - m, dn = m - mn;  // each one fp32 rounding
-      a = fmaxf(a, fmaxf(up, dn));
+      __syncthreads();
+      sh[tid] = sum;
+      shf[tid] = mxv;
+      shf[stride + tid] = mnv;
+      __syncthreads();
+      const int nd = min((int)blockDim.x, p.D - d0);
+      if (tid < nd) {
+        const int dd = p.D < (int)blockDim.x ? tid : tid;
+        double s2 = 0.0;
+        float x2 = -INFINITY, n2 = INFINITY;
+        const int width = p.D < (int)blockDim.x ? p.D : (int)blockDim.x;
+        for (int q = 0; q < nsplit; ++q) {
+          s2 += sh[q * width + dd];
+          x2 = fmaxf(x2, shf[q * width + dd]);
+          n2 = fminf(n2, shf[stride + q * width + dd]);
+        }
+        const float m = (float)(s2 / (double)p.L);
+        p.kmean[((size_t)c * p.H + h) * p.D + d0 + dd] = m;
+        const float up = x2 - m, dn = m - n2;  // each one fp32 rounding
+        a = fmaxf(a, fmaxf(up, dn));
+      }
     }
   } else {
-    for (int ts = tid; ts < p.nst; ts += blockDim.x) a = fmaxf(a, p.pvabs[((size_t)c * p.H + h) * p.nst + ts]);
+    for (int jj = tid; jj < p.nst; jj += blockDim.x) a = fmaxf(a, fetch(&p.pvabs[hb + jj]));
   }
   a = wave_max(a);
+  __syncthreads();
   if ((tid & 63) == 0) shw[tid >> 6] = a;
   __syncthreads();
   if (tid == 0) {
-    float m = 0.0f;
-    for (int w = 0; w < (int)((blockDim.x + 63) / 64); ++w) m = fmaxf(m, shw[w]);
-    p.hamax[((size_t)tau * p.nc + c) * p.H + h] = m;
+    float hm = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x / 64); ++w) hm = fmaxf(hm, shw[w]);
+    p.hamax[((size_t)tau * p.nc + c) * p.H + h] = hm;
   }
 }
 
@@ -235,22 +299,35 @@ __device__ __forceinline__ void kv_quant_body(const KVParams& p, int tau, int c,
   uint8_t* codes = p.codes[tau];
   uint8_t* scales = p.scales[tau];
   unsigned n4 = 0, nblk = 0;
-  for (int r = r0 + roff; r < r1; r += p.RP) {
-    const size_t blk = (row0 + r) * p.NB + col;
-    const uint4* src = reinterpret_cast<const uint4*>(xb + blk * 16);
-    const uint4 a = src[0], b = src[1];
-    float z[16];
-    unpack16(a, b, z);
+  for (int rb = r0 + roff; rb < r1; rb += kBatch * p.RP) {
+    uint4 a[kBatch], b[kBatch];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float xs = SMOOTH ? z[i] - m[i] : z[i];  // k' = fl(K - m)
-      z[i] = xs * g;                                  // z = fl(k' * g_enc)
+    for (int q = 0; q < kBatch; ++q) {
+      const int r = rb + q * p.RP;
+      if (r < r1) {
+        const size_t blk = (row0 + r) * p.NB + col;
+        a[q] = load_nt(xb + blk * 16);
+        b[q] = load_nt(xb + blk * 16 + 8);
+      }
     }
-    const Block46 q = quant_block16<MODE>(z);
-    *reinterpret_cast<uint2*>(codes + blk * 8) = make_uint2(q.lo, q.hi);
-    scales[blk] = (uint8_t)q.scale;
-    n4 += q.use4;
-    nblk += 1;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int r = rb + q * p.RP;
+      if (r >= r1) continue;
+      const size_t blk = (row0 + r) * p.NB + col;
+      float z[16];
+      unpack16(a[q], b[q], z);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float xs = SMOOTH ? z[i] - m[i] : z[i];  // k' = fl(K - m)
+        z[i] = xs * g;                                  // z = fl(k' * g_enc)
+      }
+      const Block46 qb = quant_block16<MODE>(z);
+      store_nt(codes + blk * 8, qb.lo, qb.hi);
+      store_nt(scales + blk, (uint8_t)qb.scale);
+      n4 += qb.use4;
+      nblk += 1;
+    }
   }
   if (p.choice) {
     n4 = wave_sum_u32(n4);
@@ -263,8 +340,7 @@ __device__ __forceinline__ void kv_quant_body(const KVParams& p, int tau, int c,
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kMaxThreads) void kv_quant_kernel(KVParams p) {
-  const int qt = blockIdx.x, h = blockIdx.y, tau = blockIdx.z & 1, c = p.chunk0 + (int)(blockIdx.z >> 1);
+__device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt) {
   // tensor scale of (tau, chunk) from the heads' maxima
   float A = 0.0f;
   const float* ha = p.hamax + ((size_t)tau * p.nc + c) * p.H;
@@ -278,68 +354,100 @@ __global__ __launch_bounds__(kMaxThreads) void kv_quant_kernel(KVParams p) {
     kv_quant_body<MODE, false>(p, tau, c, h, qt, g);
 }
 
-__global__ void zero_u64_kernel(unsigned long long* p, int n) {
+// Statistics of chunks [s0, s1): one workgroup per (chunk, tensor, head,
+// tile), tile fastest, K and V interleaved.
+__global__ __launch_bounds__(kMaxThreads) void kv_stats_kernel(KVParams p) {
+  __shared__ double sh[16 * (kMaxThreads + 1)];
+  __shared__ float shw[kMaxThreads / 64];
+  __shared__ unsigned sh_flag;
+  unsigned idx = blockIdx.x;
+  const int ts = idx % p.nst;
+  idx /= p.nst;
+  const int h = idx % p.H;
+  idx /= p.H;
+  kv_stats_tile(p, p.s0 + (int)(idx >> 1), (int)(idx & 1), h, ts, sh, shw, &sh_flag);
+}
+
+// Quantization of chunks [q0, q1): one workgroup per (chunk, tensor, head,
+// tile).  No LDS, so occupancy is set by registers alone.
+template <int MODE>
+__global__ __launch_bounds__(kMaxThreads) void kv_quant_kernel(KVParams p) {
+  unsigned idx = blockIdx.x;
+  const int qt = idx % p.nqt;
+  idx /= p.nqt;
+  const int h = idx % p.H;
+  idx /= p.H;
+  kv_quant_tile<MODE>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt);
+}
+
+__global__ void zero_counters_kernel(unsigned* cnt, int n, unsigned long long* choice) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0ull;
+  if (i < n) cnt[i] = 0u;
+  if (choice && i < 4) choice[i] = 0ull;
 }
 
 // -------------------------------------------------------------- dequant ---
 
+// Two lanes per 16-element block (each lane one 8-element half), so every
+// 16-byte bf16 store of a wave lands in one contiguous 1 KB run.  Thread t
+// owns half-column t % HB (HB = 2 * D/16 halves per row) for all its rows.
 struct DeqParams {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* tscale;
   const float* mean;
   uint16_t* out;
-  int H, T, D, L, NB, RP, rows_q;
+  int H, T, D, L, HB, RP, rows_q;
 };
 
+struct DeqGeom {
+  int HB, RP, threads, rows_q, nqt;
+};
+
+static DeqGeom deq_geom(int D, int L) {
+  DeqGeom g;
+  g.HB = D / 8;
+  g.RP = g.HB >= kMaxThreads ? 1 : kMaxThreads / g.HB;
+  g.threads = (g.HB * g.RP + 63) / 64 * 64;
+  g.rows_q = g.RP * kQuantPasses * 2;
+  g.nqt = (L + g.rows_q - 1) / g.rows_q;
+  return g;
+}
+
 template <bool MEAN>
-__global__ __launch_bounds__(kMaxThreads) void dequant_kernel(DeqParams p) {
+__global__ __launch_bounds__(512) void dequant_kernel(DeqParams p) {
   const int qt = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
-  const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
+  const int tid = threadIdx.x, hc = tid % p.HB, roff = tid / p.HB;
   if (roff >= p.RP) return;
-  float m[16];
+  float m[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m[i] = 0.0f;
+  for (int i = 0; i < 8; ++i) m[i] = 0.0f;
   if (MEAN) {
-    const float4* mp = reinterpret_cast<const float4*>(p.mean + ((size_t)c * p.H + h) * p.D + (size_t)col * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = mp[j];
-      m[4 * j] = v.x; m[4 * j + 1] = v.y; m[4 * j + 2] = v.z; m[4 * j + 3] = v.w;
-    }
+    const float4* mp = reinterpret_cast<const float4*>(p.mean + ((size_t)c * p.H + h) * p.D + (size_t)hc * 8);
+    const float4 a = mp[0], b = mp[1];
+    m[0] = a.x; m[1] = a.y; m[2] = a.z; m[3] = a.w; m[4] = b.x; m[5] = b.y; m[6] = b.z; m[7] = b.w;
   }
   const float g = p.tscale[c];
   const int r0 = qt * p.rows_q;
   const int r1 = min(r0 + p.rows_q, p.L);
   const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
   for (int r = r0 + roff; r < r1; r += p.RP) {
-    const size_t blk = (row0 + r) * p.NB + col;
-    const uint2 q = *reinterpret_cast<const uint2*>(p.codes + blk * 8);
-    const float S = __builtin_amdgcn_cvt_f32_fp8((int)p.scales[blk], 0);
-    float v[16];
+    const size_t half = (row0 + r) * p.HB + hc;  // index of this 8-element half
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(p.codes + half * 4);
+    const float S = __builtin_amdgcn_cvt_f32_fp8((int)p.scales[half >> 1], 0);
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+    const float v[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+    uint32_t w[4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t w = half ? q.y : q.x;
-      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-      const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-      float* o = v + 8 * half;
-      o[0] = v0[0]; o[1] = v0[1]; o[2] = v1[0]; o[3] = v1[1];
-      o[4] = v2[0]; o[5] = v2[1]; o[6] = v3[0]; o[7] = v3[1];
-    }
-    uint32_t w[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       float a = (v[2 * j] * S) * g, b = (v[2 * j + 1] * S) * g;
       if (MEAN) { a = a + m[2 * j]; b = b + m[2 * j + 1]; }
       w[j] = pack_bf16x2(a, b);
     }
-    uint4* dst = reinterpret_cast<uint4*>(p.out + blk * 16);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    *reinterpret_cast<uint4*>(p.out + half * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -353,6 +461,7 @@ static bool kv_shape_ok(int H, int T, int D, int L) {
   if (H < 0 || T < 0 || D <= 0 || L <= 0) return false;
   if (D % 16 != 0 || D > NVFP4_KV_MAX_D) return false;
   if (T % L != 0) return false;
+  if (H > 65535 || T / L > 16384) return false;  // launch grid limits
   // block indices and row counts stay in 31 bits
   if ((long long)H * T * (D / 16) >= (1LL << 31)) return false;
   return true;
@@ -360,7 +469,9 @@ static bool kv_shape_ok(int H, int T, int D, int L) {
 
 extern "C" NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len) || H == 0 || T == 0) return 0;
-  return kv_workspace_layout(kv_geom(H, T, D, chunk_len)).total;
+  const size_t two_pass = kv_workspace_layout(kv_geom(H, T, D, chunk_len)).total;
+  const size_t fused = fused_workspace_bound(H, T, D, chunk_len);
+  return two_pass > fused ? two_pass : fused;
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
@@ -370,6 +481,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
                                                     unsigned long long* choice_counts, void* workspace,
                                                     size_t workspace_bytes, void* stream) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len)) return NVFP4_ERR_SHAPE;
+  const bool force_two_pass = (mode & NVFP4_KV_FORCE_TWO_PASS) != 0;
+  mode &= ~NVFP4_KV_FORCE_TWO_PASS;
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
   if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
@@ -379,7 +492,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
     return NVFP4_ERR_ALIGN;
   const KVGeom g = kv_geom(H, T, D, chunk_len);
   const KVWorkspace wl = kv_workspace_layout(g);
-  if (!workspace || workspace_bytes < wl.total) return NVFP4_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < nvfp4_kv_workspace_bytes(H, T, D, chunk_len)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   const size_t n = (size_t)H * T * D;
   const Range in[2] = {range_of(k, n * 2), range_of(v, n * 2)};
@@ -391,6 +504,20 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
 
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
+  (void)hipGetLastError();  // start from a clean error state
+  if (!force_two_pass) {
+    FusedParams f;
+    f.x[0] = k; f.x[1] = v;
+    f.codes[0] = k_codes; f.codes[1] = v_codes;
+    f.scales[0] = k_scales; f.scales[1] = v_scales;
+    f.tscale[0] = k_tensor_scale; f.tscale[1] = v_tensor_scale;
+    f.kmean = k_mean;
+    f.choice = choice_counts;
+    f.H = H; f.T = T; f.D = D; f.L = chunk_len; f.nc = g.nc;
+    f.spin_limit = kFusedSpinLimit;
+    const int rc = fused_try_launch(f, mode, workspace, workspace_bytes, s);
+    if (rc <= 0) return rc;  // enqueued, or a launch error
+  }
   KVParams p;
   p.x[0] = k; p.x[1] = v;
   p.codes[0] = k_codes; p.codes[1] = v_codes;
@@ -402,25 +529,28 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   p.pmin = reinterpret_cast<float*>(ws + wl.pmin);
   p.pvabs = reinterpret_cast<float*>(ws + wl.pvabs);
   p.hamax = reinterpret_cast<float*>(ws + wl.hamax);
+  p.cnt = reinterpret_cast<unsigned*>(ws + wl.counters);
   p.choice = choice_counts;
   p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.nc = g.nc; p.NB = g.NB; p.RP = g.RP;
-  p.rows_s = g.rows_s; p.rows_q = g.rows_q; p.nst = g.nst;
+  p.rows_s = g.rows_s; p.rows_q = g.rows_q; p.nst = g.nst; p.nqt = g.nqt;
 
-  (void)hipGetLastError();  // start from a clean error state
-  if (choice_counts) zero_u64_kernel<<<1, 64, 0, s>>>(choice_counts, 4);
+  zero_counters_kernel<<<(wl.n_counters + 255) / 256 + 1, 256, 0, s>>>(p.cnt, wl.n_counters, choice_counts);
   const size_t chunk_bytes = (size_t)2 * H * chunk_len * D * sizeof(uint16_t);
   int group = (int)(kGroupBytes / (chunk_bytes > 0 ? chunk_bytes : 1));
-  group = group < 1 ? 1 : (group > 16384 ? 16384 : group);
+  group = group < 1 ? 1 : group;
+  const long long per_chunk_wgs = 2LL * H * (g.nst > g.nqt ? g.nst : g.nqt);
+  if ((long long)group * per_chunk_wgs > (1LL << 30)) group = (int)((1LL << 30) / per_chunk_wgs);
+  // per group of chunks: the statistics kernel, then the quantize kernel
   for (int c0 = 0; c0 < g.nc; c0 += group) {
-    const int gn = g.nc - c0 < group ? g.nc - c0 : group;
-    p.chunk0 = c0;
-    kv_stats_kernel<<<dim3(g.nst, H, 2 * gn), g.threads, 0, s>>>(p);
-    kv_finalize_kernel<<<dim3(H, gn, 2), kMaxThreads, 0, s>>>(p);
-    const dim3 qgrid(g.nqt, H, 2 * gn);
+    p.s0 = p.q0 = c0;
+    p.s1 = p.q1 = c0 + group < g.nc ? c0 + group : g.nc;
+    const long long ns = (long long)(p.s1 - p.s0) * 2 * H * g.nst;
+    const long long nq = (long long)(p.q1 - p.q0) * 2 * H * g.nqt;
+    kv_stats_kernel<<<(unsigned)ns, g.threads, 0, s>>>(p);
     switch (mode) {
-      case NVFP4_MODE_FIXED6: kv_quant_kernel<kModeFixed6><<<qgrid, g.threads, 0, s>>>(p); break;
-      case NVFP4_MODE_FIXED4: kv_quant_kernel<kModeFixed4><<<qgrid, g.threads, 0, s>>>(p); break;
-      default: kv_quant_kernel<kMode4over6><<<qgrid, g.threads, 0, s>>>(p); break;
+      case NVFP4_MODE_FIXED6: kv_quant_kernel<kModeFixed6><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
+      case NVFP4_MODE_FIXED4: kv_quant_kernel<kModeFixed4><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
+      default: kv_quant_kernel<kMode4over6><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
     }
   }
   return launch_status();
@@ -440,15 +570,16 @@ extern "C" NVFP4KV_API int nvfp4_dequantize(const uint8_t* codes, const uint8_t*
                        range_of(mean, mean ? (size_t)g.nc * H * D * 4 : 0)};
   const Range outr[1] = {range_of(out, n * 2)};
   if (any_alias(in, 4, outr, 1)) return NVFP4_ERR_ALIAS;
+  const DeqGeom dg = deq_geom(D, chunk_len);
   DeqParams p;
   p.codes = codes; p.scales = scales; p.tscale = tensor_scale; p.mean = mean; p.out = out;
-  p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.NB = g.NB; p.RP = g.RP; p.rows_q = g.rows_q;
+  p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.HB = dg.HB; p.RP = dg.RP; p.rows_q = dg.rows_q;
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  const dim3 grid(g.nqt, H, g.nc);
+  const dim3 grid(dg.nqt, H, g.nc);
   if (mean)
-    dequant_kernel<true><<<grid, g.threads, 0, s>>>(p);
+    dequant_kernel<true><<<grid, dg.threads, 0, s>>>(p);
   else
-    dequant_kernel<false><<<grid, g.threads, 0, s>>>(p);
+    dequant_kernel<false><<<grid, dg.threads, 0, s>>>(p);
   return launch_status();
 }

@@ -174,6 +174,59 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return u;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming 16-byte load / stores (non-temporal: the data is used once).
+__device__ __forceinline__ uint4 load_nt(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint32_t lo, uint32_t hi) {
+  const u32x2 v = {lo, hi};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint8_t b) { __builtin_nontemporal_store(b, p); }
+
+// Hand-off of small results between workgroups of one kernel.
+//
+// On this multi-XCD part every XCD has its own L2, and an agent-scope
+// release / acquire fence writes back / invalidates that whole L2; with
+// hundreds of workgroups publishing, those fences serialize and dominate.
+// So results that other workgroups read inside the same kernel are written
+// with agent-scope atomic exchanges, which are performed at the device's
+// coherence point, and read with agent-scope atomic loads.  A writer waits
+// for every exchange to return (completion at the coherence point) before
+// the barrier after which one thread bumps the counter; a reader issues its
+// loads only after it has seen the counter (the loads depend on the
+// counter's value), so it observes the published values.
+__device__ __forceinline__ unsigned add_agent(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned load_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(unsigned* p, unsigned v) {
+  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// publish: exchange, and fold the returned old value into `done` so the
+// caller can make the exchange's completion explicit (see wait_published)
+__device__ __forceinline__ void publish(float* p, float v, uint32_t& done) {
+  done ^= __float_as_uint(__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void publish(double* p, double v, uint32_t& done) {
+  const double o = __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  done ^= (uint32_t)__double_as_longlong(o);
+}
+// forces the wait for every exchange folded into `done` (its value is needed)
+__device__ __forceinline__ void wait_published(uint32_t done) { asm volatile("" ::"v"(done)); }
+__device__ __forceinline__ float fetch(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double fetch(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wave-level reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -23,11 +23,34 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True):
+SENTINEL = 0x5A  # every output byte is pre-filled with it, so a missing write cannot pass
+
+
+def kv_outputs(H, T, D, L, counts=True):
+    """Output tensors for nvfp4_kv_smooth_quantize, filled with a sentinel."""
+    nc = T // L
+
+    def fill(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device="cuda")
+        t.view(torch.uint8).fill_(SENTINEL)
+        return t
+
+    out = {"k_codes": fill((H, T, D // 2), torch.uint8), "v_codes": fill((H, T, D // 2), torch.uint8),
+           "k_scales": fill((H, T, D // 16), torch.uint8), "v_scales": fill((H, T, D // 16), torch.uint8),
+           "k_tensor_scale": fill((nc,), torch.float32), "v_tensor_scale": fill((nc,), torch.float32),
+           "k_mean": fill((nc, H, D), torch.float32)}
+    if counts:
+        out["choice_counts"] = fill((2, 2), torch.int64)
+    return out
+
+
+def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True, two_pass=False):
     """K, V given as numpy bf16 bits [H, T, D] -> GPU outputs as numpy."""
     k = W.from_bits(kb, "cuda")
     v = W.from_bits(vb, "cuda")
-    out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts)
+    H, T, D = kb.shape
+    out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts, two_pass=two_pass,
+                                     out=kv_outputs(H, T, D, L, counts))
     torch.cuda.synchronize()
     return {key: t.cpu().numpy() for key, t in out.items()}, out
 
@@ -64,9 +87,12 @@ def check_kv(kb, vb, L, mode, res, dev_out=None, nthreads=0, check_dequant=True)
         n = res["k_codes"].size // 8
         assert res["choice_counts"].tolist() == [[n - ref["k_use4"], ref["k_use4"]], [n - ref["v_use4"], ref["v_use4"]]]
     if check_dequant and dev_out is not None:
-        dk = P.nvfp4_dequantize(dev_out["k_codes"], dev_out["k_scales"], dev_out["k_tensor_scale"],
-                                dev_out["k_mean"], L)
-        dv = P.nvfp4_dequantize(dev_out["v_codes"], dev_out["v_scales"], dev_out["v_tensor_scale"], None, L)
+        H, T, D2 = res["k_codes"].shape
+        dk = torch.full((H, T, 2 * D2), -777.0, dtype=torch.bfloat16, device="cuda")
+        dv = torch.full((H, T, 2 * D2), -777.0, dtype=torch.bfloat16, device="cuda")
+        P.nvfp4_dequantize(dev_out["k_codes"], dev_out["k_scales"], dev_out["k_tensor_scale"], dev_out["k_mean"], L,
+                           out=dk)
+        P.nvfp4_dequantize(dev_out["v_codes"], dev_out["v_scales"], dev_out["v_tensor_scale"], None, L, out=dv)
         torch.cuda.synchronize()
         rk = O.dequantize(ref["k_codes"], ref["k_scales"], ref["k_tensor_scale"], res["k_mean"], L, nthreads)
         rv = O.dequantize(ref["v_codes"], ref["v_scales"], ref["v_tensor_scale"], None, L, nthreads)

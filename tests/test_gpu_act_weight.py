@@ -12,18 +12,26 @@ from gpu_helpers import say, to_np
 pytestmark = pytest.mark.gpu
 
 
+def _filled(shape, dtype):
+    t = torch.empty(shape, dtype=dtype, device="cuda")
+    t.view(torch.uint8).fill_(0x5A)  # sentinel: a missing write cannot pass
+    return t
+
+
 def _check_1d(xb, mode, hadamard, mask):
     x = W.from_bits(xb, "cuda")
-    out = P.nvfp4_quantize_1d(x, mode, hadamard, mask)
+    rows, cols = xb.shape
+    out = P.nvfp4_quantize_1d(x, mode, hadamard, mask, out={
+        "codes": _filled((rows, cols // 2), torch.uint8), "scales": _filled((rows, cols // 16), torch.uint8),
+        "tensor_scale": _filled((1,), torch.float32)})
     torch.cuda.synchronize()
     ref = O.quantize_1d(xb, mode, hadamard, mask)
     for key in ("codes", "scales"):
         a = out[key].cpu().numpy()
         assert np.array_equal(a, ref[key]), (key, int((a != ref[key]).sum()))
     assert out["tensor_scale"].cpu().numpy().view(np.uint32)[0] == ref["tensor_scale"].view(np.uint32)[0]
-    rows, cols = xb.shape
     d = P.nvfp4_dequantize(out["codes"].view(1, rows, cols // 2), out["scales"].view(1, rows, cols // 16),
-                           out["tensor_scale"], None, rows)
+                           out["tensor_scale"], None, rows, out=_filled((1, rows, cols), torch.bfloat16))
     torch.cuda.synchronize()
     rd = O.dequantize(ref["codes"][None], ref["scales"][None], ref["tensor_scale"], None, rows)
     assert np.array_equal(to_np(d), rd)
@@ -48,14 +56,18 @@ def test_activation_shapes_and_modes(rows, cols, mode, had):
 
 def _check_2d(wb, mode):
     w = W.from_bits(wb, "cuda")
-    out = P.nvfp4_quantize_2d(w, mode)
+    rows, cols = wb.shape
+    out = P.nvfp4_quantize_2d(w, mode, out={
+        "codes": _filled((rows, cols // 2), torch.uint8), "scales": _filled((rows // 16, cols // 16), torch.uint8),
+        "tensor_scale": _filled((1,), torch.float32)})
     torch.cuda.synchronize()
     ref = O.quantize_2d(wb, mode)
     for key in ("codes", "scales"):
         a = out[key].cpu().numpy()
         assert np.array_equal(a, ref[key]), (key, int((a != ref[key]).sum()))
     assert out["tensor_scale"].cpu().numpy().view(np.uint32)[0] == ref["tensor_scale"].view(np.uint32)[0]
-    d = P.nvfp4_dequantize_2d(out["codes"], out["scales"], out["tensor_scale"])
+    d = P.nvfp4_dequantize_2d(out["codes"], out["scales"], out["tensor_scale"],
+                              out=_filled((rows, cols), torch.bfloat16))
     torch.cuda.synchronize()
     assert np.array_equal(to_np(d), O.dequantize_2d(ref["codes"], ref["scales"], ref["tensor_scale"]))
 

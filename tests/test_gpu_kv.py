@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import precision_kv_cache_amd as P
 import workloads as W
-from gpu_helpers import check_kv, gpu_kv, say, to_np
+from gpu_helpers import SENTINEL, check_kv, gpu_kv, kv_outputs, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -18,12 +18,17 @@ def _lib_loaded():
     P.lib()  # raises if the HIP library is missing
 
 
+PATHS = [False, True]  # single-read persistent kernel, two-pass kernels
+PATH_IDS = ["single-read", "two-pass"]
+
+
+@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
-def test_tiny_workload(mode):
-    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode)
+def test_tiny_workload(mode, two_pass):
+    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode, "two_pass", two_pass)
     k, v = W.gaussian_kv(W.TINY, W.SEED_TINY)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode)
+    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode, two_pass=two_pass)
     check_kv(kb, vb, W.TINY.chunk_len, mode, res, dev)
 
 
@@ -36,37 +41,41 @@ def test_tiny_matches_golden_fixture():
             assert np.array_equal(res[key], g[key]), key
 
 
-def test_one_chunk_workload():
+@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
+def test_one_chunk_workload(two_pass):
     s = W.ONE_CHUNK
-    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK)
+    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK, "two_pass", two_pass)
     k, v = W.gaussian_kv(s, W.SEED_ONE_CHUNK)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, s.chunk_len)
+    res, dev = gpu_kv(kb, vb, s.chunk_len, two_pass=two_pass)
     ref = check_kv(kb, vb, s.chunk_len, O.MODE_4OVER6, res, dev)
     assert 0 < ref["k_use4"] < res["k_codes"].size // 8
 
 
-def test_heavy_tail_workload():
+@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
+def test_heavy_tail_workload(two_pass):
     s = W.ONE_CHUNK
-    say("heavy-tail KV", s, "seed", W.SEED_HEAVY)
+    say("heavy-tail KV", s, "seed", W.SEED_HEAVY, "two_pass", two_pass)
     k, v = W.heavy_tail_kv(s, W.SEED_HEAVY)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
     for mode in (O.MODE_4OVER6, O.MODE_FIXED6):
         say("  mode", mode)
-        res, dev = gpu_kv(kb, vb, s.chunk_len, mode)
+        res, dev = gpu_kv(kb, vb, s.chunk_len, mode, two_pass=two_pass)
         check_kv(kb, vb, s.chunk_len, mode, res, dev)
 
 
+@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("layer", [0, 29])
-def test_full_cache_layer_sampled(layer):
+def test_full_cache_layer_sampled(layer, two_pass):
     """A full-size layer of the 8-chunk cache ([24, 56320, 128], the launch
     configuration the benchmark times), drawn on the GPU; chunks 0, 3 and 7
     are checked completely against the oracle, and the whole layer's outputs
     against properties that hold at any size."""
     s = W.CACHE_LAYER
-    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer))
+    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "two_pass", two_pass)
     k, v = W.gaussian_kv(s, W.cache_layer_seed(layer), device="cuda")
-    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True)
+    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, two_pass=two_pass,
+                                     out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     dk = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len)
     dv = P.nvfp4_dequantize(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, s.chunk_len)
     torch.cuda.synchronize()
@@ -104,6 +113,10 @@ def test_full_cache_layer_sampled(layer):
     (2, 130, 256, 65),   # 16 blocks per row
     (1, 40, 4096, 8),    # widest rows
     (2, 7, 32, 1),       # one token per chunk: K' = 0 everywhere
+    (24, 1000, 128, 100),  # single-read kernel: 10 chunks, ragged slices
+    (3, 77, 128, 7),     # single-read kernel: one row per workgroup at most
+    (600, 32, 128, 32),  # more heads than resident workgroups: two-pass kernels
+    (1, 204800, 128, 204800),  # one head, more rows than the single-read kernel holds
 ])
 def test_ragged_and_odd_shapes(H, T, D, L):
     say("shape", (H, T, D, L))
@@ -135,10 +148,11 @@ def test_degenerate_values():
         "one spike": (np.where(rng.random((H, T, D)) < 1e-3, 1e4, 0.0), np.eye(T, D)[None].repeat(H, 0)),
     }
     for name, (k, v) in cases.items():
-        say("degenerate:", name)
-        kb, vb = _bits(k), _bits(v)
-        res, dev = gpu_kv(kb, vb, L)
-        check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
+        for two_pass in PATHS:
+            say("degenerate:", name, "two_pass", two_pass)
+            kb, vb = _bits(k), _bits(v)
+            res, dev = gpu_kv(kb, vb, L, two_pass=two_pass)
+            check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
 
 
 def test_deterministic_and_stream_ordered():
@@ -147,11 +161,15 @@ def test_deterministic_and_stream_ordered():
     k, v = W.gaussian_kv(s, 99, device="cuda")
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
-        a = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True)
-        b = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True)
+        a = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        b = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        c = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, two_pass=True,
+                                       out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     side.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+        if key != "k_mean":  # the two paths combine the fp64 channel sums in different orders
+            assert torch.equal(a[key], c[key]), key
 
 
 def test_dequant_without_mean_and_empty():
