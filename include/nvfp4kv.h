@@ -81,13 +81,14 @@ typedef enum {
   NVFP4_MODE_FIXED4 = 2  /* +-4 only, C = 1792                               */
 } nvfp4_mode;
 
-/* Option bit for nvfp4_kv_smooth_quantize's mode: run the two-pass kernels
- * (stats pass, then quantize pass re-reading K and V) instead of the
- * single-read persistent kernel.  Same results; for testing and for callers
- * that cannot use a cooperative launch.  The single-read kernel is used by
- * default when D == 128 and the device can keep a unit resident; other
- * shapes always take the two-pass kernels. */
-#define NVFP4_KV_FORCE_TWO_PASS 0x100
+/* Option bit for nvfp4_kv_smooth_quantize's mode: use the single-read
+ * persistent kernel (each K and V element read from HBM once; workgroups
+ * synchronize through the workspace) instead of the default two-pass kernels
+ * (a statistics pass, then a quantize pass that reads K and V again).  Same
+ * results.  It applies when D == 128 and the device supports a cooperative
+ * launch of the kernel's resident grid; otherwise the call silently takes the
+ * two-pass kernels. */
+#define NVFP4_KV_SINGLE_READ 0x200
 
 /* Largest supported head dimension / row length for the KV entry points. */
 #define NVFP4_KV_MAX_D 4096
@@ -107,7 +108,7 @@ NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) 
  *   H, T, D       heads, tokens, head dimension (D % 16 == 0, D <= 4096).
  *   chunk_len     T_c, tokens per chunk; each chunk gets its own K mean and
  *                 its own tensor scales.
- *   mode          nvfp4_mode, optionally | NVFP4_KV_FORCE_TWO_PASS.
+ *   mode          nvfp4_mode, optionally | NVFP4_KV_SINGLE_READ.
  *   k_codes, v_codes     out, uint8 [H, T, D/2], 8-byte aligned.
  *   k_scales, v_scales   out, E4M3FN bytes [H, T, D/16].
  *   k_tensor_scale, v_tensor_scale  out, fp32 [n_chunks], g_dec per chunk.

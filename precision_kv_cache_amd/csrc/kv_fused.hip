@@ -39,7 +39,10 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
   __shared__ unsigned sh_flag;
 
   const int w = blockIdx.x;
-  if (w >= p.WPH * p.H) return;  // spare workgroup: owns no rows
+  if (w >= p.WPH * p.H) {  // spare workgroup: owns no rows
+    if (p.choice && threadIdx.x == 0) *reinterpret_cast<uint4*>(p.tally + (size_t)w * 4) = make_uint4(0, 0, 0, 0);
+    return;
+  }
   const int h = w / p.WPH, j = w % p.WPH;
   const int tid = threadIdx.x, col = tid % NB, roff = tid / NB;
   const int r0 = j * p.RPW;
@@ -268,7 +271,10 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
       sh_flag = ok;
     }
     __syncthreads();
-    if (!sh_flag) return;  // time-out: results are invalid, the error word says so
+    if (!sh_flag) {  // time-out: results are invalid, the error word says so
+      if (p.choice && tid == 0) *reinterpret_cast<uint4*>(p.tally + (size_t)w * 4) = make_uint4(0, 0, 0, 0);
+      return;
+    }
     const float g = fetch(&p.genc[u]);
     if (tau == 0) {  // the head's channel means, shared by the workgroup through LDS
       for (int d = tid; d < D; d += kFusedThreads) sh_mean[d] = fetch(&p.kmean[((size_t)c * p.H + h) * D + d]);
@@ -313,21 +319,14 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
   }
 
   if (p.choice) {
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const unsigned a = wave_sum_u32(n4[t2]), b = wave_sum_u32(nblk[t2]);
-      if ((tid & 63) == 0 && b) {
-        atomicAdd(p.choice + 2 * t2 + 1, (unsigned long long)a);
-        atomicAdd(p.choice + 2 * t2 + 0, (unsigned long long)(b - a));
-      }
-    }
+    const unsigned t[4] = {n4[0], nblk[0], n4[1], nblk[1]};
+    store_wg_tally(p.tally + (size_t)blockIdx.x * 4, t, reinterpret_cast<unsigned*>(sh));
   }
 }
 
-__global__ void fused_zero_kernel(unsigned* p, int n, unsigned long long* choice) {
+__global__ void fused_zero_kernel(unsigned* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
-  if (choice && i < 4) choice[i] = 0ull;
 }
 
 // ------------------------------------------------------------- host side ---
@@ -343,6 +342,7 @@ FusedLayout fused_layout(int H, int nc, int D, int WPH) {
   l.pv = off;       off = align_up(off + (size_t)nc * H * WPH * sizeof(float), 256);
   l.hamax = off;    off = align_up(off + (size_t)U * H * sizeof(float), 256);
   l.genc = off;     off = align_up(off + (size_t)U * sizeof(float), 256);
+  l.tally = off;    off = align_up(off + (size_t)kFusedMaxWG * 4 * sizeof(uint32_t), 256);
   l.counters = off;  // cnt_head [U][H], cnt_unit [U], flag [U], err [1]
   l.n_counters = U * H + U + U + 1;
   off = align_up(off + (size_t)l.n_counters * sizeof(unsigned), 256);
@@ -405,6 +405,7 @@ int fused_try_launch(FusedParams p, int mode, void* workspace, size_t ws_bytes, 
   p.pv = reinterpret_cast<float*>(ws + l.pv);
   p.hamax = reinterpret_cast<float*>(ws + l.hamax);
   p.genc = reinterpret_cast<float*>(ws + l.genc);
+  p.tally = reinterpret_cast<uint32_t*>(ws + l.tally);
   unsigned* cnt = reinterpret_cast<unsigned*>(ws + l.counters);
   const int U = 2 * p.nc;
   p.cnt_head = cnt;
@@ -413,12 +414,16 @@ int fused_try_launch(FusedParams p, int mode, void* workspace, size_t ws_bytes, 
   p.err = p.flag + U;
   p.WPH = WPH;
   p.RPW = RPW;
-  fused_zero_kernel<<<(l.n_counters + 255) / 256, 256, 0, s>>>(cnt, l.n_counters, p.choice);
+  fused_zero_kernel<<<(l.n_counters + 255) / 256, 256, 0, s>>>(cnt, l.n_counters);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   void* args[] = {&p};
   if (hipLaunchCooperativeKernel(kern, dim3(nwg_target), dim3(kFusedThreads), args, 0, s) != hipSuccess) {
     (void)hipGetLastError();
     return NVFP4_ERR_HIP;
+  }
+  if (p.choice) {
+    launch_choice_reduce(p.tally, nwg_target, p.choice, s);
+    if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   }
   return NVFP4_OK;
 }

@@ -31,17 +31,22 @@ struct FusedParams {
   unsigned* cnt_unit;  // [2nc]
   unsigned* flag;      // [2nc]
   unsigned* err;       // [1]
+  uint32_t* tally;     // [grid][4] per-workgroup 4/6 choice counts
   int H, T, D, L, nc, WPH, RPW;
   unsigned spin_limit;
 };
 
 struct FusedLayout {
-  size_t psum, pmax, pmin, pv, hamax, genc, counters, total;
+  size_t psum, pmax, pmin, pv, hamax, genc, tally, counters, total;
   int n_counters;
 };
 
 FusedLayout fused_layout(int H, int nc, int D, int WPH);
 size_t fused_workspace_bound(int H, int T, int D, int L);
 int fused_try_launch(FusedParams p, int mode, void* workspace, size_t ws_bytes, hipStream_t s);
+
+// Adds up nslots per-workgroup tallies [nslots][4] into the caller's
+// choice_counts [2][2] (K kept +-6, K kept +-4, V kept +-6, V kept +-4).
+void launch_choice_reduce(const uint32_t* tally, size_t nslots, unsigned long long* choice, hipStream_t s);
 
 }  // namespace nvfp4

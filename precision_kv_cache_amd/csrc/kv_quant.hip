@@ -9,8 +9,9 @@
 //               (h, t, D/16 column); one lane of a workgroup owns one block.
 //   k_mean      [nc, H, D] fp32; tensor scales [nc] fp32 per tensor.
 //
-// Two passes over each group of chunks (the group is sized so that its K
-// and V could stay in the Infinity Cache between the passes):
+// Two passes, each one launch over all chunks of the layer (tens of
+// thousands of workgroups, so the per-tile reduction latency of one
+// workgroup hides behind the others' streaming):
 //   kv_stats    per (chunk, tensor, head, row tile): K channel sum (fp64),
 //               max, min, or V largest magnitude -> workspace; the last tile
 //               of a head (atomic counter) reduces the head: mean
@@ -40,8 +41,8 @@ namespace nvfp4 {
 constexpr int kMaxThreads = 256;
 constexpr int kStatsPasses = 16;  // rows per stats tile = RP * kStatsPasses
 constexpr int kQuantPasses = 4;   // rows per quant / dequant tile = RP * kQuantPasses
-constexpr int kBatch = 4;         // rows whose loads are issued together
-constexpr size_t kGroupBytes = size_t(96) << 20;  // K+V bytes per chunk group
+constexpr int kBatch = 2;         // rows whose loads are issued together
+constexpr long long kMaxLaunchWGs = 1LL << 22;   // workgroups per launch (grid limits)
 
 struct KVGeom {
   int H, T, D, L, nc;
@@ -64,8 +65,9 @@ static KVGeom kv_geom(int H, int T, int D, int L) {
 }
 
 struct KVWorkspace {
-  size_t psum, pmax, pmin, pvabs, hamax, counters, total;  // byte offsets
+  size_t psum, pmax, pmin, pvabs, hamax, tally, counters, total;  // byte offsets
   int n_counters;
+  size_t n_tally;
 };
 
 static KVWorkspace kv_workspace_layout(const KVGeom& g) {
@@ -77,6 +79,9 @@ static KVWorkspace kv_workspace_layout(const KVGeom& g) {
   w.pmin = off;  off = align_up(off + nch * sizeof(float), 256);
   w.pvabs = off; off = align_up(off + (size_t)g.nc * g.H * g.nst * sizeof(float), 256);
   w.hamax = off; off = align_up(off + (size_t)2 * g.nc * g.H * sizeof(float), 256);
+  w.tally = off;  // [nc][2][H][nqt][4] per-workgroup 4/6 choice counts
+  w.n_tally = (size_t)2 * g.nc * g.H * g.nqt;
+  off = align_up(off + (size_t)w.n_tally * 4 * sizeof(uint32_t), 256);
   w.counters = off;  // one per (chunk, tensor, head)
   w.n_counters = 2 * g.nc * g.H;
   off = align_up(off + (size_t)w.n_counters * sizeof(unsigned), 256);
@@ -96,6 +101,7 @@ struct KVParams {
   float* pvabs;   // [nc][H][nst]
   float* hamax;   // [2][nc][H]
   unsigned* cnt;  // [nc][2][H]
+  uint32_t* tally;  // [nc][2][H][nqt][4]
   unsigned long long* choice;
   int H, T, D, L, nc, NB, RP, rows_s, rows_q, nst, nqt;
   int s0, s1;  // chunks whose statistics this launch computes
@@ -277,8 +283,9 @@ __device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, 
 
 // ---------------------------------------------------------------- quant ---
 
+// Returns this thread's {blocks kept at +-4, blocks}.
 template <int MODE, bool SMOOTH>
-__device__ __forceinline__ void kv_quant_body(const KVParams& p, int tau, int c, int h, int qt, float g) {
+__device__ __forceinline__ uint2 kv_quant_body(const KVParams& p, int tau, int c, int h, int qt, float g) {
   const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
   const bool active = roff < p.RP;
   float m[16];
@@ -329,18 +336,11 @@ __device__ __forceinline__ void kv_quant_body(const KVParams& p, int tau, int c,
       nblk += 1;
     }
   }
-  if (p.choice) {
-    n4 = wave_sum_u32(n4);
-    nblk = wave_sum_u32(nblk);
-    if ((tid & 63) == 0 && nblk) {
-      atomicAdd(p.choice + 2 * tau + 1, (unsigned long long)n4);
-      atomicAdd(p.choice + 2 * tau + 0, (unsigned long long)(nblk - n4));
-    }
-  }
+  return make_uint2(n4, nblk);
 }
 
 template <int MODE>
-__device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt) {
+__device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt, unsigned* sh_tally) {
   // tensor scale of (tau, chunk) from the heads' maxima
   float A = 0.0f;
   const float* ha = p.hamax + ((size_t)tau * p.nc + c) * p.H;
@@ -348,10 +348,12 @@ __device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt) 
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
   if (qt == 0 && h == 0 && threadIdx.x == 0) p.tscale[tau][c] = A / C;
-  if (tau == 0)
-    kv_quant_body<MODE, true>(p, tau, c, h, qt, g);
-  else
-    kv_quant_body<MODE, false>(p, tau, c, h, qt, g);
+  const uint2 n = tau == 0 ? kv_quant_body<MODE, true>(p, tau, c, h, qt, g)
+                           : kv_quant_body<MODE, false>(p, tau, c, h, qt, g);
+  if (p.choice) {
+    const unsigned t[4] = {tau == 0 ? n.x : 0u, tau == 0 ? n.y : 0u, tau == 1 ? n.x : 0u, tau == 1 ? n.y : 0u};
+    store_wg_tally(p.tally + ((((size_t)c * 2 + tau) * p.H + h) * p.nqt + qt) * 4, t, sh_tally);
+  }
 }
 
 // Statistics of chunks [s0, s1): one workgroup per (chunk, tensor, head,
@@ -369,21 +371,53 @@ __global__ __launch_bounds__(kMaxThreads) void kv_stats_kernel(KVParams p) {
 }
 
 // Quantization of chunks [q0, q1): one workgroup per (chunk, tensor, head,
-// tile).  No LDS, so occupancy is set by registers alone.
+// tile).  Only 64 bytes of LDS (the choice tally), so occupancy is set by
+// registers.
 template <int MODE>
 __global__ __launch_bounds__(kMaxThreads) void kv_quant_kernel(KVParams p) {
+  __shared__ unsigned sh_tally[4 * (kMaxThreads / 64)];
   unsigned idx = blockIdx.x;
   const int qt = idx % p.nqt;
   idx /= p.nqt;
   const int h = idx % p.H;
   idx /= p.H;
-  kv_quant_tile<MODE>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt);
+  kv_quant_tile<MODE>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt, sh_tally);
 }
 
-__global__ void zero_counters_kernel(unsigned* cnt, int n, unsigned long long* choice) {
+__global__ void zero_counters_kernel(unsigned* cnt, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) cnt[i] = 0u;
-  if (choice && i < 4) choice[i] = 0ull;
+}
+
+// One workgroup adds up the per-workgroup tallies [nslots][4] in 64-bit and
+// writes choice [2][2] = {K kept +-6, K kept +-4, V kept +-6, V kept +-4}.
+__global__ __launch_bounds__(256) void choice_reduce_kernel(const uint32_t* tally, size_t nslots,
+                                                            unsigned long long* choice) {
+  __shared__ unsigned long long sh[4][256];
+  const int tid = threadIdx.x;
+  unsigned long long a[4] = {0ull, 0ull, 0ull, 0ull};
+  for (size_t i = tid; i < nslots; i += 256) {
+    const uint4 t = *reinterpret_cast<const uint4*>(tally + (size_t)i * 4);
+    a[0] += t.x; a[1] += t.y; a[2] += t.z; a[3] += t.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sh[j][tid] = a[j];
+  __syncthreads();
+  if (tid < 4) {
+    unsigned long long s = 0ull;
+    for (int q = 0; q < 256; ++q) s += sh[tid][q];
+    sh[tid][0] = s;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const unsigned long long n4 = sh[2 * tid][0], nb = sh[2 * tid + 1][0];
+    choice[2 * tid + 0] = nb - n4;
+    choice[2 * tid + 1] = n4;
+  }
+}
+
+void launch_choice_reduce(const uint32_t* tally, size_t nslots, unsigned long long* choice, hipStream_t s) {
+  choice_reduce_kernel<<<1, 256, 0, s>>>(tally, nslots, choice);
 }
 
 // -------------------------------------------------------------- dequant ---
@@ -481,8 +515,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
                                                     unsigned long long* choice_counts, void* workspace,
                                                     size_t workspace_bytes, void* stream) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len)) return NVFP4_ERR_SHAPE;
-  const bool force_two_pass = (mode & NVFP4_KV_FORCE_TWO_PASS) != 0;
-  mode &= ~NVFP4_KV_FORCE_TWO_PASS;
+  const bool single_read = (mode & NVFP4_KV_SINGLE_READ) != 0;
+  mode &= ~NVFP4_KV_SINGLE_READ;
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
   if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
@@ -505,7 +539,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();  // start from a clean error state
-  if (!force_two_pass) {
+  if (single_read) {
     FusedParams f;
     f.x[0] = k; f.x[1] = v;
     f.codes[0] = k_codes; f.codes[1] = v_codes;
@@ -530,16 +564,16 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   p.pvabs = reinterpret_cast<float*>(ws + wl.pvabs);
   p.hamax = reinterpret_cast<float*>(ws + wl.hamax);
   p.cnt = reinterpret_cast<unsigned*>(ws + wl.counters);
+  p.tally = reinterpret_cast<uint32_t*>(ws + wl.tally);
   p.choice = choice_counts;
   p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.nc = g.nc; p.NB = g.NB; p.RP = g.RP;
   p.rows_s = g.rows_s; p.rows_q = g.rows_q; p.nst = g.nst; p.nqt = g.nqt;
 
-  zero_counters_kernel<<<(wl.n_counters + 255) / 256 + 1, 256, 0, s>>>(p.cnt, wl.n_counters, choice_counts);
-  const size_t chunk_bytes = (size_t)2 * H * chunk_len * D * sizeof(uint16_t);
-  int group = (int)(kGroupBytes / (chunk_bytes > 0 ? chunk_bytes : 1));
-  group = group < 1 ? 1 : group;
+  zero_counters_kernel<<<(wl.n_counters + 255) / 256, 256, 0, s>>>(p.cnt, wl.n_counters);
+  // Chunks per launch: all of them unless the grid would get too large.
   const long long per_chunk_wgs = 2LL * H * (g.nst > g.nqt ? g.nst : g.nqt);
-  if ((long long)group * per_chunk_wgs > (1LL << 30)) group = (int)((1LL << 30) / per_chunk_wgs);
+  int group = (int)(kMaxLaunchWGs / per_chunk_wgs);
+  group = group < 1 ? 1 : (group > g.nc ? g.nc : group);
   // per group of chunks: the statistics kernel, then the quantize kernel
   for (int c0 = 0; c0 < g.nc; c0 += group) {
     p.s0 = p.q0 = c0;
@@ -553,6 +587,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
       default: kv_quant_kernel<kMode4over6><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
     }
   }
+  if (choice_counts) launch_choice_reduce(p.tally, wl.n_tally, choice_counts, s);
   return launch_status();
 }
 

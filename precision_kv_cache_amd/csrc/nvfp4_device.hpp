@@ -239,4 +239,29 @@ __device__ __forceinline__ unsigned wave_sum_u32(unsigned v) {
   return v;
 }
 
+// 4/6 choice tallies without contended atomics: each workgroup sums its
+// threads' counts {K kept +-4, K blocks, V kept +-4, V blocks} through LDS
+// (sh: one entry of 4 per wave) and thread 0 stores them in the workgroup's
+// own 16-byte slot; a one-workgroup kernel adds the slots up at the end.
+// Every thread of the workgroup calls this (it holds two barriers).
+__device__ __forceinline__ void store_wg_tally(uint32_t* slot, const unsigned (&t)[4], unsigned* sh) {
+  const int tid = threadIdx.x, nw = (int)(blockDim.x + 63) / 64;
+  unsigned w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = wave_sum_u32(t[j]);
+  __syncthreads();
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sh[(tid >> 6) * 4 + j] = w[j];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned a[4] = {0u, 0u, 0u, 0u};
+    for (int q = 0; q < nw; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] += sh[q * 4 + j];
+    *reinterpret_cast<uint4*>(slot) = make_uint4(a[0], a[1], a[2], a[3]);
+  }
+}
+
 }  // namespace nvfp4

@@ -18,17 +18,17 @@ def _lib_loaded():
     P.lib()  # raises if the HIP library is missing
 
 
-PATHS = [False, True]  # single-read persistent kernel, two-pass kernels
-PATH_IDS = ["single-read", "two-pass"]
+PATHS = [False, True]  # two-pass kernels, single-read persistent kernel
+PATH_IDS = ["two-pass", "single-read"]
 
 
-@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
-def test_tiny_workload(mode, two_pass):
-    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode, "two_pass", two_pass)
+def test_tiny_workload(mode, single_read):
+    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode, "single_read", single_read)
     k, v = W.gaussian_kv(W.TINY, W.SEED_TINY)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode, two_pass=two_pass)
+    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode, single_read=single_read)
     check_kv(kb, vb, W.TINY.chunk_len, mode, res, dev)
 
 
@@ -41,40 +41,40 @@ def test_tiny_matches_golden_fixture():
             assert np.array_equal(res[key], g[key]), key
 
 
-@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
-def test_one_chunk_workload(two_pass):
+@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
+def test_one_chunk_workload(single_read):
     s = W.ONE_CHUNK
-    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK, "two_pass", two_pass)
+    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK, "single_read", single_read)
     k, v = W.gaussian_kv(s, W.SEED_ONE_CHUNK)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, s.chunk_len, two_pass=two_pass)
+    res, dev = gpu_kv(kb, vb, s.chunk_len, single_read=single_read)
     ref = check_kv(kb, vb, s.chunk_len, O.MODE_4OVER6, res, dev)
     assert 0 < ref["k_use4"] < res["k_codes"].size // 8
 
 
-@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
-def test_heavy_tail_workload(two_pass):
+@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
+def test_heavy_tail_workload(single_read):
     s = W.ONE_CHUNK
-    say("heavy-tail KV", s, "seed", W.SEED_HEAVY, "two_pass", two_pass)
+    say("heavy-tail KV", s, "seed", W.SEED_HEAVY, "single_read", single_read)
     k, v = W.heavy_tail_kv(s, W.SEED_HEAVY)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
     for mode in (O.MODE_4OVER6, O.MODE_FIXED6):
         say("  mode", mode)
-        res, dev = gpu_kv(kb, vb, s.chunk_len, mode, two_pass=two_pass)
+        res, dev = gpu_kv(kb, vb, s.chunk_len, mode, single_read=single_read)
         check_kv(kb, vb, s.chunk_len, mode, res, dev)
 
 
-@pytest.mark.parametrize("two_pass", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("layer", [0, 29])
-def test_full_cache_layer_sampled(layer, two_pass):
+def test_full_cache_layer_sampled(layer, single_read):
     """A full-size layer of the 8-chunk cache ([24, 56320, 128], the launch
     configuration the benchmark times), drawn on the GPU; chunks 0, 3 and 7
     are checked completely against the oracle, and the whole layer's outputs
     against properties that hold at any size."""
     s = W.CACHE_LAYER
-    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "two_pass", two_pass)
+    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "single_read", single_read)
     k, v = W.gaussian_kv(s, W.cache_layer_seed(layer), device="cuda")
-    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, two_pass=two_pass,
+    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, single_read=single_read,
                                      out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     dk = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len)
     dv = P.nvfp4_dequantize(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, s.chunk_len)
@@ -148,10 +148,10 @@ def test_degenerate_values():
         "one spike": (np.where(rng.random((H, T, D)) < 1e-3, 1e4, 0.0), np.eye(T, D)[None].repeat(H, 0)),
     }
     for name, (k, v) in cases.items():
-        for two_pass in PATHS:
-            say("degenerate:", name, "two_pass", two_pass)
+        for single_read in PATHS:
+            say("degenerate:", name, "single_read", single_read)
             kb, vb = _bits(k), _bits(v)
-            res, dev = gpu_kv(kb, vb, L, two_pass=two_pass)
+            res, dev = gpu_kv(kb, vb, L, single_read=single_read)
             check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
 
 
@@ -161,9 +161,11 @@ def test_deterministic_and_stream_ordered():
     k, v = W.gaussian_kv(s, 99, device="cuda")
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
-        a = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
-        b = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
-        c = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, two_pass=True,
+        a = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, single_read=True,
+                                       out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        b = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, single_read=True,
+                                       out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        c = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True,
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     side.synchronize()
     for key in a:
