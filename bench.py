@@ -25,6 +25,31 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kv_two_pass_full_cache_traffic.md")
+
+
+def kernel_sources_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "precision_kv_cache_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per quantize call from the committed rocprofv3 counter
+    summary, or None once the kernel sources differ from the measured ones."""
+    try:
+        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_call: ", "kernel_sources_sha256: ")))
+    except OSError:
+        return None
+    if fields.get("kernel_sources_sha256", "").strip() != kernel_sources_sha256():
+        return None
+    return int(fields["traffic_bytes_per_call"])
 METRIC = "NVFP4 4/6 KV quantize GB/s (bytes in+out) and % of MI355X HBM peak"
 
 
@@ -211,7 +236,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if dominant == "quantize" and not a.single_read else None,
             "bytes_per_launch": qbytes_layer,
         },
         "input_generation_s": round(gen_s, 2),
