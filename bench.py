@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--mode", type=int, default=0, help="0 = 4/6, 1 = fixed 6, 2 = fixed 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-read", action="store_true", help="use the single-read persistent KV kernel")
+    ap.add_argument("--pipelined", action="store_true", help="use the persistent pipelined KV kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
     return ap.parse_args()
 
@@ -129,7 +130,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream,
-                                   single_read=a.single_read)
+                                   single_read=a.single_read, pipelined=a.pipelined)
         if ev is not None:
             ev[1].record(stream)
 
@@ -218,7 +219,7 @@ def main():
                         "chunks of 7040 tokens; 4/6 smooth-quantize every layer, then dequantize the cache",
             "layers": nlayers, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
             "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": step_bytes,
-            "kv_path": "single-read" if a.single_read else "two-pass",
+            "kv_path": "single-read" if a.single_read else ("pipelined" if a.pipelined else "two-pass"),
         },
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "quantize_GBps": round(q_gbps, 1),
@@ -236,7 +237,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic() if dominant == "quantize" and not a.single_read else None,
+            "traffic": measured_traffic() if dominant == "quantize" and not (a.single_read or a.pipelined) else None,
             "bytes_per_launch": qbytes_layer,
         },
         "input_generation_s": round(gen_s, 2),

@@ -90,6 +90,11 @@ typedef enum {
  * two-pass kernels. */
 #define NVFP4_KV_SINGLE_READ 0x200
 
+/* Option bit: the pipelined two-pass form (one launch per (chunk, tensor)
+ * unit; statistics of unit u overlap the quantization of unit u - 1, which
+ * re-reads its input from the Infinity Cache).  Same results. */
+#define NVFP4_KV_PIPELINED 0x400
+
 /* Largest supported head dimension / row length for the KV entry points. */
 #define NVFP4_KV_MAX_D 4096
 

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
   __shared__ float shw[kFusedThreads / 64];
   __shared__ float sh_mean[NB * 16];
   __shared__ unsigned sh_flag;
+  __shared__ float sh_g;
 
   const int w = blockIdx.x;
   if (w >= p.WPH * p.H) {  // spare workgroup: owns no rows
@@ -269,13 +270,16 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
       }
       if (!ok) atomicOr(p.err, 1u);
       sh_flag = ok;
+      // one lane reads the encode scale: a device-scope load of one word by
+      // every lane of every workgroup would be serialized
+      if (ok) sh_g = fetch(&p.genc[u]);
     }
     __syncthreads();
     if (!sh_flag) {  // time-out: results are invalid, the error word says so
       if (p.choice && tid == 0) *reinterpret_cast<uint4*>(p.tally + (size_t)w * 4) = make_uint4(0, 0, 0, 0);
       return;
     }
-    const float g = fetch(&p.genc[u]);
+    const float g = sh_g;
     if (tau == 0) {  // the head's channel means, shared by the workgroup through LDS
       for (int d = tid; d < D; d += kFusedThreads) sh_mean[d] = fetch(&p.kmean[((size_t)c * p.H + h) * D + d]);
       __syncthreads();

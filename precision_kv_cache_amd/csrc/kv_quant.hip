@@ -33,6 +33,7 @@
 
 #include "host_common.hpp"
 #include "kv_fused.hpp"
+#include "kv_pipe.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4kv.h"
 
@@ -110,6 +111,7 @@ struct KVParams {
 
 // ---------------------------------------------------------------- stats ---
 
+template <bool NT>
 __device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, double* sh, float* shw,
                               unsigned* sh_flag) {
   const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
@@ -131,8 +133,8 @@ __device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, 
       for (int q = 0; q < kBatch; ++q) {
         const int r = rb + q * p.RP;
         if (r < r1) {
-          a[q] = load_nt(base + (size_t)r * p.D);
-          b[q] = load_nt(base + (size_t)r * p.D + 8);
+          a[q] = load16<NT>(base + (size_t)r * p.D);
+          b[q] = load16<NT>(base + (size_t)r * p.D + 8);
         }
       }
 #pragma unroll
@@ -186,8 +188,8 @@ __device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, 
       for (int q = 0; q < kBatch; ++q) {
         const int r = rb + q * p.RP;
         if (r < r1) {
-          a[q] = load_nt(base + (size_t)r * p.D);
-          b[q] = load_nt(base + (size_t)r * p.D + 8);
+          a[q] = load16<NT>(base + (size_t)r * p.D);
+          b[q] = load16<NT>(base + (size_t)r * p.D + 8);
         }
       }
 #pragma unroll
@@ -284,7 +286,7 @@ __device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, 
 // ---------------------------------------------------------------- quant ---
 
 // Returns this thread's {blocks kept at +-4, blocks}.
-template <int MODE, bool SMOOTH>
+template <int MODE, bool SMOOTH, bool NT>
 __device__ __forceinline__ uint2 kv_quant_body(const KVParams& p, int tau, int c, int h, int qt, float g) {
   const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
   const bool active = roff < p.RP;
@@ -301,45 +303,11 @@ __device__ __forceinline__ uint2 kv_quant_body(const KVParams& p, int tau, int c
   }
   const int r0 = qt * p.rows_q;
   const int r1 = active ? min(r0 + p.rows_q, p.L) : r0;  // idle lanes take no rows
-  const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
-  const uint16_t* xb = p.x[tau];
-  uint8_t* codes = p.codes[tau];
-  uint8_t* scales = p.scales[tau];
-  unsigned n4 = 0, nblk = 0;
-  for (int rb = r0 + roff; rb < r1; rb += kBatch * p.RP) {
-    uint4 a[kBatch], b[kBatch];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int r = rb + q * p.RP;
-      if (r < r1) {
-        const size_t blk = (row0 + r) * p.NB + col;
-        a[q] = load_nt(xb + blk * 16);
-        b[q] = load_nt(xb + blk * 16 + 8);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int r = rb + q * p.RP;
-      if (r >= r1) continue;
-      const size_t blk = (row0 + r) * p.NB + col;
-      float z[16];
-      unpack16(a[q], b[q], z);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float xs = SMOOTH ? z[i] - m[i] : z[i];  // k' = fl(K - m)
-        z[i] = xs * g;                                  // z = fl(k' * g_enc)
-      }
-      const Block46 qb = quant_block16<MODE>(z);
-      store_nt(codes + blk * 8, qb.lo, qb.hi);
-      store_nt(scales + blk, (uint8_t)qb.scale);
-      n4 += qb.use4;
-      nblk += 1;
-    }
-  }
-  return make_uint2(n4, nblk);
+  return quant_rows<MODE, SMOOTH, NT, kBatch>(p.x[tau], p.codes[tau], p.scales[tau],
+                                              (size_t)h * p.T + (size_t)c * p.L, r0 + roff, r1, p.RP, p.NB, col, m, g);
 }
 
-template <int MODE>
+template <int MODE, bool NT>
 __device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt, unsigned* sh_tally) {
   // tensor scale of (tau, chunk) from the heads' maxima
   float A = 0.0f;
@@ -348,8 +316,8 @@ __device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt, 
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
   if (qt == 0 && h == 0 && threadIdx.x == 0) p.tscale[tau][c] = A / C;
-  const uint2 n = tau == 0 ? kv_quant_body<MODE, true>(p, tau, c, h, qt, g)
-                           : kv_quant_body<MODE, false>(p, tau, c, h, qt, g);
+  const uint2 n = tau == 0 ? kv_quant_body<MODE, true, NT>(p, tau, c, h, qt, g)
+                           : kv_quant_body<MODE, false, NT>(p, tau, c, h, qt, g);
   if (p.choice) {
     const unsigned t[4] = {tau == 0 ? n.x : 0u, tau == 0 ? n.y : 0u, tau == 1 ? n.x : 0u, tau == 1 ? n.y : 0u};
     store_wg_tally(p.tally + ((((size_t)c * 2 + tau) * p.H + h) * p.nqt + qt) * 4, t, sh_tally);
@@ -367,7 +335,7 @@ __global__ __launch_bounds__(kMaxThreads) void kv_stats_kernel(KVParams p) {
   idx /= p.nst;
   const int h = idx % p.H;
   idx /= p.H;
-  kv_stats_tile(p, p.s0 + (int)(idx >> 1), (int)(idx & 1), h, ts, sh, shw, &sh_flag);
+  kv_stats_tile<true>(p, p.s0 + (int)(idx >> 1), (int)(idx & 1), h, ts, sh, shw, &sh_flag);
 }
 
 // Quantization of chunks [q0, q1): one workgroup per (chunk, tensor, head,
@@ -381,7 +349,7 @@ __global__ __launch_bounds__(kMaxThreads) void kv_quant_kernel(KVParams p) {
   idx /= p.nqt;
   const int h = idx % p.H;
   idx /= p.H;
-  kv_quant_tile<MODE>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt, sh_tally);
+  kv_quant_tile<MODE, true>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt, sh_tally);
 }
 
 __global__ void zero_counters_kernel(unsigned* cnt, int n) {
@@ -505,7 +473,9 @@ extern "C" NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int 
   if (!kv_shape_ok(H, T, D, chunk_len) || H == 0 || T == 0) return 0;
   const size_t two_pass = kv_workspace_layout(kv_geom(H, T, D, chunk_len)).total;
   const size_t fused = fused_workspace_bound(H, T, D, chunk_len);
-  return two_pass > fused ? two_pass : fused;
+  const size_t pipe = pipe_workspace_bound(H, T, D, chunk_len);
+  const size_t m = two_pass > fused ? two_pass : fused;
+  return m > pipe ? m : pipe;
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
@@ -516,7 +486,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
                                                     size_t workspace_bytes, void* stream) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len)) return NVFP4_ERR_SHAPE;
   const bool single_read = (mode & NVFP4_KV_SINGLE_READ) != 0;
-  mode &= ~NVFP4_KV_SINGLE_READ;
+  const bool pipelined = (mode & NVFP4_KV_PIPELINED) != 0;
+  mode &= ~(NVFP4_KV_SINGLE_READ | NVFP4_KV_PIPELINED);
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
   if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
@@ -539,6 +510,18 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();  // start from a clean error state
+  if (pipelined) {
+    PipeParams q;
+    q.x[0] = k; q.x[1] = v;
+    q.codes[0] = k_codes; q.codes[1] = v_codes;
+    q.scales[0] = k_scales; q.scales[1] = v_scales;
+    q.tscale[0] = k_tensor_scale; q.tscale[1] = v_tensor_scale;
+    q.kmean = k_mean;
+    q.mode = mode;
+    q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
+    const int rc = pipe_try_launch(q, workspace, workspace_bytes, choice_counts, s);
+    if (rc <= 0) return rc;  // enqueued, or a launch error
+  }
   if (single_read) {
     FusedParams f;
     f.x[0] = k; f.x[1] = v;

@@ -182,11 +182,61 @@ __device__ __forceinline__ uint4 load_nt(const uint16_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// NT = false: an ordinary load, which allocates in the Infinity Cache so
+// that a second read of the same data soon after is served from there.
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  if (NT) return load_nt(p);
+  return *reinterpret_cast<const uint4*>(p);
+}
 __device__ __forceinline__ void store_nt(uint8_t* p, uint32_t lo, uint32_t hi) {
   const u32x2 v = {lo, hi};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }
 __device__ __forceinline__ void store_nt(uint8_t* p, uint8_t b) { __builtin_nontemporal_store(b, p); }
+
+// The quantize loop of one lane: rows r, r + step, ... < r_end of a
+// [rows, NB blocks] slab whose first row is row0 (absolute row of the
+// [H, T] row space), column block col.  m: the channel means subtracted
+// first when SMOOTH (the K path), g: the encode scale.  BATCH rows' loads are
+// issued before the first is used.  Returns {blocks kept at +-4, blocks}.
+template <int MODE, bool SMOOTH, bool NT, int BATCH>
+__device__ __forceinline__ uint2 quant_rows(const uint16_t* xb, uint8_t* codes, uint8_t* scales, size_t row0,
+                                            int r, int r_end, int step, int NB, int col, const float (&m)[16],
+                                            float g) {
+  unsigned n4 = 0, nblk = 0;
+  for (int rb = r; rb < r_end; rb += BATCH * step) {
+    uint4 a[BATCH], b[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int rr = rb + q * step;
+      if (rr < r_end) {
+        const size_t blk = (row0 + rr) * NB + col;
+        a[q] = load16<NT>(xb + blk * 16);
+        b[q] = load16<NT>(xb + blk * 16 + 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int rr = rb + q * step;
+      if (rr >= r_end) continue;
+      const size_t blk = (row0 + rr) * NB + col;
+      float z[16];
+      unpack16(a[q], b[q], z);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float xs = SMOOTH ? z[i] - m[i] : z[i];  // k' = fl(K - m)
+        z[i] = xs * g;                                  // z = fl(k' * g_enc)
+      }
+      const Block46 qb = quant_block16<MODE>(z);
+      store_nt(codes + blk * 8, qb.lo, qb.hi);
+      store_nt(scales + blk, (uint8_t)qb.scale);
+      n4 += qb.use4;
+      nblk += 1;
+    }
+  }
+  return make_uint2(n4, nblk);
+}
 
 // Hand-off of small results between workgroups of one kernel.
 //

@@ -44,12 +44,12 @@ def kv_outputs(H, T, D, L, counts=True):
     return out
 
 
-def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True, single_read=False):
+def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True, path=None):
     """K, V given as numpy bf16 bits [H, T, D] -> GPU outputs as numpy."""
     k = W.from_bits(kb, "cuda")
     v = W.from_bits(vb, "cuda")
     H, T, D = kb.shape
-    out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts, single_read=single_read,
+    out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts, **(path or {}),
                                      out=kv_outputs(H, T, D, L, counts))
     torch.cuda.synchronize()
     return {key: t.cpu().numpy() for key, t in out.items()}, out

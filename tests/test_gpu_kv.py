@@ -18,17 +18,17 @@ def _lib_loaded():
     P.lib()  # raises if the HIP library is missing
 
 
-PATHS = [False, True]  # two-pass kernels, single-read persistent kernel
-PATH_IDS = ["two-pass", "single-read"]
+PATHS = [{}, {"single_read": True}, {"pipelined": True}]  # keyword options of the binding
+PATH_IDS = ["two-pass", "single-read", "pipelined"]
 
 
-@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
-def test_tiny_workload(mode, single_read):
-    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode, "single_read", single_read)
+def test_tiny_workload(mode, path):
+    say("tiny KV", W.TINY, "seed", W.SEED_TINY, "mode", mode, "path", path)
     k, v = W.gaussian_kv(W.TINY, W.SEED_TINY)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode, single_read=single_read)
+    res, dev = gpu_kv(kb, vb, W.TINY.chunk_len, mode, path=path)
     check_kv(kb, vb, W.TINY.chunk_len, mode, res, dev)
 
 
@@ -41,40 +41,40 @@ def test_tiny_matches_golden_fixture():
             assert np.array_equal(res[key], g[key]), key
 
 
-@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
-def test_one_chunk_workload(single_read):
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_one_chunk_workload(path):
     s = W.ONE_CHUNK
-    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK, "single_read", single_read)
+    say("one chunk KV", s, "seed", W.SEED_ONE_CHUNK, "path", path)
     k, v = W.gaussian_kv(s, W.SEED_ONE_CHUNK)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, s.chunk_len, single_read=single_read)
+    res, dev = gpu_kv(kb, vb, s.chunk_len, path=path)
     ref = check_kv(kb, vb, s.chunk_len, O.MODE_4OVER6, res, dev)
     assert 0 < ref["k_use4"] < res["k_codes"].size // 8
 
 
-@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
-def test_heavy_tail_workload(single_read):
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_heavy_tail_workload(path):
     s = W.ONE_CHUNK
-    say("heavy-tail KV", s, "seed", W.SEED_HEAVY, "single_read", single_read)
+    say("heavy-tail KV", s, "seed", W.SEED_HEAVY, "path", path)
     k, v = W.heavy_tail_kv(s, W.SEED_HEAVY)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
     for mode in (O.MODE_4OVER6, O.MODE_FIXED6):
         say("  mode", mode)
-        res, dev = gpu_kv(kb, vb, s.chunk_len, mode, single_read=single_read)
+        res, dev = gpu_kv(kb, vb, s.chunk_len, mode, path=path)
         check_kv(kb, vb, s.chunk_len, mode, res, dev)
 
 
-@pytest.mark.parametrize("single_read", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("layer", [0, 29])
-def test_full_cache_layer_sampled(layer, single_read):
+def test_full_cache_layer_sampled(layer, path):
     """A full-size layer of the 8-chunk cache ([24, 56320, 128], the launch
     configuration the benchmark times), drawn on the GPU; chunks 0, 3 and 7
     are checked completely against the oracle, and the whole layer's outputs
     against properties that hold at any size."""
     s = W.CACHE_LAYER
-    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "single_read", single_read)
+    say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "path", path)
     k, v = W.gaussian_kv(s, W.cache_layer_seed(layer), device="cuda")
-    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, single_read=single_read,
+    out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, **path,
                                      out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     dk = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len)
     dv = P.nvfp4_dequantize(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, s.chunk_len)
@@ -148,10 +148,10 @@ def test_degenerate_values():
         "one spike": (np.where(rng.random((H, T, D)) < 1e-3, 1e4, 0.0), np.eye(T, D)[None].repeat(H, 0)),
     }
     for name, (k, v) in cases.items():
-        for single_read in PATHS:
-            say("degenerate:", name, "single_read", single_read)
+        for path in PATHS:
+            say("degenerate:", name, "path", path)
             kb, vb = _bits(k), _bits(v)
-            res, dev = gpu_kv(kb, vb, L, single_read=single_read)
+            res, dev = gpu_kv(kb, vb, L, path=path)
             check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
 
 
@@ -167,10 +167,13 @@ def test_deterministic_and_stream_ordered():
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
         c = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True,
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        d = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, pipelined=True,
+                                       out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     side.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
-        if key != "k_mean":  # the two paths combine the fp64 channel sums in different orders
+        assert torch.equal(c[key], d[key]), key  # same statistics tiles, same reduction order
+        if key != "k_mean":  # the single-read kernel combines the fp64 channel sums in another order
             assert torch.equal(a[key], c[key]), key
 
 
