@@ -242,9 +242,111 @@ def main():
         },
         "input_generation_s": round(gen_s, 2),
     }
+    outs.clear()
+    deq.clear()
+    torch.cuda.empty_cache()
+    result["act_weight"] = act_weight_timing(P, W, a.mode, stream)
+    result["heavy_tail_report"] = heavy_tail_report(P, W)
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def act_weight_timing(P, W, mode, stream, reps=20):
+    """The GEMM-operand quantizers on their workload: activation [16384, 3072]
+    with the 16-point RHT and 1D blocks, weight [3072, 3072] with 16x16
+    tiles.  Several input copies are rotated (at least 400 MB in all) so no
+    call finds its input in the 256 MB Infinity Cache."""
+    import torch
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    x, sign_mask, w = W.act_weight(device="cuda")
+    xs = [x] + [x.clone() for _ in range(3)]
+    wsz = [w] + [w.clone() for _ in range(21)]
+    rows, cols = x.shape
+    n = x.numel()
+    xo = P.nvfp4_quantize_1d(x, mode, hadamard=True, sign_mask=sign_mask)
+    wo = P.nvfp4_quantize_2d(w, mode)
+    xws = torch.empty(int(P.lib().nvfp4_quantize_1d_workspace_bytes(rows, cols)) or 1, dtype=torch.uint8,
+                      device="cuda")
+    wws = torch.empty(int(P.lib().nvfp4_quantize_2d_workspace_bytes(*w.shape)) or 1, dtype=torch.uint8,
+                      device="cuda")
+    res = {}
+    for name, fn, nbytes in (
+            ("act_rht_quantize_1d", lambda i: P.nvfp4_quantize_1d(xs[i % len(xs)], mode, hadamard=True,
+                                                                  sign_mask=sign_mask, out=xo, workspace=xws,
+                                                                  stream=stream),
+             2 * n + n // 2 + n // 16 + 4),
+            ("weight_quantize_2d", lambda i: P.nvfp4_quantize_2d(wsz[i % len(wsz)], mode, out=wo, workspace=wws,
+                                                                 stream=stream),
+             2 * w.numel() + w.numel() // 2 + w.numel() // 256 + 4)):
+        for i in range(3):
+            fn(i)
+        e0, e1 = E(), E()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                     "bytes": nbytes}
+    res["shapes"] = {"activation": [rows, cols], "weight": list(w.shape)}
+    return res
+
+
+def heavy_tail_report(P, W):
+    """4/6 against fixed-6 on the heavy-tailed chunk (Student-t(3) with per-
+    channel scales, [24, 7040, 128]): reconstruction MSE in fp64 of the
+    dequantized bf16 against the input, and the share of blocks keeping the
+    +-4 candidate by decile of the block's largest magnitude.  A block's
+    choice is read off its codes: the block maximum encodes to 4 (code 6)
+    under +-4 and to 6 (code 7) under +-6; blocks whose largest code is
+    neither (tiny E4M3 scales) are counted apart."""
+    import torch
+
+    s = W.ONE_CHUNK
+    k, v = W.heavy_tail_kv(s, W.SEED_HEAVY, device="cuda")
+    L = s.chunk_len
+    rep = {"shape": [s.H, s.T, s.D], "chunk_len": L}
+    mags = None
+    for mode, name in ((P.MODE_4OVER6, "4over6"), (P.MODE_FIXED6, "fixed6")):
+        o = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=True)
+        dk = P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L)
+        dv = P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L)
+        entry = {}
+        for t, x, d in (("K", k, dk), ("V", v, dv)):
+            x64, d64 = x.double(), d.double()
+            mse = torch.mean((d64 - x64) ** 2).item()
+            entry[t] = {"mse": mse, "rel_mse": mse / torch.mean(x64 ** 2).item()}
+        cc = o["choice_counts"].cpu().tolist()
+        entry["kept4_share"] = {"K": cc[0][1] / max(1, sum(cc[0])), "V": cc[1][1] / max(1, sum(cc[1]))}
+        if mode == P.MODE_4OVER6:
+            lut = torch.tensor([0, 1, 2, 3, 4, 5, 6, 7, 0, 1, 2, 3, 4, 5, 6, 7], dtype=torch.uint8, device="cuda")
+            deciles = {}
+            for t, x, codes, mean in (("K", k, o["k_codes"], o["k_mean"]), ("V", v, o["v_codes"], None)):
+                xf = x.float()
+                if mean is not None:  # smoothed K: x' = K - mean of its chunk
+                    xf = xf - mean.permute(1, 0, 2).repeat_interleave(L, dim=1)
+                amax = xf.abs().reshape(-1, 16).amax(1)
+                q = codes.reshape(-1, 8)
+                top = torch.maximum(lut[(q & 15).long()], lut[(q >> 4).long()]).amax(1)
+                edges = torch.quantile(amax[amax > 0].float()[::97], torch.linspace(0, 1, 11, device="cuda"))
+                bins = torch.bucketize(amax, edges[1:-1])
+                rows = []
+                for b in range(10):
+                    m = bins == b
+                    nb = int(m.sum())
+                    rows.append({"blocks": nb, "kept4": int(((top == 6) & m).sum()),
+                                 "kept6": int(((top == 7) & m).sum()),
+                                 "other": int(((top != 6) & (top != 7) & m).sum())})
+                deciles[t] = rows
+            entry["by_block_max_decile"] = deciles
+        rep[name] = entry
+    rep["mse_ratio_4over6_to_fixed6"] = {t: rep["4over6"][t]["mse"] / rep["fixed6"][t]["mse"] for t in ("K", "V")}
+    return rep
 
 
 def cpu_baseline(ks, vs, L, mode, target_s):
