@@ -28,13 +28,18 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kv_two_pass_full_cache_traffic.md")
 
 
+# the sources the KV quantize call's kernels are built from
+KV_KERNEL_SOURCES = ("precision_kv_cache_amd/csrc/kv_quant.hip", "precision_kv_cache_amd/csrc/nvfp4_device.hpp",
+                     "precision_kv_cache_amd/csrc/host_common.hpp", "precision_kv_cache_amd/csrc/kv_fused.hpp",
+                     "precision_kv_cache_amd/csrc/kv_pipe.hpp", "include/nvfp4kv.h")
+
+
 def kernel_sources_sha256():
-    import glob
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "precision_kv_cache_amd", "csrc", "*"))):
-        h.update(os.path.basename(p).encode())
-        with open(p, "rb") as f:
+    for rel in KV_KERNEL_SOURCES:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 

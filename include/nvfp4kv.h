@@ -154,7 +154,8 @@ NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, i
 NVFP4KV_API int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                                  const float* mean, int H, int T, int D, int chunk_len, uint16_t* out, void* stream) NVFP4KV_NOEXCEPT;
 
-/* Workspace bytes of nvfp4_quantize_1d / nvfp4_quantize_2d (a few words). */
+/* Workspace bytes of nvfp4_quantize_1d / nvfp4_quantize_2d (under 9 KB: the
+ * tensor maximum and per-workgroup partial maxima). */
 NVFP4KV_API size_t nvfp4_quantize_1d_workspace_bytes(int rows, int cols) NVFP4KV_NOEXCEPT;
 NVFP4KV_API size_t nvfp4_quantize_2d_workspace_bytes(int rows, int cols) NVFP4KV_NOEXCEPT;
 

@@ -4,9 +4,10 @@
 // random-sign Hadamard transform, and weights with 2D 16x16 tiles.
 //
 // Both need the tensor's largest magnitude before any block can be encoded,
-// so each is two passes: an amax pass (order-free, merged with an integer
-// atomic max on the non-negative fp32 bit pattern) and the quantize pass,
-// which recomputes the rotation in registers instead of storing it.
+// so each is two passes: an amax pass (every workgroup stores its partial
+// maximum in its own workspace slot, one small workgroup combines them; a
+// shared atomic would serialize thousands of workgroups) and the quantize
+// pass, which recomputes the rotation in registers instead of storing it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,6 +18,9 @@
 namespace nvfp4 {
 
 constexpr int kAWThreads = 256;
+constexpr int kAmaxMaxWG = 2048;  // workgroups of the amax pass (grid-stride)
+// workspace: [0, 256) the tensor maximum's bits; [256, ...) partial maxima
+constexpr size_t kAWWorkspace = 256 + (size_t)kAmaxMaxWG * sizeof(float);
 
 // 16-point random-sign Hadamard transform of one block, in place:
 // u = s * x (exact sign flips), fast Walsh-Hadamard butterflies with strides
@@ -44,15 +48,10 @@ __device__ __forceinline__ void sign_flips(uint32_t mask, uint32_t (&flip)[16]) 
   for (int j = 0; j < 16; ++j) flip[j] = ((mask >> j) & 1u) << 31;
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
 // Largest |value| over nseg 16-element segments (optionally rotated).
 template <bool RHT>
 __global__ __launch_bounds__(kAWThreads) void amax16_kernel(const uint16_t* x, long long nseg, uint32_t sign_mask,
-                                                            uint32_t* amax_bits) {
+                                                            float* partial) {
   __shared__ float shw[kAWThreads / 64];
   uint32_t flip[16];
   sign_flips(sign_mask, flip);
@@ -73,7 +72,22 @@ __global__ __launch_bounds__(kAWThreads) void amax16_kernel(const uint16_t* x, l
   if (threadIdx.x == 0) {
     float m = 0.0f;
     for (int w = 0; w < (int)(blockDim.x / 64); ++w) m = fmaxf(m, shw[w]);
-    atomicMax(amax_bits, __float_as_uint(m));  // non-negative floats order as integers
+    partial[blockIdx.x] = m;
+  }
+}
+
+// The tensor maximum from n partial maxima (one workgroup).
+__global__ __launch_bounds__(kAWThreads) void amax_reduce_kernel(const float* partial, int n, uint32_t* amax_bits) {
+  __shared__ float shw[kAWThreads / 64];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, partial[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x / 64); ++w) a = fmaxf(a, shw[w]);
+    *amax_bits = __float_as_uint(a);
   }
 }
 
@@ -217,11 +231,26 @@ static bool aw_shape_ok(int rows, int cols, bool tiles) {
 }
 
 extern "C" NVFP4KV_API size_t nvfp4_quantize_1d_workspace_bytes(int rows, int cols) noexcept {
-  return aw_shape_ok(rows, cols, false) ? 256 : 0;
+  return aw_shape_ok(rows, cols, false) ? kAWWorkspace : 0;
 }
 
 extern "C" NVFP4KV_API size_t nvfp4_quantize_2d_workspace_bytes(int rows, int cols) noexcept {
-  return aw_shape_ok(rows, cols, true) ? 256 : 0;
+  return aw_shape_ok(rows, cols, true) ? kAWWorkspace : 0;
+}
+
+// amax pass over nseg 16-element segments, then the reduction into the
+// workspace's first word.
+static void launch_amax(const uint16_t* x, long long nseg, bool rht, uint32_t sign_mask, void* workspace,
+                        hipStream_t s) {
+  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256);
+  const unsigned g0 = grid_for(nseg, 4);
+  const unsigned ga = g0 < (unsigned)kAmaxMaxWG ? g0 : (unsigned)kAmaxMaxWG;
+  if (rht)
+    amax16_kernel<true><<<ga, kAWThreads, 0, s>>>(x, nseg, sign_mask, partial);
+  else
+    amax16_kernel<false><<<ga, kAWThreads, 0, s>>>(x, nseg, sign_mask, partial);
+  amax_reduce_kernel<<<1, kAWThreads, 0, s>>>(partial, (int)ga, amax);
 }
 
 extern "C" NVFP4KV_API int nvfp4_quantize_1d(const uint16_t* x, int rows, int cols, int mode, int hadamard,
@@ -232,24 +261,20 @@ extern "C" NVFP4KV_API int nvfp4_quantize_1d(const uint16_t* x, int rows, int co
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (rows == 0) return NVFP4_OK;
   if (!x || !codes || !scales || !tensor_scale) return NVFP4_ERR_NULL;
-  if (!workspace || workspace_bytes < 256) return NVFP4_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kAWWorkspace) return NVFP4_ERR_WORKSPACE;
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   const size_t n = (size_t)rows * cols;
   const Range in[1] = {range_of(x, n * 2)};
   const Range out[4] = {range_of(codes, n / 2), range_of(scales, n / 16), range_of(tensor_scale, 4),
-                        range_of(workspace, 256)};
+                        range_of(workspace, kAWWorkspace)};
   if (any_alias(in, 1, out, 4)) return NVFP4_ERR_ALIAS;
   hipStream_t s = as_stream(stream);
   uint32_t* amax = static_cast<uint32_t*>(workspace);
   const long long nblk = (long long)(n / 16);
   (void)hipGetLastError();
-  zero_u32_kernel<<<1, 64, 0, s>>>(amax, 1);
-  const unsigned ga = grid_for(nblk, 4), gq = grid_for(nblk, 2);
-  if (hadamard)
-    amax16_kernel<true><<<ga, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax);
-  else
-    amax16_kernel<false><<<ga, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax);
+  launch_amax(x, nblk, hadamard != 0, sign_mask, workspace, s);
+  const unsigned gq = grid_for(nblk, 2);
 #define NVFP4_Q1D(MODE)                                                                                   \
   (hadamard ? quant1d_kernel<MODE, true><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax, codes, scales, \
                                                                    tensor_scale)                          \
@@ -271,19 +296,18 @@ extern "C" NVFP4KV_API int nvfp4_quantize_2d(const uint16_t* w, int rows, int co
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (rows == 0) return NVFP4_OK;
   if (!w || !codes || !scales || !tensor_scale) return NVFP4_ERR_NULL;
-  if (!workspace || workspace_bytes < 256) return NVFP4_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kAWWorkspace) return NVFP4_ERR_WORKSPACE;
   if (!aligned(w, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   const size_t n = (size_t)rows * cols;
   const Range in[1] = {range_of(w, n * 2)};
   const Range out[4] = {range_of(codes, n / 2), range_of(scales, n / 256), range_of(tensor_scale, 4),
-                        range_of(workspace, 256)};
+                        range_of(workspace, kAWWorkspace)};
   if (any_alias(in, 1, out, 4)) return NVFP4_ERR_ALIAS;
   hipStream_t s = as_stream(stream);
   uint32_t* amax = static_cast<uint32_t*>(workspace);
   (void)hipGetLastError();
-  zero_u32_kernel<<<1, 64, 0, s>>>(amax, 1);
-  amax16_kernel<false><<<grid_for((long long)(n / 16), 4), kAWThreads, 0, s>>>(w, (long long)(n / 16), 0u, amax);
+  launch_amax(w, (long long)(n / 16), false, 0u, workspace, s);
   const long long ntiles = (long long)(rows / 16) * (cols / 16);
   const unsigned gq = grid_for((ntiles + 3) / 4 * 64, 1);
   switch (mode) {

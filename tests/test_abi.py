@@ -105,8 +105,9 @@ def test_dequant_and_1d_2d_argument_errors():
                               V(FAKE + 16), None) == ALIAS
     assert L.nvfp4_dequantize(V(FAKE), V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), V(FAKE + (4 << 30) + 4), 1, 32,
                               32, 32, V(FAKE + (3 << 30)), None) == ALIGN
+    ws1 = L.nvfp4_quantize_1d_workspace_bytes(16, 32)
     args1d = [V(FAKE), 16, 32, 0, 1, 0, V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), V(FAKE + (3 << 30)),
-              V(FAKE + (4 << 30)), 256, None]
+              V(FAKE + (4 << 30)), ws1, None]
     a = list(args1d); a[2] = 33
     assert L.nvfp4_quantize_1d(*a) == SHAPE
     a = list(args1d); a[3] = 7
@@ -116,7 +117,7 @@ def test_dequant_and_1d_2d_argument_errors():
     a = list(args1d); a[6] = V(FAKE + 32)
     assert L.nvfp4_quantize_1d(*a) == ALIAS
     assert L.nvfp4_quantize_2d(V(FAKE), 24, 32, 0, V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), V(FAKE + (3 << 30)),
-                               V(FAKE + (4 << 30)), 256, None) == SHAPE
+                               V(FAKE + (4 << 30)), L.nvfp4_quantize_2d_workspace_bytes(32, 32), None) == SHAPE
     assert L.nvfp4_dequantize_2d(V(FAKE), V(FAKE + (1 << 30)), None, 32, 32, V(FAKE + (2 << 30)), None) == NULL
     assert L.nvfp4_diag_e2m1_encode(None, 10, None, None) == NULL
     assert L.nvfp4_diag_candidates(None, -1, None, None, None) == SHAPE
