@@ -96,6 +96,9 @@ template <int MODE, bool RHT>
 __global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, long long nblk, uint32_t sign_mask,
                                                              const uint32_t* amax_bits, uint8_t* codes,
                                                              uint8_t* scales, float* tensor_scale) {
+  __shared__ float2 sh_tab[128];
+  fill_scale_table(sh_tab);
+  __syncthreads();
   const float A = __uint_as_float(*amax_bits);
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, 
     if (RHT) rht16(z, flip);
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = z[i] * g;
-    const Block46 q = quant_block16<MODE>(z);
+    const Block46 q = quant_block16<MODE>(z, sh_tab);
     *reinterpret_cast<uint2*>(codes + f * 8) = make_uint2(q.lo, q.hi);
     scales[f] = (uint8_t)q.scale;
   }
@@ -124,6 +127,9 @@ template <int MODE>
 __global__ __launch_bounds__(kAWThreads) void quant2d_kernel(const uint16_t* w, int rows, int cols,
                                                              const uint32_t* amax_bits, uint8_t* codes,
                                                              uint8_t* scales, float* tensor_scale) {
+  __shared__ float2 sh_tab[128];
+  fill_scale_table(sh_tab);
+  __syncthreads();
   const float A = __uint_as_float(*amax_bits);
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
@@ -155,15 +161,15 @@ __global__ __launch_bounds__(kAWThreads) void quant2d_kernel(const uint16_t* w, 
     const uint32_t s = candidate_codes(t);
     uint32_t lo, hi, scale, use4;
     if (MODE == kModeFixed6 || MODE == kModeFixed4) {
-      const float S = MODE == kModeFixed6 ? e4m3_byte<0>(s) : e4m3_byte<1>(s);
-      const Encoded16 e = encode16(z, S, recip_e4m3(S));
+      const float2 sc = sh_tab[MODE == kModeFixed6 ? (s & 0xffu) : (s >> 8)];
+      const Encoded16 e = encode16(z, sc.x, sc.y);
       lo = e.lo; hi = e.hi;
       scale = MODE == kModeFixed6 ? (s & 0xffu) : (s >> 8);
       use4 = MODE == kModeFixed4;
     } else {
-      const float S6 = e4m3_byte<0>(s), S4 = e4m3_byte<1>(s);
-      const Encoded16 e6 = encode16(z, S6, recip_e4m3(S6));
-      const Encoded16 e4 = encode16(z, S4, recip_e4m3(S4));
+      const float2 c6 = sh_tab[s & 0xffu], c4 = sh_tab[s >> 8];
+      const Encoded16 e6 = encode16(z, c6.x, c6.y);
+      const Encoded16 e4 = encode16(z, c4.x, c4.y);
       float err6 = e6.err_lo + e6.err_hi, err4 = e4.err_lo + e4.err_hi;
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {  // pairwise tree over the 16 tile rows

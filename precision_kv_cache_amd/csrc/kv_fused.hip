@@ -38,12 +38,15 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
   __shared__ float sh_mean[NB * 16];
   __shared__ unsigned sh_flag;
   __shared__ float sh_g;
+  __shared__ float2 sh_tab[128];
 
   const int w = blockIdx.x;
   if (w >= p.WPH * p.H) {  // spare workgroup: owns no rows
     if (p.choice && threadIdx.x == 0) *reinterpret_cast<uint4*>(p.tally + (size_t)w * 4) = make_uint4(0, 0, 0, 0);
     return;
   }
+  fill_scale_table(sh_tab);
+  __syncthreads();
   const int h = w / p.WPH, j = w % p.WPH;
   const int tid = threadIdx.x, col = tid % NB, roff = tid / NB;
   const int r0 = j * p.RPW;
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(kFusedThreads, kFusedWavesPerEU) void kv_fused_kern
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) z[i] = z[i] * g;  // z = fl(k' * g_enc)
-        const Block46 q = quant_block16<MODE>(z);
+        const Block46 q = quant_block16<MODE>(z, sh_tab);
         const size_t blk = ((size_t)h * p.T + (size_t)c * p.L + (r0 + roff + k * RPP)) * NB + col;
         store_nt(codes + blk * 8, q.lo, q.hi);
         store_nt(scales + blk, (uint8_t)q.scale);

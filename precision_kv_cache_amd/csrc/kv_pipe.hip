@@ -252,8 +252,11 @@ __global__ __launch_bounds__(kPipeThreads) void kv_pipe_kernel(PipeParams p) {
   __shared__ float sh_mean[kD];
   __shared__ float shw[kPipeThreads / 64];
   __shared__ unsigned sh_flag;
+  __shared__ float2 sh_tab[128];
   const int tid = threadIdx.x;
   const long long b = blockIdx.x, G = gridDim.x;
+  fill_scale_table(sh_tab);
+  __syncthreads();
   const int U = 2 * p.nc;
   const long long ns = (long long)p.H * p.nst, nq = (long long)p.H * p.nqt;
   const int col = tid % kNB, roff = tid / kNB;
@@ -314,10 +317,10 @@ __global__ __launch_bounds__(kPipeThreads) void kv_pipe_kernel(PipeParams p) {
       const int r1 = min(r0 + kPipeQuantRows, p.L);
       const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
       const uint2 n = tau == 0
-          ? quant_rows<MODE, true, false, kQuantBatch>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
-                                                       kQuantRowsPerPass, kNB, col, m, g)
-          : quant_rows<MODE, false, false, kQuantBatch>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff, r1,
-                                                        kQuantRowsPerPass, kNB, col, m, g);
+          ? quant_rows<MODE, true, false, kQuantBatch, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
+                                                            kQuantRowsPerPass, kNB, col, m, g, sh_tab)
+          : quant_rows<MODE, false, false, kQuantBatch, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff,
+                                                             r1, kQuantRowsPerPass, kNB, col, m, g, sh_tab);
       t4[2 * tau] += n.x;
       t4[2 * tau + 1] += n.y;
     }

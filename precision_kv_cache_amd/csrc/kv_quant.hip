@@ -285,9 +285,11 @@ __device__ void kv_stats_tile(const KVParams& p, int c, int tau, int h, int ts, 
 
 // ---------------------------------------------------------------- quant ---
 
-// Returns this thread's {blocks kept at +-4, blocks}.
-template <int MODE, bool SMOOTH, bool NT>
-__device__ __forceinline__ uint2 kv_quant_body(const KVParams& p, int tau, int c, int h, int qt, float g) {
+// Returns this thread's {blocks kept at +-4, blocks}.  Lane (roff, col)
+// takes rows r0 + roff, r0 + roff + RP, ... of the tile.
+template <int MODE, bool SMOOTH, bool NT, int NBC>
+__device__ __forceinline__ uint2 kv_quant_body(const KVParams& p, int tau, int c, int h, int qt, float g,
+                                               const float2* tab) {
   const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
   const bool active = roff < p.RP;
   float m[16];
@@ -303,12 +305,14 @@ __device__ __forceinline__ uint2 kv_quant_body(const KVParams& p, int tau, int c
   }
   const int r0 = qt * p.rows_q;
   const int r1 = active ? min(r0 + p.rows_q, p.L) : r0;  // idle lanes take no rows
-  return quant_rows<MODE, SMOOTH, NT, kBatch>(p.x[tau], p.codes[tau], p.scales[tau],
-                                              (size_t)h * p.T + (size_t)c * p.L, r0 + roff, r1, p.RP, p.NB, col, m, g);
+  return quant_rows<MODE, SMOOTH, NT, kBatch, NBC>(p.x[tau], p.codes[tau], p.scales[tau],
+                                                   (size_t)h * p.T + (size_t)c * p.L, r0 + roff, r1, p.RP,
+                                                   p.NB, col, m, g, tab);
 }
 
-template <int MODE, bool NT>
-__device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt, unsigned* sh_tally) {
+template <int MODE, bool NT, int NBC>
+__device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt, unsigned* sh_tally,
+                              const float2* tab) {
   // tensor scale of (tau, chunk) from the heads' maxima
   float A = 0.0f;
   const float* ha = p.hamax + ((size_t)tau * p.nc + c) * p.H;
@@ -316,8 +320,8 @@ __device__ void kv_quant_tile(const KVParams& p, int c, int tau, int h, int qt, 
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
   if (qt == 0 && h == 0 && threadIdx.x == 0) p.tscale[tau][c] = A / C;
-  const uint2 n = tau == 0 ? kv_quant_body<MODE, true, NT>(p, tau, c, h, qt, g)
-                           : kv_quant_body<MODE, false, NT>(p, tau, c, h, qt, g);
+  const uint2 n = tau == 0 ? kv_quant_body<MODE, true, NT, NBC>(p, tau, c, h, qt, g, tab)
+                           : kv_quant_body<MODE, false, NT, NBC>(p, tau, c, h, qt, g, tab);
   if (p.choice) {
     const unsigned t[4] = {tau == 0 ? n.x : 0u, tau == 0 ? n.y : 0u, tau == 1 ? n.x : 0u, tau == 1 ? n.y : 0u};
     store_wg_tally(p.tally + ((((size_t)c * 2 + tau) * p.H + h) * p.nqt + qt) * 4, t, sh_tally);
@@ -339,17 +343,21 @@ __global__ __launch_bounds__(kMaxThreads) void kv_stats_kernel(KVParams p) {
 }
 
 // Quantization of chunks [q0, q1): one workgroup per (chunk, tensor, head,
-// tile).  Only 64 bytes of LDS (the choice tally), so occupancy is set by
-// registers.
-template <int MODE>
+// tile).  About 1 KB of LDS (the scale table, the choice tally), so
+// occupancy is set by registers.
+// NBC: blocks per row fixed at compile time (8 for D = 128), or 0.
+template <int MODE, int NBC>
 __global__ __launch_bounds__(kMaxThreads) void kv_quant_kernel(KVParams p) {
   __shared__ unsigned sh_tally[4 * (kMaxThreads / 64)];
+  __shared__ float2 sh_tab[128];
+  fill_scale_table(sh_tab);
+  __syncthreads();
   unsigned idx = blockIdx.x;
   const int qt = idx % p.nqt;
   idx /= p.nqt;
   const int h = idx % p.H;
   idx /= p.H;
-  kv_quant_tile<MODE, true>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt, sh_tally);
+  kv_quant_tile<MODE, true, NBC>(p, p.q0 + (int)(idx >> 1), (int)(idx & 1), h, qt, sh_tally, sh_tab);
 }
 
 __global__ void zero_counters_kernel(unsigned* cnt, int n) {
@@ -564,10 +572,20 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
     const long long ns = (long long)(p.s1 - p.s0) * 2 * H * g.nst;
     const long long nq = (long long)(p.q1 - p.q0) * 2 * H * g.nqt;
     kv_stats_kernel<<<(unsigned)ns, g.threads, 0, s>>>(p);
+    const bool d128 = D == 128;
     switch (mode) {
-      case NVFP4_MODE_FIXED6: kv_quant_kernel<kModeFixed6><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
-      case NVFP4_MODE_FIXED4: kv_quant_kernel<kModeFixed4><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
-      default: kv_quant_kernel<kMode4over6><<<(unsigned)nq, g.threads, 0, s>>>(p); break;
+      case NVFP4_MODE_FIXED6:
+        if (d128) kv_quant_kernel<kModeFixed6, 8><<<(unsigned)nq, g.threads, 0, s>>>(p);
+        else kv_quant_kernel<kModeFixed6, 0><<<(unsigned)nq, g.threads, 0, s>>>(p);
+        break;
+      case NVFP4_MODE_FIXED4:
+        if (d128) kv_quant_kernel<kModeFixed4, 8><<<(unsigned)nq, g.threads, 0, s>>>(p);
+        else kv_quant_kernel<kModeFixed4, 0><<<(unsigned)nq, g.threads, 0, s>>>(p);
+        break;
+      default:
+        if (d128) kv_quant_kernel<kMode4over6, 8><<<(unsigned)nq, g.threads, 0, s>>>(p);
+        else kv_quant_kernel<kMode4over6, 0><<<(unsigned)nq, g.threads, 0, s>>>(p);
+        break;
     }
   }
   if (choice_counts) launch_choice_reduce(p.tally, wl.n_tally, choice_counts, s);

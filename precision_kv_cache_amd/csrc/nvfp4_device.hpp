@@ -61,22 +61,35 @@ __device__ __forceinline__ float recip_e4m3(float S) {
   return S > 0.0f ? r2 : 0.0f;
 }
 
+// (S, fl(1/S)) for every E4M3FN byte 0 .. 127 (R = 0 for S = 0; byte 0x7F,
+// a NaN, is never a candidate).  One LDS read then replaces a candidate's
+// decode and reciprocal.  Filled by the first 128 threads of a workgroup;
+// the caller synchronizes before the first use.
+__device__ __forceinline__ void fill_scale_table(float2* tab) {
+  const int i = threadIdx.x;
+  if (i < 128) {
+    const float S = __builtin_amdgcn_cvt_f32_fp8(i, 0);
+    tab[i] = make_float2(S, recip_e4m3(S));
+  }
+}
+
 // Both candidate scales of a block with largest |z| = t: byte 0 = E4M3(t/6),
 // byte 1 = E4M3(t/4).
 __device__ __forceinline__ uint32_t candidate_codes(float t) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(div6(t), t * 0.25f, 0, false) & 0xffffu;
+  // the conversion writes the low 16 bits and keeps the rest of its first
+  // operand, which is masked off: passing t (dead here) saves zeroing a register
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(div6(t), t * 0.25f, __float_as_int(t), false) & 0xffffu;
 }
 
-template <int SEL>
-__device__ __forceinline__ float e4m3_byte(uint32_t packed) {
-  return __builtin_amdgcn_cvt_f32_fp8((int)packed, SEL);
-}
 
 // Encode 8 values z[0..7] (already in the encode domain) with reciprocal R:
 // one word of 8 E2M1 codes, element 2j in the low nibble of byte j.
 __device__ __forceinline__ uint32_t encode8(const float* z, float R) {
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[0] * R, z[1] * R, 1.0f, 0);
+  // the four conversions write all four bytes of w, so its starting value is
+  // irrelevant: starting from y0 (dead after the first one) saves zeroing it
+  const float y0 = z[0] * R;
+  uint32_t w = __float_as_uint(y0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, z[1] * R, 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[2] * R, z[3] * R, 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[4] * R, z[5] * R, 1.0f, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[6] * R, z[7] * R, 1.0f, 3);
@@ -135,23 +148,24 @@ struct Block46 {
 // Four-Over-Six on one 16-element block in the encode domain: both
 // candidates, each block's fp32 error (two halves added), keep +-4 only when
 // its error is strictly lower.  The fixed modes evaluate one candidate.
+// tab: the scale table of fill_scale_table (in LDS).
 template <int MODE>
-__device__ __forceinline__ Block46 quant_block16(const float (&z)[16]) {
+__device__ __forceinline__ Block46 quant_block16(const float (&z)[16], const float2* tab) {
   const float t = block_absmax(z);
   const uint32_t s = candidate_codes(t);
   Block46 out;
   if (MODE == kModeFixed6) {
-    const float S = e4m3_byte<0>(s);
-    const Encoded16 e = encode16(z, S, recip_e4m3(S));
+    const float2 c = tab[s & 0xffu];
+    const Encoded16 e = encode16(z, c.x, c.y);
     out.lo = e.lo; out.hi = e.hi; out.scale = s & 0xffu; out.use4 = 0;
   } else if (MODE == kModeFixed4) {
-    const float S = e4m3_byte<1>(s);
-    const Encoded16 e = encode16(z, S, recip_e4m3(S));
+    const float2 c = tab[s >> 8];
+    const Encoded16 e = encode16(z, c.x, c.y);
     out.lo = e.lo; out.hi = e.hi; out.scale = s >> 8; out.use4 = 1;
   } else {
-    const float S6 = e4m3_byte<0>(s), S4 = e4m3_byte<1>(s);
-    const Encoded16 e6 = encode16(z, S6, recip_e4m3(S6));
-    const Encoded16 e4 = encode16(z, S4, recip_e4m3(S4));
+    const float2 c6 = tab[s & 0xffu], c4 = tab[s >> 8];
+    const Encoded16 e6 = encode16(z, c6.x, c6.y);
+    const Encoded16 e4 = encode16(z, c4.x, c4.y);
     const float err6 = e6.err_lo + e6.err_hi;
     const float err4 = e4.err_lo + e4.err_hi;
     const bool use4 = err4 < err6;
@@ -195,32 +209,40 @@ __device__ __forceinline__ void store_nt(uint8_t* p, uint32_t lo, uint32_t hi) {
 }
 __device__ __forceinline__ void store_nt(uint8_t* p, uint8_t b) { __builtin_nontemporal_store(b, p); }
 
-// The quantize loop of one lane: rows r, r + step, ... < r_end of a
-// [rows, NB blocks] slab whose first row is row0 (absolute row of the
-// [H, T] row space), column block col.  m: the channel means subtracted
-// first when SMOOTH (the K path), g: the encode scale.  BATCH rows' loads are
-// issued before the first is used.  Returns {blocks kept at +-4, blocks}.
-template <int MODE, bool SMOOTH, bool NT, int BATCH>
+// The quantize loop of one lane: rows r, r + step, ..., r + (BATCH - 1) *
+// step (their loads issued together), then the same BATCH * step rows
+// further on, and so on while below r_end, of a slab of rows of NB blocks
+// whose first row is row0 (absolute row of the [H, T] row space), column
+// block col.  With step = the workgroup's rows per pass, every load and
+// store instruction of a wave covers whole consecutive rows.  One pointer per
+// stream is advanced by a uniform offset per row, with no per-row index
+// arithmetic.  NBC: blocks per row when known at compile time (then nb is
+// ignored), else 0.  m: the channel means subtracted first when SMOOTH (the
+// K path), g: the encode scale, tab: the scale table (LDS).  Returns
+// {blocks kept at +-4, blocks}.
+template <int MODE, bool SMOOTH, bool NT, int BATCH, int NBC>
 __device__ __forceinline__ uint2 quant_rows(const uint16_t* xb, uint8_t* codes, uint8_t* scales, size_t row0,
-                                            int r, int r_end, int step, int NB, int col, const float (&m)[16],
-                                            float g) {
+                                            int r, int r_end, int step, int nb, int col, const float (&m)[16],
+                                            float g, const float2* tab) {
+  const int NB = NBC > 0 ? NBC : nb;
+  const size_t blk = (row0 + r) * NB + col;
+  const uint16_t* px = xb + blk * 16;
+  uint8_t* pc = codes + blk * 8;
+  uint8_t* ps = scales + blk;
+  const size_t dq = (size_t)step * NB;  // blocks from one row of a batch to the next
   unsigned n4 = 0, nblk = 0;
-  for (int rb = r; rb < r_end; rb += BATCH * step) {
+  for (int rb = r; rb < r_end; rb += BATCH * step, px += BATCH * dq * 16, pc += BATCH * dq * 8, ps += BATCH * dq) {
     uint4 a[BATCH], b[BATCH];
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
-      const int rr = rb + q * step;
-      if (rr < r_end) {
-        const size_t blk = (row0 + rr) * NB + col;
-        a[q] = load16<NT>(xb + blk * 16);
-        b[q] = load16<NT>(xb + blk * 16 + 8);
+      if (rb + q * step < r_end) {
+        a[q] = load16<NT>(px + q * dq * 16);
+        b[q] = load16<NT>(px + q * dq * 16 + 8);
       }
     }
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
-      const int rr = rb + q * step;
-      if (rr >= r_end) continue;
-      const size_t blk = (row0 + rr) * NB + col;
+      if (rb + q * step >= r_end) continue;
       float z[16];
       unpack16(a[q], b[q], z);
 #pragma unroll
@@ -228,9 +250,9 @@ __device__ __forceinline__ uint2 quant_rows(const uint16_t* xb, uint8_t* codes, 
         const float xs = SMOOTH ? z[i] - m[i] : z[i];  // k' = fl(K - m)
         z[i] = xs * g;                                  // z = fl(k' * g_enc)
       }
-      const Block46 qb = quant_block16<MODE>(z);
-      store_nt(codes + blk * 8, qb.lo, qb.hi);
-      store_nt(scales + blk, (uint8_t)qb.scale);
+      const Block46 qb = quant_block16<MODE>(z, tab);
+      store_nt(pc + q * dq * 8, qb.lo, qb.hi);
+      store_nt(ps + q * dq, (uint8_t)qb.scale);
       n4 += qb.use4;
       nblk += 1;
     }
