@@ -25,11 +25,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kv_two_pass_full_cache_traffic.md")
+# rocprofv3 HBM-traffic summaries of the KV quantize call, per kernel path
+TRAFFIC_FILES = {"overlap": os.path.join(ROOT, "profiles", "kv_overlap_full_cache_traffic.md"),
+                 "two-pass": os.path.join(ROOT, "profiles", "kv_two_pass_full_cache_traffic.md")}
 
 
 # the sources the KV quantize call's kernels are built from
-KV_KERNEL_SOURCES = ("precision_kv_cache_amd/csrc/kv_quant.hip", "precision_kv_cache_amd/csrc/nvfp4_device.hpp",
+KV_KERNEL_SOURCES = ("precision_kv_cache_amd/csrc/kv_quant.hip", "precision_kv_cache_amd/csrc/kv_overlap.hip",
+                     "precision_kv_cache_amd/csrc/kv_overlap.hpp", "precision_kv_cache_amd/csrc/nvfp4_device.hpp",
                      "precision_kv_cache_amd/csrc/host_common.hpp", "precision_kv_cache_amd/csrc/kv_fused.hpp",
                      "precision_kv_cache_amd/csrc/kv_pipe.hpp", "include/nvfp4kv.h")
 
@@ -44,11 +47,14 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per quantize call from the committed rocprofv3 counter
-    summary, or None once the kernel sources differ from the measured ones."""
+def measured_traffic(path):
+    """HBM bytes per quantize call of a kernel path from the committed
+    rocprofv3 counter summary, or None once the kernel sources differ from the
+    measured ones."""
+    if path not in TRAFFIC_FILES:
+        return None
     try:
-        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_FILES[path]).read().splitlines()
                       if line.startswith(("traffic_bytes_per_call: ", "kernel_sources_sha256: ")))
     except OSError:
         return None
@@ -66,6 +72,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=30, help="cache layers (the workload has 30)")
     ap.add_argument("--mode", type=int, default=0, help="0 = 4/6, 1 = fixed 6, 2 = fixed 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--single-read", action="store_true", help="use the single-read persistent KV kernel")
     ap.add_argument("--pipelined", action="store_true", help="use the persistent pipelined KV kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
@@ -135,7 +142,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream,
-                                   single_read=a.single_read, pipelined=a.pipelined)
+                                   single_read=a.single_read, pipelined=a.pipelined, two_pass=a.two_pass)
         if ev is not None:
             ev[1].record(stream)
 
@@ -204,6 +211,8 @@ def main():
     copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    kv_path = ("single-read" if a.single_read else "pipelined" if a.pipelined else
+               "two-pass" if a.two_pass or D != 128 else "overlap")
     dominant = "quantize" if q_ms >= d_ms else "dequantize"
     ach = q_gbps if dominant == "quantize" else d_gbps
     result = {
@@ -224,7 +233,7 @@ def main():
                         "chunks of 7040 tokens; 4/6 smooth-quantize every layer, then dequantize the cache",
             "layers": nlayers, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
             "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": step_bytes,
-            "kv_path": "single-read" if a.single_read else ("pipelined" if a.pipelined else "two-pass"),
+            "kv_path": kv_path,
         },
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "quantize_GBps": round(q_gbps, 1),
@@ -242,7 +251,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic() if dominant == "quantize" and not (a.single_read or a.pipelined) else None,
+            "traffic": measured_traffic(kv_path) if dominant == "quantize" else None,
             "bytes_per_launch": qbytes_layer,
         },
         "input_generation_s": round(gen_s, 2),

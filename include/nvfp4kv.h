@@ -81,18 +81,24 @@ typedef enum {
   NVFP4_MODE_FIXED4 = 2  /* +-4 only, C = 1792                               */
 } nvfp4_mode;
 
-/* Option bit for nvfp4_kv_smooth_quantize's mode: use the single-read
- * persistent kernel (each K and V element read from HBM once; workgroups
- * synchronize through the workspace) instead of the default two-pass kernels
- * (a statistics pass, then a quantize pass that reads K and V again).  Same
- * results.  It applies when D == 128 and the device supports a cooperative
- * launch of the kernel's resident grid; otherwise the call silently takes the
- * two-pass kernels. */
+/* Kernels of nvfp4_kv_smooth_quantize.  By default, for D == 128, one
+ * launch whose grid interleaves the statistics tiles of each (chunk, tensor)
+ * unit with the quantize tiles of an earlier unit; the quantize tiles re-read
+ * their rows from the Infinity Cache, so K and V are read from HBM about
+ * once.  Other shapes, or the option bit below, take the two-pass kernels (a
+ * statistics pass, then a quantize pass that reads K and V again).  Both give
+ * the same results. */
+#define NVFP4_KV_TWO_PASS 0x100
+
+/* Option bit: the single-read persistent kernel (each K and V element read
+ * from HBM once; workgroups synchronize through the workspace).  It applies
+ * when D == 128 and the device supports a cooperative launch of the kernel's
+ * resident grid; otherwise the call takes the default kernels. */
 #define NVFP4_KV_SINGLE_READ 0x200
 
-/* Option bit: the pipelined two-pass form (one launch per (chunk, tensor)
- * unit; statistics of unit u overlap the quantization of unit u - 1, which
- * re-reads its input from the Infinity Cache).  Same results. */
+/* Option bit: the persistent pipelined form (statistics of unit u overlap
+ * the quantization of unit u - 1, which re-reads its input from the
+ * Infinity Cache; one cooperative launch).  Same results. */
 #define NVFP4_KV_PIPELINED 0x400
 
 /* Largest supported head dimension / row length for the KV entry points. */
@@ -113,7 +119,7 @@ NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) 
  *   H, T, D       heads, tokens, head dimension (D % 16 == 0, D <= 4096).
  *   chunk_len     T_c, tokens per chunk; each chunk gets its own K mean and
  *                 its own tensor scales.
- *   mode          nvfp4_mode, optionally | NVFP4_KV_SINGLE_READ.
+ *   mode          nvfp4_mode, optionally | one NVFP4_KV_* option bit.
  *   k_codes, v_codes     out, uint8 [H, T, D/2], 8-byte aligned.
  *   k_scales, v_scales   out, E4M3FN bytes [H, T, D/16].
  *   k_tensor_scale, v_tensor_scale  out, fp32 [n_chunks], g_dec per chunk.

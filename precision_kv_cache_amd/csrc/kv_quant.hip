@@ -33,6 +33,7 @@
 
 #include "host_common.hpp"
 #include "kv_fused.hpp"
+#include "kv_overlap.hpp"
 #include "kv_pipe.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4kv.h"
@@ -482,8 +483,10 @@ extern "C" NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int 
   const size_t two_pass = kv_workspace_layout(kv_geom(H, T, D, chunk_len)).total;
   const size_t fused = fused_workspace_bound(H, T, D, chunk_len);
   const size_t pipe = pipe_workspace_bound(H, T, D, chunk_len);
-  const size_t m = two_pass > fused ? two_pass : fused;
-  return m > pipe ? m : pipe;
+  const size_t ov = overlap_workspace_bound(H, T, D, chunk_len);
+  size_t m = two_pass > fused ? two_pass : fused;
+  m = m > pipe ? m : pipe;
+  return m > ov ? m : ov;
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
@@ -495,7 +498,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   if (!kv_shape_ok(H, T, D, chunk_len)) return NVFP4_ERR_SHAPE;
   const bool single_read = (mode & NVFP4_KV_SINGLE_READ) != 0;
   const bool pipelined = (mode & NVFP4_KV_PIPELINED) != 0;
-  mode &= ~(NVFP4_KV_SINGLE_READ | NVFP4_KV_PIPELINED);
+  const bool two_pass = (mode & NVFP4_KV_TWO_PASS) != 0;
+  mode &= ~(NVFP4_KV_SINGLE_READ | NVFP4_KV_PIPELINED | NVFP4_KV_TWO_PASS);
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
   if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
@@ -518,6 +522,17 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();  // start from a clean error state
+  if (!two_pass && !single_read && !pipelined && D == 128) {
+    OverlapParams q;
+    q.x[0] = k; q.x[1] = v;
+    q.codes[0] = k_codes; q.codes[1] = v_codes;
+    q.scales[0] = k_scales; q.scales[1] = v_scales;
+    q.tscale[0] = k_tensor_scale; q.tscale[1] = v_tensor_scale;
+    q.kmean = k_mean;
+    q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
+    const int rc = overlap_try_launch(q, mode, workspace, workspace_bytes, choice_counts, s);
+    if (rc <= 0) return rc;  // enqueued, or a launch error
+  }
   if (pipelined) {
     PipeParams q;
     q.x[0] = k; q.x[1] = v;

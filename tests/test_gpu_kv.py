@@ -18,8 +18,8 @@ def _lib_loaded():
     P.lib()  # raises if the HIP library is missing
 
 
-PATHS = [{}, {"single_read": True}, {"pipelined": True}]  # keyword options of the binding
-PATH_IDS = ["two-pass", "single-read", "pipelined"]
+PATHS = [{}, {"two_pass": True}, {"single_read": True}, {"pipelined": True}]  # keyword options of the binding
+PATH_IDS = ["overlap", "two-pass", "single-read", "pipelined"]
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -118,12 +118,13 @@ def test_full_cache_layer_sampled(layer, path):
     (600, 32, 128, 32),  # more heads than resident workgroups: two-pass kernels
     (1, 204800, 128, 204800),  # one head, more rows than the single-read kernel holds
 ])
-def test_ragged_and_odd_shapes(H, T, D, L):
-    say("shape", (H, T, D, L))
+@pytest.mark.parametrize("path", [{}, {"two_pass": True}], ids=["overlap", "two-pass"])
+def test_ragged_and_odd_shapes(H, T, D, L, path):
+    say("shape", (H, T, D, L), "path", path)
     shape = W.KVShape(H, T, D, L)
     k, v = W.gaussian_kv(shape, 4242 + H * T + D)
     kb, vb = W.bf16_bits(k), W.bf16_bits(v)
-    res, dev = gpu_kv(kb, vb, L)
+    res, dev = gpu_kv(kb, vb, L, path=path)
     check_kv(kb, vb, L, O.MODE_4OVER6, res, dev)
     if L == 1:
         assert not res["k_codes"].any() and not res["k_scales"].any() and not res["k_tensor_scale"].any()
@@ -165,13 +166,18 @@ def test_deterministic_and_stream_ordered():
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
         b = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, single_read=True,
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
-        c = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True,
+        c = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, two_pass=True,
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
         d = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, pipelined=True,
+                                       out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        e = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True,
+                                       out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+        f = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True,
                                        out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
     side.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+        assert torch.equal(e[key], f[key]), key
         assert torch.equal(c[key], d[key]), key  # same statistics tiles, same reduction order
         if key != "k_mean":  # the single-read kernel combines the fp64 channel sums in another order
             assert torch.equal(a[key], c[key]), key
