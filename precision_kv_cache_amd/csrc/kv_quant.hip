@@ -401,7 +401,12 @@ void launch_choice_reduce(const uint32_t* tally, size_t nslots, unsigned long lo
 
 // Two lanes per 16-element block (each lane one 8-element half), so every
 // 16-byte bf16 store of a wave lands in one contiguous 1 KB run.  Thread t
-// owns half-column t % HB (HB = 2 * D/16 halves per row) for all its rows.
+// owns half-column t % HB (HB = 2 * D/16 halves per row) for kDeqRows rows,
+// RP rows apart; it issues all of their code and scale loads before the
+// first store, so each lane keeps kDeqRows loads in flight.  The bf16 output
+// is streamed out with non-temporal stores: nothing here reads it again.
+constexpr int kDeqRows = 4;
+
 struct DeqParams {
   const uint8_t* codes;
   const uint8_t* scales;
@@ -420,16 +425,19 @@ static DeqGeom deq_geom(int D, int L) {
   g.HB = D / 8;
   g.RP = g.HB >= kMaxThreads ? 1 : kMaxThreads / g.HB;
   g.threads = (g.HB * g.RP + 63) / 64 * 64;
-  g.rows_q = g.RP * kQuantPasses * 2;
+  g.rows_q = g.RP * kDeqRows;
   g.nqt = (L + g.rows_q - 1) / g.rows_q;
   return g;
 }
 
-template <bool MEAN>
+// HBC: halves per row fixed at compile time (16 for D = 128), or 0.
+template <bool MEAN, int HBC>
 __global__ __launch_bounds__(512) void dequant_kernel(DeqParams p) {
+  const int HB = HBC > 0 ? HBC : p.HB;
+  const int RP = HBC > 0 ? kMaxThreads / HBC : p.RP;
   const int qt = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
-  const int tid = threadIdx.x, hc = tid % p.HB, roff = tid / p.HB;
-  if (roff >= p.RP) return;
+  const int tid = threadIdx.x, hc = tid % HB, roff = tid / HB;
+  if (roff >= RP) return;
   float m[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) m[i] = 0.0f;
@@ -439,17 +447,29 @@ __global__ __launch_bounds__(512) void dequant_kernel(DeqParams p) {
     m[0] = a.x; m[1] = a.y; m[2] = a.z; m[3] = a.w; m[4] = b.x; m[5] = b.y; m[6] = b.z; m[7] = b.w;
   }
   const float g = p.tscale[c];
-  const int r0 = qt * p.rows_q;
-  const int r1 = min(r0 + p.rows_q, p.L);
-  const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
-  for (int r = r0 + roff; r < r1; r += p.RP) {
-    const size_t half = (row0 + r) * p.HB + hc;  // index of this 8-element half
-    const uint32_t q = *reinterpret_cast<const uint32_t*>(p.codes + half * 4);
-    const float S = __builtin_amdgcn_cvt_f32_fp8((int)p.scales[half >> 1], 0);
-    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
-    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
-    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
-    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+  const int r = qt * RP * kDeqRows + roff;  // this lane's first row of the chunk
+  const int r1 = min((qt + 1) * RP * kDeqRows, p.L);
+  const size_t half = ((size_t)h * p.T + (size_t)c * p.L + r) * HB + hc;  // index of this lane's first half
+  const uint32_t* cp = reinterpret_cast<const uint32_t*>(p.codes) + half;
+  const uint8_t* sp = p.scales + (half >> 1);
+  uint16_t* op = p.out + half * 8;
+  const size_t step = (size_t)RP * HB;  // halves from one of the lane's rows to the next
+  uint32_t q[kDeqRows], sb[kDeqRows];
+#pragma unroll
+  for (int k = 0; k < kDeqRows; ++k) {
+    if (r + k * RP < r1) {
+      q[k] = cp[k * step];
+      sb[k] = sp[k * (step >> 1)];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDeqRows; ++k) {
+    if (r + k * RP >= r1) break;
+    const float S = __builtin_amdgcn_cvt_f32_fp8((int)sb[k], 0);
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[k], 1.0f, 0);
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[k], 1.0f, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[k], 1.0f, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[k], 1.0f, 3);
     const float v[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
     uint32_t w[4];
 #pragma unroll
@@ -458,7 +478,8 @@ __global__ __launch_bounds__(512) void dequant_kernel(DeqParams p) {
       if (MEAN) { a = a + m[2 * j]; b = b + m[2 * j + 1]; }
       w[j] = pack_bf16x2(a, b);
     }
-    *reinterpret_cast<uint4*>(p.out + half * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    const u32x4 ov = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(op + k * step * 8));
   }
 }
 
@@ -628,9 +649,12 @@ extern "C" NVFP4KV_API int nvfp4_dequantize(const uint8_t* codes, const uint8_t*
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   const dim3 grid(dg.nqt, H, g.nc);
-  if (mean)
-    dequant_kernel<true><<<grid, dg.threads, 0, s>>>(p);
-  else
-    dequant_kernel<false><<<grid, dg.threads, 0, s>>>(p);
+  if (D == 128) {
+    if (mean) dequant_kernel<true, 16><<<grid, dg.threads, 0, s>>>(p);
+    else dequant_kernel<false, 16><<<grid, dg.threads, 0, s>>>(p);
+  } else {
+    if (mean) dequant_kernel<true, 0><<<grid, dg.threads, 0, s>>>(p);
+    else dequant_kernel<false, 0><<<grid, dg.threads, 0, s>>>(p);
+  }
   return launch_status();
 }
