@@ -33,8 +33,7 @@ TRAFFIC_FILES = {"overlap": os.path.join(ROOT, "profiles", "kv_overlap_full_cach
 # the sources the KV quantize call's kernels are built from
 KV_KERNEL_SOURCES = ("precision_kv_cache_amd/csrc/kv_quant.hip", "precision_kv_cache_amd/csrc/kv_overlap.hip",
                      "precision_kv_cache_amd/csrc/kv_overlap.hpp", "precision_kv_cache_amd/csrc/nvfp4_device.hpp",
-                     "precision_kv_cache_amd/csrc/host_common.hpp", "precision_kv_cache_amd/csrc/kv_fused.hpp",
-                     "precision_kv_cache_amd/csrc/kv_pipe.hpp", "include/nvfp4kv.h")
+                     "precision_kv_cache_amd/csrc/host_common.hpp", "include/nvfp4kv.h")
 
 
 def kernel_sources_sha256():
@@ -73,8 +72,6 @@ def parse():
     ap.add_argument("--mode", type=int, default=0, help="0 = 4/6, 1 = fixed 6, 2 = fixed 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
-    ap.add_argument("--single-read", action="store_true", help="use the single-read persistent KV kernel")
-    ap.add_argument("--pipelined", action="store_true", help="use the persistent pipelined KV kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
     return ap.parse_args()
 
@@ -142,7 +139,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream,
-                                   single_read=a.single_read, pipelined=a.pipelined, two_pass=a.two_pass)
+                                   two_pass=a.two_pass)
         if ev is not None:
             ev[1].record(stream)
 
@@ -211,8 +208,7 @@ def main():
     copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    kv_path = ("single-read" if a.single_read else "pipelined" if a.pipelined else
-               "two-pass" if a.two_pass or D != 128 else "overlap")
+    kv_path = "two-pass" if a.two_pass or D != 128 else "overlap"
     dominant = "quantize" if q_ms >= d_ms else "dequantize"
     ach = q_gbps if dominant == "quantize" else d_gbps
     result = {

@@ -90,17 +90,6 @@ typedef enum {
  * the same results. */
 #define NVFP4_KV_TWO_PASS 0x100
 
-/* Option bit: the single-read persistent kernel (each K and V element read
- * from HBM once; workgroups synchronize through the workspace).  It applies
- * when D == 128 and the device supports a cooperative launch of the kernel's
- * resident grid; otherwise the call takes the default kernels. */
-#define NVFP4_KV_SINGLE_READ 0x200
-
-/* Option bit: the persistent pipelined form (statistics of unit u overlap
- * the quantization of unit u - 1, which re-reads its input from the
- * Infinity Cache; one cooperative launch).  Same results. */
-#define NVFP4_KV_PIPELINED 0x400
-
 /* Largest supported head dimension / row length for the KV entry points. */
 #define NVFP4_KV_MAX_D 4096
 
@@ -119,7 +108,7 @@ NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) 
  *   H, T, D       heads, tokens, head dimension (D % 16 == 0, D <= 4096).
  *   chunk_len     T_c, tokens per chunk; each chunk gets its own K mean and
  *                 its own tensor scales.
- *   mode          nvfp4_mode, optionally | one NVFP4_KV_* option bit.
+ *   mode          nvfp4_mode, optionally | NVFP4_KV_TWO_PASS.
  *   k_codes, v_codes     out, uint8 [H, T, D/2], 8-byte aligned.
  *   k_scales, v_scales   out, E4M3FN bytes [H, T, D/16].
  *   k_tensor_scale, v_tensor_scale  out, fp32 [n_chunks], g_dec per chunk.
@@ -132,10 +121,10 @@ NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) 
  *                 256-byte aligned; contents on entry are ignored.  Calls
  *                 that share a workspace must be ordered on one stream.
  *
- * The single-read kernel keeps every workgroup resident (cooperative launch)
- * and synchronizes them through flags in the workspace; each wait is bounded,
- * and if one ever times out the kernel stops early and leaves the results
- * invalid (the workspace's error word is then non-zero).
+ * The overlapped kernel's quantize tiles wait, through words in the
+ * workspace, for statistics tiles that precede them in the grid; each wait
+ * is bounded, and if one ever timed out the tile would stop early and leave
+ * its results invalid (the workspace's error word is then non-zero).
  *
  * Smoothing: k' = fl(K - mean) in fp32.  V is quantized as is.
  */

@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = [
-    "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "KV_SINGLE_READ", "KV_PIPELINED", "Nvfp4Error", "lib", "nvfp4_status_string",
+    "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
@@ -91,13 +91,11 @@ def nvfp4_kv_workspace_bytes(H, T, D, chunk_len):
     return int(lib().nvfp4_kv_workspace_bytes(H, T, D, chunk_len))
 
 
-KV_SINGLE_READ = 0x200
-KV_PIPELINED = 0x400
 KV_TWO_PASS = 0x100
 
 
 def nvfp4_kv_smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, choice_counts=False, out=None, workspace=None,
-                             stream=None, single_read=False, pipelined=False, two_pass=False):
+                             stream=None, two_pass=False):
     """K smoothing + 4/6 NVFP4 quantization of K, V bf16 [H, T, D].
 
     Returns a dict with k_codes, v_codes [H, T, D/2] uint8, k_scales, v_scales
@@ -107,9 +105,7 @@ def nvfp4_kv_smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, choice_counts=Fa
     (and ``workspace`` a uint8 device buffer) to avoid allocation.
     By default (D == 128) one overlapped launch interleaves each unit's
     statistics with the quantization of an earlier unit; ``two_pass`` forces
-    the statistics-then-quantize kernels, ``single_read`` the single-read
-    persistent kernel and ``pipelined`` the persistent pipelined kernel (same
-    results).
+    the statistics-then-quantize kernels (same results).
     """
     _bf16_dev(k, "k"); _bf16_dev(v, "v")
     if k.shape != v.shape or k.dim() != 3:
@@ -133,7 +129,7 @@ def nvfp4_kv_smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, choice_counts=Fa
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     rc = lib().nvfp4_kv_smooth_quantize(
-        _ptr(k), _ptr(v), H, T, D, chunk_len, mode | (KV_SINGLE_READ if single_read else 0) | (KV_PIPELINED if pipelined else 0) | (KV_TWO_PASS if two_pass else 0), _ptr(out["k_codes"]), _ptr(out["v_codes"]),
+        _ptr(k), _ptr(v), H, T, D, chunk_len, mode | (KV_TWO_PASS if two_pass else 0), _ptr(out["k_codes"]), _ptr(out["v_codes"]),
         _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
         _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream))

@@ -32,9 +32,7 @@
 #include <stdint.h>
 
 #include "host_common.hpp"
-#include "kv_fused.hpp"
 #include "kv_overlap.hpp"
-#include "kv_pipe.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4kv.h"
 
@@ -502,12 +500,8 @@ static bool kv_shape_ok(int H, int T, int D, int L) {
 extern "C" NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len) || H == 0 || T == 0) return 0;
   const size_t two_pass = kv_workspace_layout(kv_geom(H, T, D, chunk_len)).total;
-  const size_t fused = fused_workspace_bound(H, T, D, chunk_len);
-  const size_t pipe = pipe_workspace_bound(H, T, D, chunk_len);
   const size_t ov = overlap_workspace_bound(H, T, D, chunk_len);
-  size_t m = two_pass > fused ? two_pass : fused;
-  m = m > pipe ? m : pipe;
-  return m > ov ? m : ov;
+  return two_pass > ov ? two_pass : ov;
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
@@ -517,10 +511,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
                                                     unsigned long long* choice_counts, void* workspace,
                                                     size_t workspace_bytes, void* stream) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len)) return NVFP4_ERR_SHAPE;
-  const bool single_read = (mode & NVFP4_KV_SINGLE_READ) != 0;
-  const bool pipelined = (mode & NVFP4_KV_PIPELINED) != 0;
   const bool two_pass = (mode & NVFP4_KV_TWO_PASS) != 0;
-  mode &= ~(NVFP4_KV_SINGLE_READ | NVFP4_KV_PIPELINED | NVFP4_KV_TWO_PASS);
+  mode &= ~NVFP4_KV_TWO_PASS;
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
   if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
@@ -543,7 +535,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();  // start from a clean error state
-  if (!two_pass && !single_read && !pipelined && D == 128) {
+  if (!two_pass && D == 128) {
     OverlapParams q;
     q.x[0] = k; q.x[1] = v;
     q.codes[0] = k_codes; q.codes[1] = v_codes;
@@ -552,31 +544,6 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
     q.kmean = k_mean;
     q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
     const int rc = overlap_try_launch(q, mode, workspace, workspace_bytes, choice_counts, s);
-    if (rc <= 0) return rc;  // enqueued, or a launch error
-  }
-  if (pipelined) {
-    PipeParams q;
-    q.x[0] = k; q.x[1] = v;
-    q.codes[0] = k_codes; q.codes[1] = v_codes;
-    q.scales[0] = k_scales; q.scales[1] = v_scales;
-    q.tscale[0] = k_tensor_scale; q.tscale[1] = v_tensor_scale;
-    q.kmean = k_mean;
-    q.mode = mode;
-    q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
-    const int rc = pipe_try_launch(q, workspace, workspace_bytes, choice_counts, s);
-    if (rc <= 0) return rc;  // enqueued, or a launch error
-  }
-  if (single_read) {
-    FusedParams f;
-    f.x[0] = k; f.x[1] = v;
-    f.codes[0] = k_codes; f.codes[1] = v_codes;
-    f.scales[0] = k_scales; f.scales[1] = v_scales;
-    f.tscale[0] = k_tensor_scale; f.tscale[1] = v_tensor_scale;
-    f.kmean = k_mean;
-    f.choice = choice_counts;
-    f.H = H; f.T = T; f.D = D; f.L = chunk_len; f.nc = g.nc;
-    f.spin_limit = kFusedSpinLimit;
-    const int rc = fused_try_launch(f, mode, workspace, workspace_bytes, s);
     if (rc <= 0) return rc;  // enqueued, or a launch error
   }
   KVParams p;

@@ -278,9 +278,6 @@ __device__ __forceinline__ unsigned add_agent(unsigned* p, unsigned v) {
 __device__ __forceinline__ unsigned load_agent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_agent(unsigned* p, unsigned v) {
-  (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // publish: exchange, and fold the returned old value into `done` so the
 // caller can make the exchange's completion explicit (see wait_published)
 __device__ __forceinline__ void publish(float* p, float v, uint32_t& done) {
