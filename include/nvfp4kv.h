@@ -100,6 +100,14 @@ NVFP4KV_API const char* nvfp4_status_string(int status) NVFP4KV_NOEXCEPT;
  * invalid shape).  Host function, no HIP call. */
 NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) NVFP4KV_NOEXCEPT;
 
+/* Byte offset, inside the workspace of nvfp4_kv_smooth_quantize, of the
+ * 32-bit error word of the default (overlapped) kernel for this shape, or -1
+ * when the shape takes the two-pass kernels (which never wait).  Each call
+ * clears the word; once the call has completed (the stream synchronized), a
+ * non-zero value there means one of the kernel's bounded waits timed out and
+ * the call's outputs are invalid.  Host function, no HIP call. */
+NVFP4KV_API long long nvfp4_kv_error_word_offset(int H, int T, int D, int chunk_len) NVFP4KV_NOEXCEPT;
+
 /*
  * K smoothing + 4/6 NVFP4 quantization of one layer's K and V
  * (inference pipeline, step 7; full-stack NVFP4).

@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
-    "nvfp4_kv_workspace_bytes", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
+    "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
@@ -43,6 +43,7 @@ def lib():
         sig = {
             "nvfp4_status_string": (ctypes.c_char_p, [i]),
             "nvfp4_kv_workspace_bytes": (sz, [i, i, i, i]),
+            "nvfp4_kv_error_word_offset": (ll, [i, i, i, i]),
             "nvfp4_kv_smooth_quantize": (i, [P, P, i, i, i, i, i, P, P, P, P, P, P, P, P, P, sz, P]),
             "nvfp4_dequantize": (i, [P, P, P, P, i, i, i, i, P, P]),
             "nvfp4_quantize_1d_workspace_bytes": (sz, [i, i]),
@@ -89,6 +90,12 @@ def _bf16_dev(t, name):
 
 def nvfp4_kv_workspace_bytes(H, T, D, chunk_len):
     return int(lib().nvfp4_kv_workspace_bytes(H, T, D, chunk_len))
+
+
+def nvfp4_kv_error_word_offset(H, T, D, chunk_len):
+    """Byte offset of the overlapped kernel's error word in the workspace, or
+    -1 for shapes that take the two-pass kernels."""
+    return int(lib().nvfp4_kv_error_word_offset(H, T, D, chunk_len))
 
 
 KV_TWO_PASS = 0x100

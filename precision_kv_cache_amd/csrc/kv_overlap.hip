@@ -458,6 +458,17 @@ size_t overlap_workspace_bound(int H, int T, int D, int L) {
   return overlap_layout(H, T / L, nst, nqt).total;
 }
 
+long long overlap_error_offset(int H, int T, int D, int L) {
+  if (D != kD || H <= 0 || L <= 0 || T <= 0 || T % L != 0) return -1;
+  const int nc = T / L;
+  const int nst = (L + kOvStatsRows - 1) / kOvStatsRows;
+  const int nqt = (L + kOvQuantRows - 1) / kOvQuantRows;
+  const long long grid = 2LL * nc * H * ((long long)nst + nqt);
+  if (grid >= (1LL << 24) || (long long)L * kD * 2 >= (1LL << 31)) return -1;  // as overlap_try_launch
+  const OverlapLayout l = overlap_layout(H, nc, nst, nqt);
+  return (long long)(l.counters + ((size_t)2 * nc * H + 2 * nc) * sizeof(unsigned));
+}
+
 __global__ void overlap_zero_kernel(unsigned* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;

@@ -43,6 +43,8 @@ struct OverlapLayout {
 
 OverlapLayout overlap_layout(int H, int nc, int nst, int nqt);
 size_t overlap_workspace_bound(int H, int T, int D, int L);
+// byte offset of the error word in the workspace, -1 when the form does not apply
+long long overlap_error_offset(int H, int T, int D, int L);
 // NVFP4_OK after enqueueing (and the choice-count reduction when choice is
 // set), a positive value when this form does not apply to the shape, or
 // NVFP4_ERR_HIP.

@@ -504,6 +504,11 @@ extern "C" NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int 
   return two_pass > ov ? two_pass : ov;
 }
 
+extern "C" NVFP4KV_API long long nvfp4_kv_error_word_offset(int H, int T, int D, int chunk_len) noexcept {
+  if (!kv_shape_ok(H, T, D, chunk_len) || H == 0 || T == 0) return -1;
+  return overlap_error_offset(H, T, D, chunk_len);
+}
+
 extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
                                                     int chunk_len, int mode, uint8_t* k_codes, uint8_t* v_codes,
                                                     uint8_t* k_scales, uint8_t* v_scales, float* k_tensor_scale,

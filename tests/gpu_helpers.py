@@ -45,13 +45,20 @@ def kv_outputs(H, T, D, L, counts=True):
 
 
 def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True, path=None):
-    """K, V given as numpy bf16 bits [H, T, D] -> GPU outputs as numpy."""
+    """K, V given as numpy bf16 bits [H, T, D] -> GPU outputs as numpy.  The
+    workspace starts out filled with garbage (its contents on entry are
+    documented as ignored); after the call the overlapped kernel's error word
+    must read zero (no wait timed out)."""
     k = W.from_bits(kb, "cuda")
     v = W.from_bits(vb, "cuda")
     H, T, D = kb.shape
+    ws = torch.full((max(1, P.nvfp4_kv_workspace_bytes(H, T, D, L)),), 0xA5, dtype=torch.uint8, device="cuda")
     out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts, **(path or {}),
-                                     out=kv_outputs(H, T, D, L, counts))
+                                     out=kv_outputs(H, T, D, L, counts), workspace=ws)
     torch.cuda.synchronize()
+    off = P.nvfp4_kv_error_word_offset(H, T, D, L)
+    if off >= 0 and not (path or {}).get("two_pass"):
+        assert int(ws[off:off + 4].cpu().view(torch.int32)[0]) == 0, "a wait of the overlapped kernel timed out"
     return {key: t.cpu().numpy() for key, t in out.items()}, out
 
 

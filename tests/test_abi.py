@@ -51,6 +51,12 @@ def test_workspace_sizes():
     assert P.nvfp4_kv_workspace_bytes(24, 56320, 128, 7040) > P.nvfp4_kv_workspace_bytes(24, 7040, 128, 7040)
     for bad in ((24, 7040, 100, 7040), (24, 7041, 128, 7040), (-1, 10, 16, 10), (1, 16, 8192, 16), (1, 16, 16, 0)):
         assert P.nvfp4_kv_workspace_bytes(*bad) == 0, bad
+    # the error word lies inside the workspace; shapes without the overlapped kernel have none
+    for shape in ((24, 7040, 128, 7040), (24, 56320, 128, 7040), (1, 256, 128, 256), (3, 77, 128, 7)):
+        off = P.nvfp4_kv_error_word_offset(*shape)
+        assert 0 <= off and off + 4 <= P.nvfp4_kv_workspace_bytes(*shape) and off % 4 == 0, shape
+    assert P.nvfp4_kv_error_word_offset(2, 96, 48, 32) == -1      # D != 128: two-pass kernels
+    assert P.nvfp4_kv_error_word_offset(24, 7041, 128, 7040) == -1  # invalid shape
     assert P.lib().nvfp4_quantize_1d_workspace_bytes(16, 48) > 0
     assert P.lib().nvfp4_quantize_2d_workspace_bytes(24, 48) == 0  # rows % 16
 

@@ -74,11 +74,15 @@ def test_full_cache_layer_sampled(layer, path):
     s = W.CACHE_LAYER
     say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "path", path)
     k, v = W.gaussian_kv(s, W.cache_layer_seed(layer), device="cuda")
+    ws = torch.full((P.nvfp4_kv_workspace_bytes(s.H, s.T, s.D, s.chunk_len),), 0xA5, dtype=torch.uint8, device="cuda")
     out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, **path,
-                                     out=kv_outputs(s.H, s.T, s.D, s.chunk_len))
+                                     out=kv_outputs(s.H, s.T, s.D, s.chunk_len), workspace=ws)
     dk = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len)
     dv = P.nvfp4_dequantize(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, s.chunk_len)
     torch.cuda.synchronize()
+    if not path.get("two_pass"):
+        off = P.nvfp4_kv_error_word_offset(s.H, s.T, s.D, s.chunk_len)
+        assert int(ws[off:off + 4].cpu().view(torch.int32)[0]) == 0, "a wait of the overlapped kernel timed out"
     L = s.chunk_len
     for c in (0, 3, 7):
         say("  chunk", c)
