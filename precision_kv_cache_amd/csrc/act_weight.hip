@@ -22,15 +22,26 @@ constexpr int kAmaxMaxWG = 2048;  // workgroups of the amax pass (grid-stride)
 // workspace: [0, 256) the tensor maximum's bits; [256, ...) partial maxima
 constexpr size_t kAWWorkspace = 256 + (size_t)kAmaxMaxWG * sizeof(float);
 
-// 16-point random-sign Hadamard transform of one block, in place:
-// u = s * x (exact sign flips), fast Walsh-Hadamard butterflies with strides
-// 1, 2, 4, 8 turning (a, b) into (a + b, a - b), then times 1/4 (exact).
-// flip[j] is 0x80000000 where bit j of the sign mask is set.
-__device__ __forceinline__ void rht16(float (&u)[16], const uint32_t (&flip)[16]) {
+// 16-point random-sign Hadamard transform of one block, in place, without
+// its final factor 1/4: w = H16 (s * x).  The sign flips ride on the first
+// butterfly stage: with t = s_i x_i (exact), the pair (i, i + 1) becomes
+// (fl(t + s_{i+1} x_{i+1}), fl(t - s_{i+1} x_{i+1})), each one fused
+// multiply-add whose product is exact, so the rounding is that of the plain
+// sum and difference; strides 2, 4, 8 then turn (a, b) into (a + b, a - b).
+// The callers apply the 1/4 where it is exact and free: u = w / 4 exactly
+// (w is a multiple of 2^-133, so w / 4 cannot underflow), hence
+// max|u| = max|w| / 4 and fl(u * g) = fl(w * (g / 4)) with g / 4 exact.
+// sgn[j] is -1 where bit j of the sign mask is set, else +1.
+__device__ __forceinline__ void rht16_unscaled(float (&u)[16], const float (&sgn)[16]) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) u[j] = __uint_as_float(__float_as_uint(u[j]) ^ flip[j]);
+  for (int i = 0; i < 16; i += 2) {
+    const float t = u[i] * sgn[i];
+    const float b = u[i + 1];
+    u[i] = __builtin_fmaf(b, sgn[i + 1], t);
+    u[i + 1] = __builtin_fmaf(b, -sgn[i + 1], t);
+  }
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = 2; h < 16; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i & h) continue;
@@ -39,32 +50,45 @@ __device__ __forceinline__ void rht16(float (&u)[16], const uint32_t (&flip)[16]
       u[i + h] = a - b;
     }
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) u[j] = u[j] * 0.25f;
 }
 
-__device__ __forceinline__ void sign_flips(uint32_t mask, uint32_t (&flip)[16]) {
+__device__ __forceinline__ void sign_factors(uint32_t mask, float (&sgn)[16]) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) flip[j] = ((mask >> j) & 1u) << 31;
+  for (int j = 0; j < 16; ++j) sgn[j] = ((mask >> j) & 1u) ? -1.0f : 1.0f;
 }
+
+constexpr int kAmaxUnroll = 4;  // segments whose loads a lane issues together
 
 // Largest |value| over nseg 16-element segments (optionally rotated).
+// Each lane takes segments f, f + G, f + 2G, f + 3G (G = the grid's lanes)
+// per step, their loads issued together.
 template <bool RHT>
 __global__ __launch_bounds__(kAWThreads) void amax16_kernel(const uint16_t* x, long long nseg, uint32_t sign_mask,
                                                             float* partial) {
   __shared__ float shw[kAWThreads / 64];
-  uint32_t flip[16];
-  sign_flips(sign_mask, flip);
+  float sgn[16];
+  sign_factors(sign_mask, sgn);
   float am = 0.0f;
-  for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nseg;
-       f += (long long)gridDim.x * blockDim.x) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + f * 16);
-    const uint4 a = src[0], b = src[1];
-    float u[16];
-    unpack16(a, b, u);
-    if (RHT) rht16(u, flip);
+  const long long G = (long long)gridDim.x * blockDim.x;
+  for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nseg; f += kAmaxUnroll * G) {
+    uint4 a[kAmaxUnroll], b[kAmaxUnroll];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
+    for (int q = 0; q < kAmaxUnroll; ++q) {
+      if (f + q * G < nseg) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + (f + q * G) * 16);
+        a[q] = src[0];
+        b[q] = src[1];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kAmaxUnroll; ++q) {
+      if (f + q * G >= nseg) continue;
+      float u[16];
+      unpack16(a[q], b[q], u);
+      if (RHT) rht16_unscaled(u, sgn);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
+    }
   }
   am = wave_max(am);
   if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = am;
@@ -72,7 +96,7 @@ __global__ __launch_bounds__(kAWThreads) void amax16_kernel(const uint16_t* x, l
   if (threadIdx.x == 0) {
     float m = 0.0f;
     for (int w = 0; w < (int)(blockDim.x / 64); ++w) m = fmaxf(m, shw[w]);
-    partial[blockIdx.x] = m;
+    partial[blockIdx.x] = RHT ? m * 0.25f : m;  // the rotation's 1/4, exact
   }
 }
 
@@ -103,17 +127,18 @@ __global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, 
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = A / C;
-  uint32_t flip[16];
-  sign_flips(sign_mask, flip);
+  const float gz = RHT ? g * 0.25f : g;  // the rotation's 1/4 folded into the scale (exact)
+  float sgn[16];
+  sign_factors(sign_mask, sgn);
   for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nblk;
        f += (long long)gridDim.x * blockDim.x) {
     const uint4* src = reinterpret_cast<const uint4*>(x + f * 16);
     const uint4 a = src[0], b = src[1];
     float z[16];
     unpack16(a, b, z);
-    if (RHT) rht16(z, flip);
+    if (RHT) rht16_unscaled(z, sgn);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = z[i] * g;
+    for (int i = 0; i < 16; ++i) z[i] = z[i] * gz;
     const Block46 q = quant_block16<MODE>(z, sh_tab);
     *reinterpret_cast<uint2*>(codes + f * 8) = make_uint2(q.lo, q.hi);
     scales[f] = (uint8_t)q.scale;
@@ -250,7 +275,7 @@ static void launch_amax(const uint16_t* x, long long nseg, bool rht, uint32_t si
                         hipStream_t s) {
   uint32_t* amax = static_cast<uint32_t*>(workspace);
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256);
-  const unsigned g0 = grid_for(nseg, 4);
+  const unsigned g0 = grid_for(nseg, 4 * kAmaxUnroll);
   const unsigned ga = g0 < (unsigned)kAmaxMaxWG ? g0 : (unsigned)kAmaxMaxWG;
   if (rht)
     amax16_kernel<true><<<ga, kAWThreads, 0, s>>>(x, nseg, sign_mask, partial);
