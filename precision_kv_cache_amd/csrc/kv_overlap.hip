@@ -11,13 +11,14 @@
 //
 //   * one launch of ordinary (non-persistent) workgroups; the grid is a
 //     sequence of segments, segment s holding the statistics tiles of unit s
-//     and the quantize tiles of unit s - depth, interleaved evenly;
+//     followed by the quantize tiles of unit s - depth;
 //   * a statistics tile reads 512 rows of one head with ordinary loads (the
 //     lines stay in the Infinity Cache) and publishes per-channel partials;
 //     the last tile of a head reduces the head (mean, head maximum), the last
-//     head of a unit sets the unit's tensor scales and raises its ready word;
+//     head of a unit sets the unit's tensor scales and raises its ready words;
 //   * a quantize tile waits for its unit's ready word (one lane polls one of
-//     several replicas), then re-reads its 256 rows and encodes them.
+//     32 copies, with ~1 us back-off), reads the head's means, then re-reads
+//     its 256 rows and encodes them.
 //
 // A quantize tile waits only for statistics tiles of an earlier segment,
 // i.e. of lower workgroup index, and statistics tiles never wait; with
