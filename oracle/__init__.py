@@ -1,4 +1,5 @@
-"""CPU oracle for the NVFP4 "Four-Over-Six" KV-cache smooth-quantize path.
+"""CPU oracle for the NVFP4 "Four-Over-Six" KV-cache smooth-quantize path,
+its dequantize and attention over the cache.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the GPU library or its binding.  It is
@@ -46,6 +47,8 @@ def lib():
             "ora_e2m1_decode_array": (None, [P, l, P, i]),
             "ora_e4m3_decode_array": (None, [P, l, P, i]),
             "ora_candidate_codes": (None, [P, l, f, P]),
+            "ora_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_double, P, l, P, P,
+                                     i]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -241,3 +244,39 @@ def dequantize_2d(codes, scales, tensor_scale):
     out = np.empty((rows, 2 * c2), np.uint16)
     _check(lib().ora_dequantize_2d(_ptr(codes), _ptr(scales), _ptr(ts), rows, 2 * c2, _ptr(out)), "dequantize_2d")
     return out
+
+
+def kv_attention(q, cache, chunk_len, ranges, scale=None, n_kv_heads=None, rows=None, nthreads=0):
+    """Softmax attention of q (bf16 bits [H, Tq, D]) over the keys listed in
+    ranges ([(start, len), ...]) of an NVFP4 cache (the dict smooth_quantize
+    returns; "k_mean" may be None), in double over the exactly decoded K and
+    V.  scale defaults to 1/sqrt(D).  rows: None for all (h, i), else flat
+    indices h * Tq + i.  Returns (out [rows, D] float64, lse [rows] float64);
+    with rows None, out is [H, Tq, D] and lse [H, Tq]."""
+    q = _c(q, np.uint16)
+    H, Tq, D = q.shape
+    kc = _c(cache["k_codes"], np.uint8)
+    Hkv, T, _ = kc.shape
+    if n_kv_heads is not None and n_kv_heads != Hkv:
+        raise ValueError("cache head count differs from n_kv_heads")
+    ks = _c(cache["k_scales"], np.uint8)
+    vc = _c(cache["v_codes"], np.uint8)
+    vs = _c(cache["v_scales"], np.uint8)
+    kg = _c(cache["k_tensor_scale"], np.float32)
+    vg = _c(cache["v_tensor_scale"], np.float32)
+    km = cache.get("k_mean")
+    km = None if km is None else _c(km, np.float32)
+    rg = np.asarray(ranges, np.int32).reshape(-1, 2)
+    rg = np.ascontiguousarray(rg)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rw = None if rows is None else _c(rows, np.int64)
+    n = H * Tq if rw is None else rw.size
+    out = np.empty((n, D), np.float64)
+    lse = np.empty((n,), np.float64)
+    _check(lib().ora_kv_attention(_ptr(q), H, Tq, D, _ptr(kc), _ptr(ks), _ptr(kg), _ptr(km), _ptr(vc), _ptr(vs),
+                                  _ptr(vg), Hkv, T, chunk_len, _ptr(rg) if rg.size else None, rg.shape[0],
+                                  float(scale), _ptr(rw), n, _ptr(out), _ptr(lse), _nt(nthreads)), "kv_attention")
+    if rw is None:
+        return out.reshape(H, Tq, D), lse.reshape(H, Tq)
+    return out, lse

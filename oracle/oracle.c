@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain, slow, CPU reference for the NVFP4 "Four-Over-Six"
- * KV-cache smooth-quantize path and its dequantize.
+ * KV-cache smooth-quantize path, its dequantize, and attention over the cache.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  The GPU library shares no
@@ -19,6 +19,8 @@
  *   - [LL2] training pipeline, step 4: NVFP4 GEMMs use 2D block scales for
  *     weights, 1D block scales for activations, and a random Hadamard
  *     transform (RHT) against outliers.
+   - [LL2] inference pipeline, steps 7 and 9: the cache feeds attention over
+ *     sink frames plus the current window (the attention function below).
  * The page does not define the number formats or the arithmetic.  The
  * readings used here (each marked "convention" where it is used):
  *   E2M1 codes in 16-element blocks, OCP E4M3FN block scales, an FP32 tensor
@@ -640,6 +642,133 @@ ORA_API int ora_dequantize_2d(const uint8_t* codes, const uint8_t* scales, const
       float vs = v * S;
       out[(size_t)r * cols + d] = ora_float_to_bf16(vs * g);
     }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention over the NVFP4 cache (consumer of [LL2] inference pipeline,     */
+/* steps 7 and 9)                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* The page builds the cache for attention (step 7) and attends to a key set
+ * made of sink frames and the current window (step 9), but prints no
+ * attention formula.  Reading (convention): ordinary softmax attention of
+ * each query over the listed keys, with K and V the values the cache
+ * represents, taken exactly (no bf16 step):
+ *   K[j][d] = v * S * g_K[c] + m[c][d],   V[j][d] = v * S * g_V[c],
+ * c = j / L the key's chunk, v the E2M1 value, S the E4M3 block scale.
+ *   s_j = scale * sum_d q[d] K[j][d],   p_j = exp(s_j) / sum_j' exp(s_j'),
+ *   out[d] = sum_j p_j V[j][d],   lse = log sum_j exp(s_j).
+ * The key set is the concatenation of the ranges [start, start + len) (a key
+ * listed twice counts twice); an empty set gives out = 0 and lse = -inf.
+ * Query head h reads cache head h / (H / H_kv).  Everything in double. */
+typedef struct {
+  const uint16_t* q;
+  int H, Tq, D;
+  const uint8_t *kc, *ks, *vc, *vs;
+  const float *kg, *vg, *km;
+  int Hkv, T, L;
+  const int* ranges;
+  int nr;
+  double scale;
+  const long* rows;
+  double *out, *lse;
+} att_ctx;
+
+/* Row j of one cache tensor of head kvh, decoded exactly into x[0..D). */
+static void att_decode_row(const uint8_t* codes, const uint8_t* scales, const float* g, const float* mean, int Hkv,
+                           int T, int D, int L, int kvh, long j, double* x) {
+  long row = (long)kvh * T + j;
+  int c = (int)(j / L);
+  for (int d = 0; d < D; ++d) {
+    uint8_t byte = codes[row * (D / 2) + d / 2];
+    uint8_t code = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15u);
+    double v = (double)ora_e2m1_decode(code);
+    double S = (double)ora_e4m3_decode(scales[row * (D / 16) + d / 16]);
+    x[d] = v * S * (double)g[c];
+    if (mean) x[d] += (double)mean[((size_t)c * Hkv + kvh) * D + d];
+  }
+}
+
+static void att_item(void* vctx, long item) {
+  att_ctx* c = (att_ctx*)vctx;
+  long r = c->rows ? c->rows[item] : item;
+  int h = (int)(r / c->Tq), i = (int)(r % c->Tq), D = c->D;
+  int kvh = h / (c->H / c->Hkv);
+  long nk = 0;
+  for (int k = 0; k < c->nr; ++k) nk += c->ranges[2 * k + 1];
+  double* out = c->out + (size_t)item * D;
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (nk == 0) {
+    c->lse[item] = -INFINITY;
+    return;
+  }
+  double* s = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* x = (double*)malloc(sizeof(double) * (size_t)D);
+  double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!s || !x || !qd) { /* out of memory: the row reads NaN */
+    for (int d = 0; d < D; ++d) out[d] = NAN;
+    c->lse[item] = NAN;
+    free(s);
+    free(x);
+    free(qd);
+    return;
+  }
+  for (int d = 0; d < D; ++d) qd[d] = (double)ora_bf16_to_float(c->q[((size_t)h * c->Tq + i) * D + d]);
+  /* scores */
+  long n = 0;
+  for (int k = 0; k < c->nr; ++k)
+    for (long j = c->ranges[2 * k]; j < (long)c->ranges[2 * k] + c->ranges[2 * k + 1]; ++j) {
+      att_decode_row(c->kc, c->ks, c->kg, c->km, c->Hkv, c->T, D, c->L, kvh, j, x);
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d) dot += qd[d] * x[d];
+      s[n++] = c->scale * dot;
+    }
+  /* softmax with the largest score subtracted, then the weighted sum of V */
+  double mx = s[0];
+  for (long j = 1; j < nk; ++j)
+    if (s[j] > mx) mx = s[j];
+  double l = 0.0;
+  for (long j = 0; j < nk; ++j) {
+    s[j] = exp(s[j] - mx);
+    l += s[j];
+  }
+  n = 0;
+  for (int k = 0; k < c->nr; ++k)
+    for (long j = c->ranges[2 * k]; j < (long)c->ranges[2 * k] + c->ranges[2 * k + 1]; ++j) {
+      att_decode_row(c->vc, c->vs, c->vg, NULL, c->Hkv, c->T, D, c->L, kvh, j, x);
+      double p = s[n++] / l;
+      for (int d = 0; d < D; ++d) out[d] += p * x[d];
+    }
+  c->lse[item] = mx + log(l);
+  free(s);
+  free(x);
+  free(qd);
+}
+
+/* q bf16 [H, Tq, D]; cache tensors as the quantizer writes them ([H_kv, T, D/2]
+ * codes, [H_kv, T, D/16] scales, [T/L] tensor scales, k_mean [T/L, H_kv, D] or
+ * NULL); ranges [n_ranges][2] = (start, len).  rows: NULL for every (h, i) in
+ * order, else n_rows flat indices h * Tq + i.  out double [rows][D], lse
+ * double [rows]. */
+ORA_API int ora_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
+                             const uint8_t* k_scales, const float* k_tensor_scale, const float* k_mean,
+                             const uint8_t* v_codes, const uint8_t* v_scales, const float* v_tensor_scale, int Hkv,
+                             int T, int L, const int* ranges, int n_ranges, double scale, const long* rows,
+                             long n_rows, double* out, double* lse, int nthreads) {
+  if (!q || !k_codes || !k_scales || !k_tensor_scale || !v_codes || !v_scales || !v_tensor_scale || !out || !lse)
+    return -1;
+  if (H <= 0 || Tq < 0 || D <= 0 || D % 16 || Hkv <= 0 || H % Hkv || T < 0 || L <= 0 || T % L || n_ranges < 0)
+    return -2;
+  if (n_ranges > 0 && !ranges) return -1;
+  for (int k = 0; k < n_ranges; ++k)
+    if (ranges[2 * k] < 0 || ranges[2 * k + 1] < 0 || (long)ranges[2 * k] + ranges[2 * k + 1] > T) return -2;
+  long n = rows ? n_rows : (long)H * Tq;
+  for (long r = 0; rows && r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= (long)H * Tq) return -2;
+  att_ctx c = {q, H, Tq, D, k_codes, k_scales, v_codes, v_scales, k_tensor_scale, v_tensor_scale, k_mean,
+               Hkv, T, L, ranges, n_ranges, scale, rows, out, lse};
+  parallel_items(att_item, &c, n, nthreads);
   return 0;
 }
 

@@ -17,6 +17,12 @@ distributions are stated here and nowhere else:
   / 3), times a per-(head, channel) scale 10**U(-1, 1); no offset.
 * activation: N(0, 1) with 0.1 % of elements multiplied by 50, plus a seeded
   16-bit sign mask for the random Hadamard transform; weight: N(0, sigma=0.02).
+* queries (attention over the cache): Q = N(0, 1) + offset[h, d] with
+  offset ~ N(0, 1); the queries of one chunk (7040 tokens) attend to the
+  8-chunk cache layer.  Key sets of the sink layout (inference pipeline, step
+  9): a global sink of the first S_g frames, a shot sink of S_s frames at
+  the start of the current shot, and the most recent chunks; frames are 880
+  tokens, so the segment edges fall inside 64-key tiles.
 
 Draw order inside one generator: noise, offsets, outlier masks.
 """
@@ -127,6 +133,32 @@ def act_weight(seed: int = SEED_ACT, device="cpu", act_rows=ACT_ROWS, act_cols=A
     x, sign_mask = activation(act_rows, act_cols, seed, device)
     w = weight(w_rows, w_cols, seed + 7919, device)
     return x, sign_mask, w
+
+
+ATTN_QUERIES = CHUNK_TOKENS   # queries of one chunk
+SEED_ATTN = 1005
+
+
+def queries(H: int, Tq: int, D: int, seed: int, device="cpu"):
+    """Q bf16 [H, Tq, D]: N(0, 1) plus a per-(head, channel) N(0, 1) offset."""
+    g = _gen(seed, device)
+    q = torch.randn(H, Tq, D, generator=g, device=device, dtype=torch.float32)
+    q += torch.randn(H, 1, D, generator=g, device=device, dtype=torch.float32)
+    return q.to(torch.bfloat16)
+
+
+def sink_ranges(n_chunks: int, chunk_len: int = CHUNK_TOKENS, frame=TOKENS_PER_FRAME, sink_frames=3,
+                shot_start_frame=None, shot_frames=3, window_chunks=3):
+    """(start, len) key ranges of the sink layout over a cache of n_chunks
+    chunks: global sink frames [0, sink_frames), shot sink frames starting at
+    shot_start_frame (default: the middle of the cache), and the last
+    window_chunks chunks.  Segments are disjoint for the defaults."""
+    T = n_chunks * chunk_len
+    if shot_start_frame is None:
+        shot_start_frame = (T // frame) // 2 - 1
+    win = min(window_chunks, n_chunks) * chunk_len
+    r = [(0, sink_frames * frame), (shot_start_frame * frame, shot_frames * frame), (T - win, win)]
+    return [(int(a), int(b)) for a, b in r]
 
 
 def bf16_bits(t: torch.Tensor):
