@@ -196,6 +196,50 @@ NVFP4KV_API int nvfp4_quantize_2d(const uint16_t* w, int rows, int cols, int mod
 NVFP4KV_API int nvfp4_dequantize_2d(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                                     int rows, int cols, uint16_t* out, void* stream) NVFP4KV_NOEXCEPT;
 
+/* Largest number of key ranges one attention call takes. */
+#define NVFP4_ATTN_MAX_RANGES 8
+
+/*
+ * Softmax attention of bf16 queries over key ranges of one layer's NVFP4 KV
+ * cache, decoding the cache on load.  The cache is the one built in inference
+ * pipeline step 7 (smoothed K and V per chunk); the ranges express step 9's
+ * key set: a global sink (the first S_g frames), a shot sink (the first S_s
+ * frames of the current shot, START / LEN only) and the recent window.  The
+ * page gives no attention formula; the reading is ordinary softmax attention
+ * over the values the cache represents:
+ *   K[j] = v * S * g_K[c] + k_mean[c],  V[j] = v * S * g_V[c],  c = j / chunk_len,
+ *   out = sum_j softmax_j(softmax_scale * q . K[j]) V[j],
+ *   lse = ln sum_j exp(softmax_scale * q . K[j]).
+ *
+ *   q             bf16 [H, Tq, D], 16-byte aligned.
+ *   H, Tq, D      query heads, queries per head, head dimension (D == 128).
+ *   k_*, v_*      the cache as nvfp4_kv_smooth_quantize writes it for
+ *                 H_kv heads and T tokens: codes uint8 [H_kv, T, D/2]
+ *                 (k_codes 8-byte aligned, v_codes 2-byte aligned), scales
+ *                 E4M3FN [H_kv, T, D/16], tensor scales fp32 [T / chunk_len].
+ *   k_mean        nullable fp32 [T / chunk_len, H_kv, D] (16-byte aligned);
+ *                 NULL means K was stored without smoothing.
+ *   H_kv          cache heads; query head h reads cache head h / (H / H_kv).
+ *   key_ranges    HOST int [n_ranges][2] = (start, len) in tokens, each inside
+ *                 [0, T); the key set is their concatenation (a key listed
+ *                 twice counts twice).  n_ranges <= NVFP4_ATTN_MAX_RANGES.
+ *   softmax_scale finite and > 0; 1/sqrt(D) is the usual value.
+ *   out           out, bf16 [H, Tq, D], 8-byte aligned.  With no keys: 0.
+ *   lse           out, nullable fp32 [H, Tq] (natural log); -inf with no keys.
+ *
+ * Arithmetic: K is decoded to v * S, exact in bf16, so the logits are exact
+ * up to fp32 accumulation (g_K, the softmax scale and the mean term
+ * q . k_mean[c] are applied in fp32 per chunk); V is decoded to
+ * bf16(v * S * g_V); P V accumulates in fp32 on the matrix cores with P
+ * rounded to bf16, and out is rounded to bf16.
+ */
+NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
+                                   const uint8_t* k_scales, const float* k_tensor_scale, const float* k_mean,
+                                   const uint8_t* v_codes, const uint8_t* v_scales, const float* v_tensor_scale,
+                                   int H_kv, int T, int chunk_len, const int* key_ranges, int n_ranges,
+                                   float softmax_scale, uint16_t* out, float* lse,
+                                   void* stream) NVFP4KV_NOEXCEPT;
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
-    "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
+    "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "ATTN_MAX_RANGES", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
 
@@ -51,6 +51,7 @@ def lib():
             "nvfp4_quantize_1d": (i, [P, i, i, i, i, u32, P, P, P, P, sz, P]),
             "nvfp4_quantize_2d": (i, [P, i, i, i, P, P, P, P, sz, P]),
             "nvfp4_dequantize_2d": (i, [P, P, P, i, i, P, P]),
+            "nvfp4_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P, P]),
             "nvfp4_diag_e2m1_encode": (i, [P, ll, P, P]),
             "nvfp4_diag_candidates": (i, [P, ll, P, P, P]),
             "nvfp4_diag_reciprocal": (i, [P, ll, P, P]),
@@ -155,6 +156,38 @@ def nvfp4_dequantize(codes, scales, tensor_scale, mean, chunk_len, out=None, str
                                 _ptr(out), _stream(stream))
     _check(rc, "nvfp4_dequantize")
     return out
+
+
+ATTN_MAX_RANGES = 8
+
+
+def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False, stream=None):
+    """Softmax attention of q (bf16 [H, Tq, D]) over the keys listed in
+    key_ranges ([(start, len), ...], at most ATTN_MAX_RANGES) of an NVFP4
+    cache: the dict nvfp4_kv_smooth_quantize returns (k_codes, k_scales,
+    k_tensor_scale, k_mean (may be None), v_codes, v_scales, v_tensor_scale),
+    for H_kv heads with H % H_kv == 0.  softmax_scale defaults to 1/sqrt(D).
+    Returns out (bf16 [H, Tq, D]), or (out, lse fp32 [H, Tq]) when lse is
+    True."""
+    _bf16_dev(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [H, Tq, D]")
+    H, Tq, D = q.shape
+    kc = cache["k_codes"]
+    H_kv, T = kc.shape[0], kc.shape[1]
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    rg = [(int(a), int(n)) for a, n in key_ranges]
+    arr = (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
+    if out is None:
+        out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
+    lse_t = torch.empty(H, Tq, dtype=torch.float32, device=q.device) if lse else None
+    rc = lib().nvfp4_kv_attention(
+        _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
+        _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, T, chunk_len, arr,
+        len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
+    _check(rc, "nvfp4_kv_attention")
+    return (out, lse_t) if lse else out
 
 
 def nvfp4_quantize_1d(x, mode=MODE_4OVER6, hadamard=False, sign_mask=0, out=None, workspace=None, stream=None):

@@ -1,0 +1,438 @@
+// kv_attention.hip -- softmax attention of bf16 queries over key ranges of
+// one layer's NVFP4 KV cache, dequantizing the cache on load.  This is the
+// consumer of the cache that the LongLive-2.0 summary page builds in its
+// inference pipeline (step 7: smoothed K and V in NVFP4 per chunk) and reads
+// through a global sink, a shot sink and the recent window (step 9).
+//
+// One workgroup (8 waves) takes 256 queries of one head; each wave holds 32
+// queries as the B operand of v_mfma_f32_16x16x32_bf16.  Keys stream in tiles
+// of 64: the workgroup decodes each tile once into LDS (K as [key][dim], V
+// transposed to [dim][key]) and every wave then computes
+//   S^T = K~ Q^T         (4 key blocks x 2 query blocks x 4 dim steps),
+//   online softmax in the base-2 domain, lane-local per query,
+//   O^T += V~^T P^T      (8 dim blocks x 2 query blocks x 2 key steps),
+// where the S^T accumulators, rounded to bf16, are the P^T operand as they
+// stand: the V tile's key order in LDS is permuted to match them.
+//
+// Decode on load: v comes from the E2M1 conversion instruction (scale 1,
+// exact), then one fp32 multiply by the block scale S.  For K, v * S has at
+// most 6 significant bits, so K~ = v * S is exact in bf16 and the logits are
+// exact up to fp32 accumulation: the per-chunk factor g_K * scale * log2(e)
+// multiplies the accumulated dot product inside the fused multiply-add that
+// feeds exp2, and the smoothing mean enters as the bias
+// scale * log2(e) * (q . m_c), one value per (query, chunk).  For V the
+// factor S * g_V is applied before one rounding to bf16.  Tiles never cross a
+// chunk edge, so the factors and the bias are uniform over a tile.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "host_common.hpp"
+#include "nvfp4_device.hpp"
+#include "nvfp4kv.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kD = 128;              // head dimension of this kernel
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kQW = 32;              // queries per wave
+constexpr int kQB = kWaves * kQW;    // queries per workgroup
+constexpr int kKT = 64;              // keys per tile
+constexpr int kKRow = kD * 2 + 16;   // LDS bytes per K row (padded: 16 rows hit distinct banks)
+constexpr int kVRow = kKT * 2 + 16;  // LDS bytes per V^T row
+constexpr int kKBytes = kKT * kKRow;
+constexpr int kVBytes = kD * kVRow;
+constexpr int kBuf = kKBytes + kVBytes;
+constexpr int kXcds = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint8_t *kc, *ks, *vc, *vs;
+  const float *kg, *vg, *km;
+  uint16_t* out;
+  float* lse;
+  int H, Tq, group, Hkv, T, L;
+  int nr;
+  int rstart[NVFP4_ATTN_MAX_RANGES], rlen[NVFP4_ATTN_MAX_RANGES];
+  float sigma;  // softmax scale * log2(e)
+  int nqb;      // query blocks per head
+  int total;    // H * nqb
+  int per_xcd;  // workgroup slots per XCD
+};
+
+// Next tile of the key list: [start, start + n), n <= 64, inside one range
+// and one chunk.  (r, pos) is the cursor; all of it is workgroup-uniform.
+__device__ __forceinline__ bool next_tile(const AttnParams& p, int& r, int& pos, int& start, int& n) {
+  while (r < p.nr && pos >= p.rstart[r] + p.rlen[r]) {
+    ++r;
+    if (r < p.nr) pos = p.rstart[r];
+  }
+  if (r >= p.nr) return false;
+  const int end = p.rstart[r] + p.rlen[r];
+  const int cend = pos - pos % p.L + min(p.L, end - (pos - pos % p.L));  // min(chunk end, range end)
+  start = pos;
+  n = min(kKT, cend - pos);
+  pos += n;
+  return true;
+}
+
+// Raw cache bytes of one tile, held in registers between the global loads
+// and the decode into LDS.
+struct TileRegs {
+  uint32_t k0, k1;  // K: 16 codes of one (key, block)
+  uint32_t kscale;  // its E4M3 scale byte
+  uint32_t v[4];    // V: 4 codes (2 bytes) of 4 keys
+  uint32_t vscale[4];
+};
+
+// Thread roles for a tile: K -- key tid / 8, block tid % 8 (16 dims); V --
+// keys 4 (tid / 32) .. +3, dims 4 (tid % 32) .. +3.
+__device__ __forceinline__ void load_tile(const AttnParams& p, int kvh, int start, int n, TileRegs& t) {
+  const int tid = threadIdx.x;
+  const size_t row0 = (size_t)kvh * p.T + start;
+  {
+    const int kk = tid >> 3, b = tid & 7;
+    t.k0 = t.k1 = 0u;
+    t.kscale = 0u;
+    if (kk < n) {
+      const uint2 c = *reinterpret_cast<const uint2*>(p.kc + (row0 + kk) * (kD / 2) + 8 * b);
+      t.k0 = c.x;
+      t.k1 = c.y;
+      t.kscale = p.ks[(row0 + kk) * (kD / 16) + b];
+    }
+  }
+  {
+    const int a = tid >> 5, c = tid & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = 4 * a + i;
+      t.v[i] = 0u;
+      t.vscale[i] = 0u;
+      if (kk < n) {
+        t.v[i] = *reinterpret_cast<const uint16_t*>(p.vc + (row0 + kk) * (kD / 2) + 2 * c);
+        t.vscale[i] = p.vs[(row0 + kk) * (kD / 16) + (c >> 2)];
+      }
+    }
+  }
+}
+
+// Two E2M1 codes (byte `sel` of w) -> fp32, exact (scale operand 1).
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Decode the tile's registers into LDS buffer `buf`: K~ = v * S (exact in
+// bf16), V~ = bf16(v * S * gv).  Keys past the tile's end are zeros (their
+// codes and scales were loaded as 0).
+__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& t, float gv) {
+  const int tid = threadIdx.x;
+  {
+    const int kk = tid >> 3, b = tid & 7;
+    const float f = __builtin_amdgcn_cvt_f32_fp8(t.kscale, 0);
+    f32x2 x[8];
+    x[0] = fp4x2<0>(t.k0); x[1] = fp4x2<1>(t.k0); x[2] = fp4x2<2>(t.k0); x[3] = fp4x2<3>(t.k0);
+    x[4] = fp4x2<0>(t.k1); x[5] = fp4x2<1>(t.k1); x[6] = fp4x2<2>(t.k1); x[7] = fp4x2<3>(t.k1);
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(x[i].x * f, x[i].y * f);
+    uint8_t* dst = buf + kk * kKRow + 32 * b;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
+  }
+  {
+    const int a = tid >> 5, c = tid & 31;
+    float val[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = __builtin_amdgcn_cvt_f32_fp8(t.vscale[i], 0) * gv;
+      const f32x2 lo = fp4x2<0>(t.v[i]), hi = fp4x2<1>(t.v[i]);
+      val[i][0] = lo.x * f;
+      val[i][1] = lo.y * f;
+      val[i][2] = hi.x * f;
+      val[i][3] = hi.y * f;
+    }
+    // key 4a + i sits at column 32 (a / 8) + 8 (a % 4) + 4 ((a % 8) / 4) + i of
+    // the V^T rows: the order in which the S^T accumulators hold the keys.
+    const int col = 32 * (a >> 3) + 8 * (a & 3) + 4 * ((a & 7) >> 2);
+    uint8_t* vbuf = buf + kKBytes;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+      uint8_t* dst = vbuf + (4 * c + dd) * kVRow + 2 * col;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(val[0][dd], val[1][dd]), pack_bf16x2(val[2][dd], val[3][dd])};
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ float bf(const bf16x8& v, int i) { return (float)v[i]; }
+
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+
+  // Workgroups are dispatched round-robin over the XCDs; give the slots of
+  // one XCD consecutive query blocks of the same head so that they share
+  // that XCD's L2 for the head's cache.
+  const int w = (int)(blockIdx.x % kXcds) * p.per_xcd + (int)(blockIdx.x / kXcds);
+  if (w >= p.total) return;
+  const int h = w / p.nqb, qb = w % p.nqb;
+  const int kvh = h / p.group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int qw0 = qb * kQB + wave * kQW;
+
+  // Q^T fragments: lane holds query qw0 + 16 nt + l16, dims 32 ks + 8 g .. +7.
+  bf16x8 bq[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int qi = qw0 + 16 * nt + l16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (qi < p.Tq)
+        bq[nt][ks] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)h * p.Tq + qi) * kD + 32 * ks + 8 * g);
+      else
+        bq[nt][ks] = bf16x8{};
+    }
+  }
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m][0] = o[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, beta[2] = {0.f, 0.f};
+  float kf = 0.f;
+  int cur_chunk = -1;
+
+  int r = 0, pos = p.nr > 0 ? p.rstart[0] : 0;
+  int t_start = 0, t_n = 0;
+  bool have = next_tile(p, r, pos, t_start, t_n);
+  TileRegs regs;
+  if (have) {
+    load_tile(p, kvh, t_start, t_n, regs);
+    store_tile(lds, regs, p.vg[t_start / p.L]);
+  }
+  __syncthreads();
+  int cur = 0;
+
+  while (have) {
+    int n_start = 0, n_n = 0;
+    const bool nhave = next_tile(p, r, pos, n_start, n_n);
+    if (nhave) load_tile(p, kvh, n_start, n_n, regs);
+
+    // this tile's chunk: logit factor g_K * sigma and bias sigma * (q . m_c)
+    const int c = t_start / p.L;
+    if (c != cur_chunk) {
+      cur_chunk = c;
+      kf = p.kg[c] * p.sigma;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float part = 0.f;
+        if (p.km) {
+          const float* mc = p.km + ((size_t)c * p.Hkv + kvh) * kD + 8 * g;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const float4 m0 = *reinterpret_cast<const float4*>(mc + 32 * ks);
+            const float4 m1 = *reinterpret_cast<const float4*>(mc + 32 * ks + 4);
+            const bf16x8& qv = bq[nt][ks];
+            part = __builtin_fmaf(bf(qv, 0), m0.x, part);
+            part = __builtin_fmaf(bf(qv, 1), m0.y, part);
+            part = __builtin_fmaf(bf(qv, 2), m0.z, part);
+            part = __builtin_fmaf(bf(qv, 3), m0.w, part);
+            part = __builtin_fmaf(bf(qv, 4), m1.x, part);
+            part = __builtin_fmaf(bf(qv, 5), m1.y, part);
+            part = __builtin_fmaf(bf(qv, 6), m1.z, part);
+            part = __builtin_fmaf(bf(qv, 7), m1.w, part);
+          }
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        beta[nt] = part * p.sigma;
+      }
+    }
+
+    const uint8_t* kb = lds + cur * kBuf;
+    const uint8_t* vb = kb + kKBytes;
+
+    // S^T = K~ Q^T: s[mt][nt][i] = q . (v S) of key 16 mt + 4 g + i, query 16 nt + l16
+    f32x4 s[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 a = lds_frag(kb + (16 * mt + l16) * kKRow + 64 * ks + 16 * g);
+        s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[0][ks], s[mt][0], 0, 0, 0);
+        s[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[1][ks], s[mt][1], 0, 0, 0);
+      }
+    }
+    if (t_n < kKT) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * mt + 4 * g + i >= t_n) s[mt][0][i] = s[mt][1][i] = -INFINITY;
+    }
+
+    // online softmax, base 2: logit = s * kf + beta (kf >= 0, so the largest s
+    // gives the largest logit)
+    float alpha[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = s[0][nt][0];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(M[nt], __builtin_fmaf(mx, kf, beta[nt]));
+      alpha[nt] = __builtin_amdgcn_exp2f(M[nt] - mnew);
+      const float c0 = beta[nt] - mnew;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[mt][nt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][i], kf, c0));
+      if (t_n < kKT) {  // keys past the tile's end weigh 0 (also when kf == 0)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * mt + 4 * g + i >= t_n) s[mt][nt][i] = 0.f;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs += s[mt][nt][i];
+      lsum[nt] = __builtin_fmaf(lsum[nt], alpha[nt], rs);
+      M[nt] = mnew;
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[m][nt] *= alpha[nt];
+    }
+
+    // P^T fragments: keys 32 kb + 8 g + j (j < 4: block 2 kb, j >= 4: block 2 kb + 1)
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const f32x4 a = s[2 * k2][nt], b = s[2 * k2 + 1][nt];
+        const u32x4 u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                      pack_bf16x2(b[2], b[3])};
+        pb[k2][nt] = __builtin_bit_cast(bf16x8, u);
+      }
+
+    // O^T += V~^T P^T
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const bf16x8 a = lds_frag(vb + (16 * m + l16) * kVRow + 64 * k2 + 16 * g);
+        o[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k2][0], o[m][0], 0, 0, 0);
+        o[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k2][1], o[m][1], 0, 0, 0);
+      }
+    }
+
+    if (nhave) {
+      store_tile(lds + (cur ^ 1) * kBuf, regs, p.vg[n_start / p.L]);
+    }
+    __syncthreads();
+    cur ^= 1;
+    t_start = n_start;
+    t_n = n_n;
+    have = nhave;
+  }
+
+  // O = O^T / l, rows of 4 dims per lane; lse = ln 2 * (M + log2 l)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float l = lsum[nt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int qi = qw0 + 16 * nt + l16;
+    if (qi >= p.Tq) continue;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    uint16_t* dst = p.out + ((size_t)h * p.Tq + qi) * kD + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const f32x4 v = o[m][nt];
+      *reinterpret_cast<u32x2*>(dst + 16 * m) = u32x2{pack_bf16x2(v[0] * inv, v[1] * inv),
+                                                      pack_bf16x2(v[2] * inv, v[3] * inv)};
+    }
+    if (p.lse && g == 0) p.lse[(size_t)h * p.Tq + qi] = (M[nt] + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
+                                              const uint8_t* k_scales, const float* k_tensor_scale,
+                                              const float* k_mean, const uint8_t* v_codes, const uint8_t* v_scales,
+                                              const float* v_tensor_scale, int H_kv, int T, int chunk_len,
+                                              const int* key_ranges, int n_ranges, float softmax_scale,
+                                              uint16_t* out, float* lse, void* stream) noexcept {
+  if (H < 0 || Tq < 0 || T < 0 || H_kv < 1 || chunk_len < 1 || D != kD) return NVFP4_ERR_SHAPE;
+  if (H % H_kv != 0 || T % chunk_len != 0) return NVFP4_ERR_SHAPE;
+  if (n_ranges < 0 || n_ranges > NVFP4_ATTN_MAX_RANGES || !(softmax_scale > 0.f && softmax_scale <= 3.0e38f))
+    return NVFP4_ERR_SHAPE;
+  if (n_ranges > 0 && !key_ranges) return NVFP4_ERR_NULL;
+  for (int i = 0; i < n_ranges; ++i) {
+    const long long a = key_ranges[2 * i], n = key_ranges[2 * i + 1];
+    if (a < 0 || n < 0 || a + n > T) return NVFP4_ERR_SHAPE;
+  }
+  if (H == 0 || Tq == 0) return NVFP4_OK;
+  if (!q || !out) return NVFP4_ERR_NULL;
+  if (T > 0 && (!k_codes || !k_scales || !k_tensor_scale || !v_codes || !v_scales || !v_tensor_scale))
+    return NVFP4_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(k_codes, 8) || !aligned(v_codes, 2) ||
+      !aligned(k_mean, 16) || !aligned(k_tensor_scale, 4) || !aligned(v_tensor_scale, 4) || !aligned(lse, 4))
+    return NVFP4_ERR_ALIGN;
+  const size_t nq = (size_t)H * Tq * kD, nkv = (size_t)H_kv * T * kD, nc = (size_t)(T / chunk_len);
+  const Range in[8] = {range_of(q, nq * 2),
+                       range_of(k_codes, nkv / 2),
+                       range_of(k_scales, nkv / 16),
+                       range_of(k_tensor_scale, nc * 4),
+                       range_of(k_mean, k_mean ? nc * H_kv * kD * 4 : 0),
+                       range_of(v_codes, nkv / 2),
+                       range_of(v_scales, nkv / 16),
+                       range_of(v_tensor_scale, nc * 4)};
+  const Range outr[2] = {range_of(out, nq * 2), range_of(lse, lse ? (size_t)H * Tq * 4 : 0)};
+  if (any_alias(in, 8, outr, 2)) return NVFP4_ERR_ALIAS;
+
+  AttnParams p{};
+  p.q = q;
+  p.kc = k_codes; p.ks = k_scales; p.vc = v_codes; p.vs = v_scales;
+  p.kg = k_tensor_scale; p.vg = v_tensor_scale; p.km = k_mean;
+  p.out = out; p.lse = lse;
+  p.H = H; p.Tq = Tq; p.group = H / H_kv; p.Hkv = H_kv; p.T = T; p.L = chunk_len;
+  p.nr = 0;
+  for (int i = 0; i < n_ranges; ++i) {
+    if (key_ranges[2 * i + 1] == 0) continue;
+    p.rstart[p.nr] = key_ranges[2 * i];
+    p.rlen[p.nr] = key_ranges[2 * i + 1];
+    ++p.nr;
+  }
+  p.sigma = softmax_scale * 1.4426950408889634f;
+  p.nqb = (Tq + kQB - 1) / kQB;
+  const long long total = (long long)H * p.nqb;
+  if (total > (1LL << 28)) return NVFP4_ERR_SHAPE;
+  p.total = (int)total;
+  p.per_xcd = (p.total + kXcds - 1) / kXcds;
+  (void)hipGetLastError();
+  attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, as_stream(stream)>>>(p);
+  return launch_status();
+}

@@ -129,6 +129,38 @@ def test_dequant_and_1d_2d_argument_errors():
     assert L.nvfp4_diag_candidates(None, -1, None, None, None) == SHAPE
 
 
+def _att(q=FAKE, H=2, Tq=16, D=128, kc=FAKE + (1 << 30), ks=FAKE + (2 << 30), kg=FAKE + (3 << 30),
+         km=FAKE + (4 << 30), vc=FAKE + (5 << 30), vs=FAKE + (6 << 30), vg=FAKE + (7 << 30), Hkv=1, T=64, L=32,
+         ranges=((0, 64),), n=None, scale=0.088, out=FAKE + (8 << 30), lse=FAKE + (9 << 30)):
+    V = ctypes.c_void_p
+    flat = [x for r in (ranges or ()) for x in r]
+    arr = (ctypes.c_int * max(1, len(flat)))(*flat) if ranges is not None else None
+    n = len(ranges or ()) if n is None else n
+    return P.lib().nvfp4_kv_attention(V(q), H, Tq, D, V(kc), V(ks), V(kg), V(km), V(vc), V(vs), V(vg), Hkv, T, L,
+                                      arr, n, scale, V(out), V(lse), None)
+
+
+def test_attention_argument_errors():
+    assert _att(D=64) == SHAPE
+    assert _att(Hkv=3) == SHAPE                    # H % H_kv
+    assert _att(T=65) == SHAPE                     # T % chunk_len
+    assert _att(ranges=((60, 5),)) == SHAPE        # past the cache end
+    assert _att(ranges=((-1, 2),)) == SHAPE
+    assert _att(ranges=((0, 1),) * 9) == SHAPE     # more than the maximum count of ranges
+    assert _att(scale=float("inf")) == SHAPE
+    assert _att(scale=0.0) == SHAPE
+    assert _att(scale=-0.1) == SHAPE
+    assert _att(ranges=None, n=1) == NULL
+    assert _att(q=None) == NULL
+    assert _att(kc=None) == NULL
+    assert _att(q=FAKE + 8) == ALIGN
+    assert _att(km=FAKE + (4 << 30) + 4) == ALIGN
+    assert _att(out=FAKE + 64) == ALIAS            # output inside q
+    assert _att(lse=FAKE + (8 << 30) + 32) == ALIAS  # lse inside out
+    assert _att(H=0, q=None, out=None) == OK       # empty call
+    assert _att(Tq=0) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(P, "_lib", None)
     monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))

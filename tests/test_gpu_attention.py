@@ -1,0 +1,203 @@
+"""GPU parity of nvfp4_kv_attention (attention over the NVFP4 cache) with the
+oracle's fp64 attention over the exactly decoded cache.
+
+The caches are built by the oracle quantizer from the seeded workloads, so
+both sides read the same bytes.  Tolerance (derived from the kernel's
+arithmetic, stated per row):
+  - K~ = v * S is exact in bf16, so a logit differs from the exact one only by
+    fp32 accumulation and scaling: at most
+    delta = 2^-16 * sigma * sum_d |q_d| (g_K |v S|_jd + |m_d|)  (base-2 units),
+    sigma = scale * log2(e);
+  - with eps = ln 2 * max_j delta the normalized weights move by at most
+    exp(2 eps) - 1 in total; P and V~ = bf16(v S g_V) are rounded to bf16
+    (2^-9 each, at most 2^-9 max_j |V_jd| each on the output), exp2 is within
+    2^-20 relative, and out is rounded to bf16, so
+      |out - ref|_d <= max_j |V_jd| (exp(2 eps) - 1 + 2^-8 + 2^-16) + 2^-8 |ref_d|,
+      |lse - ref|   <= eps + 2^-20 |ref| + 1e-5.
+  The per-element bound assumes every rounding aligned, so each case also
+  checks the RMS error against the bf16 rounding level, and the zero-query
+  case (all weights exactly 1) checks the key set itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import precision_kv_cache_amd as P
+import workloads as W
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+def _cache(kb, vb, L):
+    return O.smooth_quantize(kb, vb, L)
+
+
+def _to_gpu(c):
+    keys = ("k_codes", "k_scales", "k_tensor_scale", "k_mean", "v_codes", "v_scales", "v_tensor_scale")
+    return {k: (None if c.get(k) is None else torch.from_numpy(np.ascontiguousarray(c[k])).cuda()) for k in keys}
+
+
+def _decode(codes, scales, g, L):
+    """Exact decode (no mean) with numpy: [Hkv, T, D] float64."""
+    Hkv, T, D2 = codes.shape
+    lo, hi = codes & 15, codes >> 4
+    q = np.stack([lo, hi], axis=-1).reshape(Hkv, T, 2 * D2)
+    v = O.e2m1_decode(q).astype(np.float64)
+    S = np.repeat(O.e4m3_decode(scales).astype(np.float64), 16, axis=-1)
+    return v * S * np.asarray(g, np.float64)[np.arange(T) // L][None, :, None]
+
+
+def _keys(ranges):
+    return np.concatenate([np.arange(a, a + n) for a, n in ranges if n > 0]) if ranges else np.zeros(0, int)
+
+
+def _run_gpu(q_bits, cache, L, ranges, scale=None):
+    q = W.from_bits(q_bits, "cuda")
+    H, Tq, D = q.shape
+    out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device="cuda")
+    out.view(torch.uint8).fill_(0xFF)          # NaN: an unwritten output cannot pass
+    o, lse = P.nvfp4_kv_attention(q, _to_gpu(cache), L, ranges, softmax_scale=scale, out=out, lse=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(q_bits, cache, L, ranges, got, got_lse, rows, scale=None, rms_rel=2.0 ** -8):
+    """got [n, D], got_lse [n] for the flat rows `rows`; compare with the oracle."""
+    H, Tq, D = q_bits.shape
+    if scale is None:
+        scale = D ** -0.5
+    ref, ref_lse = O.kv_attention(q_bits, cache, L, ranges, scale=scale, rows=rows)
+    Hkv = cache["k_codes"].shape[0]
+    keys = _keys(ranges)
+    Kp = np.abs(_decode(cache["k_codes"], cache["k_scales"], cache["k_tensor_scale"], L)[:, keys])
+    if cache.get("k_mean") is not None:
+        Kp = Kp + np.abs(np.asarray(cache["k_mean"], np.float64)[keys // L].transpose(1, 0, 2))
+    Vx = _decode(cache["v_codes"], cache["v_scales"], cache["v_tensor_scale"], L)[:, keys]
+    qf = np.abs(W.from_bits(q_bits).float().numpy().astype(np.float64)).reshape(H * Tq, D)[rows]
+    heads = rows // Tq
+    kvh = heads // (H // Hkv)
+    tol = np.empty_like(ref)
+    eps = np.empty(len(rows))
+    for i, r in enumerate(rows):
+        delta = 2.0 ** -16 * scale * LOG2E * (Kp[kvh[i]] @ qf[i]).max()
+        eps[i] = np.log(2.0) * delta
+        vmax = np.abs(Vx[kvh[i]]).max(axis=0)
+        tol[i] = vmax * (np.expm1(2 * eps[i]) + 2.0 ** -8 + 2.0 ** -16) + 2.0 ** -8 * np.abs(ref[i])
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} elements out of bound; worst excess "
+                           f"{(err - tol).max():.3g} at {np.unravel_index(np.argmax(err - tol), err.shape)}")
+    lse_err = np.abs(got_lse - ref_lse)
+    assert np.all(lse_err <= eps + 2.0 ** -20 * np.abs(ref_lse) + 1e-5), lse_err.max()
+    rms = np.sqrt(np.mean(err ** 2))
+    rms_ref = np.sqrt(np.mean(ref ** 2))
+    ratio = np.divide(err, tol, out=np.zeros_like(err), where=tol > 0)
+    say(f"rms err {rms:.3g} = {rms / rms_ref:.3g} x rms(out); max err / bound {ratio.max():.3g}; "
+        f"max lse err {lse_err.max():.3g}")
+    assert rms <= rms_rel * rms_ref, (rms, rms_ref)
+
+
+def _full(q_bits, cache, L, ranges, scale=None, **kw):
+    H, Tq, D = q_bits.shape
+    got, got_lse = _run_gpu(q_bits, cache, L, ranges, scale)
+    rows = np.arange(H * Tq)
+    _check(q_bits, cache, L, ranges, got.reshape(-1, D), got_lse.reshape(-1), rows, scale, **kw)
+
+
+def test_zero_query_weights_every_listed_key_equally():
+    """q = 0: every logit is exactly 0, so out is the mean of V~ over the key
+    set (duplicates counted) and lse = ln N; V~ and out are bf16 roundings
+    (2^-9 each), so a dropped, extra or misplaced key (weight 1/N) shows."""
+    H, Hkv, T, L, D, Tq = 4, 2, 600, 200, 128, 37
+    say("zero query", H, Hkv, T, L, Tq)
+    k, v = W.gaussian_kv(W.KVShape(Hkv, T, D, L), 21)
+    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
+    ranges = [(5, 130), (210, 1), (390, 210), (7, 3)]
+    q = np.zeros((H, Tq, D), np.uint16)
+    got, got_lse = _run_gpu(q, cache, L, ranges)
+    keys = _keys(ranges)
+    Vx = _decode(cache["v_codes"], cache["v_scales"], cache["v_tensor_scale"], L)[:, keys]
+    for h in range(H):
+        ref = Vx[h // 2].mean(axis=0)
+        tol = 2.0 ** -8 * np.abs(Vx[h // 2]).mean(axis=0) + 2.0 ** -8 * np.abs(ref) + 1e-6
+        assert np.all(np.abs(got[h] - ref) <= tol), np.abs(got[h] - ref).max()
+    np.testing.assert_allclose(got_lse, np.log(len(keys)), rtol=1e-6)
+
+
+@pytest.mark.parametrize("H,Hkv,T,L,Tq,ranges", [
+    (2, 2, 640, 128, 300, [(0, 640)]),                         # 5 chunks, ragged query block
+    (4, 2, 640, 128, 256, [(0, 70), (200, 77), (383, 257)]),   # grouped heads, segment edges inside tiles
+    (3, 1, 512, 64, 17, [(448, 64), (0, 64), (100, 1)]),       # one cache head, single-key range
+    (1, 1, 96, 96, 513, [(0, 96)]),                            # one chunk shorter than two tiles
+])
+def test_random_cache(H, Hkv, T, L, Tq, ranges):
+    say("random cache", H, Hkv, T, L, Tq, ranges)
+    k, v = W.gaussian_kv(W.KVShape(Hkv, T, 128, L), 22 + T + Tq)
+    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
+    q = W.bf16_bits(W.queries(H, Tq, 128, 31 + Tq))
+    _full(q, cache, L, ranges)
+
+
+def test_heavy_tail_cache_and_sharp_softmax():
+    """Student-t K and V with per-channel scales, and softmax_scale 1 (logits
+    ~11x larger than 1/sqrt(D)): weights concentrate on few keys."""
+    H, T, L, Tq = 2, 384, 128, 130
+    say("heavy tail", H, T, L, Tq)
+    k, v = W.heavy_tail_kv(W.KVShape(H, T, 128, L), 23)
+    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
+    q = W.bf16_bits(W.queries(H, Tq, 128, 32))
+    _full(q, cache, L, [(0, T)])
+    _full(q, cache, L, [(0, T)], scale=1.0)
+
+
+def test_no_mean_single_key_and_empty():
+    H, T, L, Tq = 2, 128, 64, 40
+    say("no mean / single key / empty", H, T, L, Tq)
+    k, v = W.gaussian_kv(W.KVShape(H, T, 128, L), 24)
+    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
+    q = W.bf16_bits(W.queries(H, Tq, 128, 33))
+    nomean = dict(cache)
+    nomean["k_mean"] = None
+    _full(q, nomean, L, [(0, T)])
+    _full(q, cache, L, [(77, 1)])
+    got, got_lse = _run_gpu(q, cache, L, [])
+    assert np.all(got == 0) and np.all(np.isneginf(got_lse))
+    got, got_lse = _run_gpu(q, cache, L, [(5, 0)])
+    assert np.all(got == 0) and np.all(np.isneginf(got_lse))
+
+
+def test_deterministic():
+    H, T, L, Tq = 2, 256, 128, 300
+    k, v = W.gaussian_kv(W.KVShape(H, T, 128, L), 25)
+    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
+    q = W.bf16_bits(W.queries(H, Tq, 128, 34))
+    a = _run_gpu(q, cache, L, [(0, T)])
+    b = _run_gpu(q, cache, L, [(0, T)])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("layout", ["all", "sink"])
+def test_full_cache_layer_sampled(layout):
+    """The benchmark's workload: one chunk of queries (24 heads x 7040) over
+    the 8-chunk cache layer (56320 keys), either every key or the sink layout
+    (global sink, shot sink across a chunk edge, recent window); 64 sampled
+    query rows, including the last, ragged query block, against the oracle."""
+    shape = W.CACHE_LAYER
+    say("full cache layer", layout, shape)
+    k, v = W.gaussian_kv(shape, W.cache_layer_seed(0), device="cuda")
+    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), shape.chunk_len)
+    del k, v
+    q = W.bf16_bits(W.queries(shape.H, W.ATTN_QUERIES, shape.D, W.SEED_ATTN))
+    ranges = [(0, shape.T)] if layout == "all" else W.sink_ranges(shape.n_chunks)
+    got, got_lse = _run_gpu(q, cache, shape.chunk_len, ranges)
+    Tq = W.ATTN_QUERIES
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.integers(0, shape.H * Tq, 56), [0, Tq - 1, shape.H * Tq - 1],
+                                     (shape.H - 1) * Tq + np.arange(Tq - 5, Tq)]))
+    _check(q, cache, shape.chunk_len, ranges, got.reshape(-1, shape.D)[rows], got_lse.reshape(-1)[rows], rows)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
