@@ -14,6 +14,11 @@ once and written once, codes (0.5 B) and E4M3 scales (1/16 B) written once
 and read once, plus the per-chunk means and tensor scales.
 
 Prints one JSON line.
+
+With --op attention it measures the consumer of the cache instead: softmax
+attention of one chunk of queries (24 heads x 7040, bf16) over one layer's
+whole NVFP4 cache (56320 keys), dequantizing on load (nvfp4_kv_attention);
+value = 4 * heads * queries * keys * head_dim flops / time per call.
 """
 import argparse
 import json
@@ -73,6 +78,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
+    ap.add_argument("--op", choices=("kv", "attention"), default="kv",
+                    help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache")
+    ap.add_argument("--layout", choices=("all", "sink"), default="all",
+                    help="attention key set: every cache key, or the sink layout (global sink, shot sink, window)")
     return ap.parse_args()
 
 
@@ -94,6 +103,9 @@ def main():
         print(f"bench.py measures one GPU only: this path runs on a single MI355X "
               f"(asked for --gpus {a.gpus}, WORLD_SIZE {world}); run it with --gpus 1.", flush=True)
         sys.exit(2)
+    if a.op == "attention":
+        attention_bench(a)
+        return
 
     import torch
 
@@ -357,6 +369,121 @@ def heavy_tail_report(P, W):
         rep[name] = entry
     rep["mse_ratio_4over6_to_fixed6"] = {t: rep["4over6"][t]["mse"] / rep["fixed6"][t]["mse"] for t in ("K", "V")}
     return rep
+
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+ATT_METRIC = "NVFP4-cache attention TFLOP/s (4 * heads * queries * keys * head_dim) and % of MI355X bf16 MFMA peak"
+
+
+def attention_bench(a):
+    """Attention over one layer's NVFP4 cache: the cache is built on the GPU
+    by nvfp4_kv_smooth_quantize from the seeded layer-0 K and V, the queries
+    are one chunk of 7040 tokens.  One step = one nvfp4_kv_attention call."""
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.CACHE_LAYER
+    H, T, D, L = s.H, s.T, s.D, s.chunk_len
+    Tq = W.ATTN_QUERIES
+    t0 = time.time()
+    k, v = W.gaussian_kv(s, W.cache_layer_seed(0), device=dev)
+    cache = P.nvfp4_kv_smooth_quantize(k, v, L)
+    q = W.queries(H, Tq, D, W.SEED_ATTN, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    ranges = [(0, T)] if a.layout == "all" else W.sink_ranges(s.n_chunks)
+    nk = sum(n for _, n in ranges)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        P.nvfp4_kv_attention(q, cache, L, ranges, out=out, stream=stream)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(a.steps)]
+    start, stop = E(), E()
+    start.record(stream)
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        P.nvfp4_kv_attention(q, cache, L, ranges, out=out, stream=stream)
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / a.steps
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
+    flops = 4.0 * H * Tq * nk * D
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    call_tflops = flops / (call_ms * 1e-3) / 1e12
+    cache_bytes = 2 * (H * nk * D // 2 + H * nk * D // 16)  # K and V codes + scales of the listed keys
+    result = {
+        "metric": ATT_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"attention of one chunk of queries [24 heads, 7040, 128] over one layer's NVFP4 cache "
+                        f"({'all 56320 keys' if a.layout == 'all' else 'sink layout'}, chunks of 7040), "
+                        f"dequantized on load",
+            "heads": H, "queries": Tq, "keys": nk, "head_dim": D, "chunk_len": L, "key_ranges": ranges,
+        },
+        "pct_of_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+        "cache_bytes_read": cache_bytes,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "nvfp4_kv_attention (one call)",
+            "achieved": round(call_tflops, 1),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(call_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops,
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = attention_cpu_baseline(k, v, q, L, ranges, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def attention_cpu_baseline(k, v, q, L, ranges, target_s):
+    """The oracle's attention as it stands, on the host cores: the cache is
+    quantized by the oracle from the same K and V, then query rows are
+    attended in batches until about target_s seconds of attention work."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    nt = O.default_threads()
+    cache = O.smooth_quantize(W.bf16_bits(k), W.bf16_bits(v), L, nthreads=nt)
+    qb = W.bf16_bits(q)
+    H, Tq, D = qb.shape
+    nk = sum(n for _, n in ranges)
+    rng = np.random.default_rng(0)
+    done, t_total = 0, 0.0
+    batch = 4 * nt
+    while t_total < target_s and done < H * Tq:
+        rows = rng.integers(0, H * Tq, batch)
+        t0 = time.perf_counter()
+        O.kv_attention(qb, cache, L, ranges, rows=rows, nthreads=nt)
+        t_total += time.perf_counter() - t0
+        done += batch
+    flops = 4.0 * done * nk * D
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+            "sample": f"{done} random query rows of [24, 7040, 128] over {nk} keys (fp64 attention over the "
+                      f"exactly decoded cache)", "seconds": round(t_total, 2)}
 
 
 def cpu_baseline(ks, vs, L, mode, target_s):
