@@ -91,13 +91,16 @@ struct TileRegs {
   uint32_t vscale[4];
 };
 
-// Thread roles for a tile: K -- key tid / 8, block tid % 8 (16 dims); V --
-// keys 4 (tid / 32) .. +3, dims 4 (tid % 32) .. +3.
+// Thread roles for a tile, chosen so that the LDS writes of a wave hit
+// distinct banks: K -- key tid % 64, block tid / 64 (16 dims; eight lanes
+// write eight consecutive padded rows); V -- keys 4 (tid % 16) .. +3, dims
+// 4 (tid / 16) .. +3 (sixteen lanes write the sixteen 8-byte slots of one
+// V^T row).
 __device__ __forceinline__ void load_tile(const AttnParams& p, int kvh, int start, int n, TileRegs& t) {
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)kvh * p.T + start;
   {
-    const int kk = tid >> 3, b = tid & 7;
+    const int kk = tid & 63, b = tid >> 6;
     t.k0 = t.k1 = 0u;
     t.kscale = 0u;
     if (kk < n) {
@@ -108,7 +111,7 @@ __device__ __forceinline__ void load_tile(const AttnParams& p, int kvh, int star
     }
   }
   {
-    const int a = tid >> 5, c = tid & 31;
+    const int a = tid & 15, c = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kk = 4 * a + i;
@@ -134,7 +137,7 @@ __device__ __forceinline__ f32x2 fp4x2(uint32_t w) {
 __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& t, float gv) {
   const int tid = threadIdx.x;
   {
-    const int kk = tid >> 3, b = tid & 7;
+    const int kk = tid & 63, b = tid >> 6;
     const float f = __builtin_amdgcn_cvt_f32_fp8(t.kscale, 0);
     f32x2 x[8];
     x[0] = fp4x2<0>(t.k0); x[1] = fp4x2<1>(t.k0); x[2] = fp4x2<2>(t.k0); x[3] = fp4x2<3>(t.k0);
@@ -147,7 +150,7 @@ __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& t, floa
     *reinterpret_cast<u32x4*>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
   }
   {
-    const int a = tid >> 5, c = tid & 31;
+    const int a = tid & 15, c = tid >> 4;
     float val[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
