@@ -240,6 +240,122 @@ NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, cons
                                    float softmax_scale, uint16_t* out, float* lse,
                                    void* stream) NVFP4KV_NOEXCEPT;
 
+/*
+ * The same attention over a chunk-major cache: codes uint8 [T / chunk_len,
+ * H_kv, chunk_len, D/2], scales [T / chunk_len, H_kv, chunk_len, D/16]; that
+ * is, chunk c is the [H_kv, chunk_len, ...] output of one
+ * nvfp4_kv_smooth_quantize call on that chunk, and chunks follow one another
+ * (the slot layout of the streaming cache below).  Key j still means token
+ * j % chunk_len of chunk j / chunk_len; tensor scales and k_mean are indexed
+ * by chunk as above.  Every other argument and rule is that of
+ * nvfp4_kv_attention.
+ */
+NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
+                                           const uint8_t* k_scales, const float* k_tensor_scale,
+                                           const float* k_mean, const uint8_t* v_codes, const uint8_t* v_scales,
+                                           const float* v_tensor_scale, int H_kv, int T, int chunk_len,
+                                           const int* key_ranges, int n_ranges, float softmax_scale,
+                                           uint16_t* out, float* lse, void* stream) NVFP4KV_NOEXCEPT;
+
+/* ---------------------------------------------------------------------------
+ * Streaming NVFP4 KV cache (inference pipeline, steps 7 to 9 of the summary
+ * page): chunks arrive one at a time and each is quantized (K smoothed, 4/6
+ * block scales) straight into a slot of caller-allocated device storage;
+ * attention then reads
+ *   - the global sink: the first S_g frames of the video (chunk 0),
+ *   - the shot sink: the first S_s frames of the current shot, a START / LEN
+ *     view into the cache (no copy) that is rebound when the prompt
+ *     switches (nvfp4_kv_cache_begin_chunk with new_shot = 1),
+ *   - the window: the last W committed chunks.
+ * A sink that lies inside the window is not listed again; sinks in chunk 0
+ * are merged (the longer of the two).  The page gives the sink structure and
+ * no slot or eviction policy; the one here: the new chunk takes an empty
+ * slot, else the slot of the oldest chunk that the current key set does not
+ * read.  So the append of chunk c never writes memory that an attention call
+ * on the committed state (the chunks before c) reads, and may run on another
+ * stream at the same time as those calls.  Attention calls issued before the
+ * previous nvfp4_kv_cache_end_chunk must be complete, or ordered before the
+ * append, since the slot it takes may have been read by them.
+ *
+ * The state is this plain struct, owned by the caller (host memory); every
+ * cache call below is a host function, and only _append and _attention
+ * enqueue device work (on `stream`).  Storage: `layers` consecutive layer
+ * blocks of nvfp4_kv_cache_layer_bytes() each (256-byte aligned), each block
+ * holding, at the byte offsets nvfp4_kv_cache_offsets() reports:
+ *   k_codes, v_codes    uint8 [capacity, heads, chunk_len, head_dim / 2]
+ *   k_scales, v_scales  E4M3FN [capacity, heads, chunk_len, head_dim / 16]
+ *   k_tensor_scale, v_tensor_scale  fp32 [capacity]
+ *   k_mean              fp32 [capacity, heads, head_dim]
+ * Slot s holds one chunk exactly as nvfp4_kv_smooth_quantize writes it, and
+ * the key set is given in slot coordinates: key j is token j % chunk_len of
+ * slot j / chunk_len (the chunk-major layout of nvfp4_kv_attention_chunked).
+ */
+#define NVFP4_CACHE_MAX_SLOTS 64
+
+typedef struct {
+  /* geometry, set by nvfp4_kv_cache_init */
+  int layers, heads, head_dim, chunk_len, capacity;
+  int frame_tokens, sink_frames, shot_frames, window;
+  /* state */
+  long long chunks;       /* chunks committed so far */
+  long long shot_chunk;   /* first chunk of the current shot */
+  long long pending;      /* chunk between begin and end, -1 when none */
+  int pending_slot;       /* its slot */
+  int pending_new_shot;   /* it starts a new shot */
+  long long slot_chunk[NVFP4_CACHE_MAX_SLOTS]; /* chunk held by each slot, -1 = empty */
+} nvfp4_kv_cache_t;
+
+/* Bytes of one layer block of the storage; 0 for an invalid geometry. */
+NVFP4KV_API size_t nvfp4_kv_cache_layer_bytes(int heads, int head_dim, int chunk_len, int capacity) NVFP4KV_NOEXCEPT;
+
+/* Byte offsets, inside a layer block, of k_codes, v_codes, k_scales,
+ * v_scales, k_tensor_scale, v_tensor_scale, k_mean (in that order) into
+ * off[7].  Host function. */
+NVFP4KV_API int nvfp4_kv_cache_offsets(const nvfp4_kv_cache_t* c, size_t* off) NVFP4KV_NOEXCEPT;
+
+/* Sets up an empty cache.  frame_tokens = L_f; sink_frames = S_g and
+ * shot_frames = S_s (each at most one chunk: frames * frame_tokens <=
+ * chunk_len; 0 disables that sink); window = W in 1 .. NVFP4_ATTN_MAX_RANGES
+ * - 2; capacity (slots per layer) in W + 3 .. NVFP4_CACHE_MAX_SLOTS.  The
+ * first chunk starts the first shot.  head_dim % 16 == 0, <= 4096 (the
+ * attention call needs 128).  Host function; the storage is not touched. */
+NVFP4KV_API int nvfp4_kv_cache_init(nvfp4_kv_cache_t* c, int layers, int heads, int head_dim, int chunk_len,
+                                    int capacity, int frame_tokens, int sink_frames, int shot_frames,
+                                    int window) NVFP4KV_NOEXCEPT;
+
+/* Starts chunk `chunks` (the next one): picks its slot (returned, >= 0), and
+ * with new_shot != 0 makes it the first chunk of a new shot once committed.
+ * NVFP4_ERR_SHAPE if a chunk is already pending.  Host function. */
+NVFP4KV_API int nvfp4_kv_cache_begin_chunk(nvfp4_kv_cache_t* c, int new_shot) NVFP4KV_NOEXCEPT;
+
+/* Quantizes one layer of the pending chunk into its slot:
+ * nvfp4_kv_smooth_quantize(k, v, heads, chunk_len, head_dim, chunk_len,
+ * mode, ...) with the slot's arrays as outputs.  k, v bf16 [heads,
+ * chunk_len, head_dim]; storage (device, 256-byte aligned) of at least
+ * layers * nvfp4_kv_cache_layer_bytes() bytes; workspace as for that call
+ * (nvfp4_kv_workspace_bytes(heads, chunk_len, head_dim, chunk_len)).  Calls
+ * for different layers may run on different streams. */
+NVFP4KV_API int nvfp4_kv_cache_append(const nvfp4_kv_cache_t* c, void* storage, size_t storage_bytes, int layer,
+                                      const uint16_t* k, const uint16_t* v, int mode, void* workspace,
+                                      size_t workspace_bytes, void* stream) NVFP4KV_NOEXCEPT;
+
+/* Commits the pending chunk (all its layers appended): it joins the window,
+ * and becomes the shot sink's chunk if it started a new shot.  Host. */
+NVFP4KV_API int nvfp4_kv_cache_end_chunk(nvfp4_kv_cache_t* c) NVFP4KV_NOEXCEPT;
+
+/* The committed key set as (start, len) ranges in slot coordinates, into
+ * ranges[NVFP4_ATTN_MAX_RANGES][2] (host); returns the count (>= 0), or a
+ * negative status.  Order: global sink, shot sink, window chunks oldest first
+ * (adjacent slots merged).  Host function. */
+NVFP4KV_API int nvfp4_kv_cache_key_ranges(const nvfp4_kv_cache_t* c, int* ranges) NVFP4KV_NOEXCEPT;
+
+/* Attention of q (bf16 [Hq, Tq, head_dim], Hq a multiple of heads) over the
+ * committed key set of one layer: nvfp4_kv_attention_chunked with that
+ * layer's slot arrays, T = capacity * chunk_len and the ranges above. */
+NVFP4KV_API int nvfp4_kv_cache_attention(const nvfp4_kv_cache_t* c, const void* storage, size_t storage_bytes,
+                                         int layer, const uint16_t* q, int Hq, int Tq, float softmax_scale,
+                                         uint16_t* out, float* lse, void* stream) NVFP4KV_NOEXCEPT;
+
 #ifdef __cplusplus
 }
 #endif

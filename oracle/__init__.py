@@ -280,3 +280,22 @@ def kv_attention(q, cache, chunk_len, ranges, scale=None, n_kv_heads=None, rows=
     if rw is None:
         return out.reshape(H, Tq, D), lse.reshape(H, Tq)
     return out, lse
+
+
+def kv_cache_key_tokens(chunks, shot_chunk, chunk_len, frame_tokens, sink_frames, shot_frames, window):
+    """The tokens attention reads from a streaming cache after `chunks`
+    committed chunks, in video token order (token i of chunk c is c * chunk_len
+    + i): the union of the global sink (the first sink_frames frames of the
+    video), the shot sink (the first shot_frames frames of the current shot,
+    which starts at chunk shot_chunk) and the window (the last `window`
+    chunks) -- inference pipeline, step 9 of the LongLive-2.0 summary page.
+    Each token once, sorted."""
+    keys = set()
+    if chunks > 0:
+        keys.update(range(0, sink_frames * frame_tokens))
+        if shot_chunk < chunks:
+            s0 = shot_chunk * chunk_len
+            keys.update(range(s0, s0 + shot_frames * frame_tokens))
+        w0 = max(0, chunks - window)
+        keys.update(range(w0 * chunk_len, chunks * chunk_len))
+    return sorted(keys)

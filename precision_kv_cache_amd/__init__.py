@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
-    "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "ATTN_MAX_RANGES", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
+    "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
+    "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
 
@@ -52,6 +53,16 @@ def lib():
             "nvfp4_quantize_2d": (i, [P, i, i, i, P, P, P, P, sz, P]),
             "nvfp4_dequantize_2d": (i, [P, P, P, i, i, P, P]),
             "nvfp4_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P, P]),
+            "nvfp4_kv_attention_chunked": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P,
+                                               P]),
+            "nvfp4_kv_cache_layer_bytes": (sz, [i, i, i, i]),
+            "nvfp4_kv_cache_offsets": (i, [P, P]),
+            "nvfp4_kv_cache_init": (i, [P, i, i, i, i, i, i, i, i, i]),
+            "nvfp4_kv_cache_begin_chunk": (i, [P, i]),
+            "nvfp4_kv_cache_append": (i, [P, P, sz, i, P, P, i, P, sz, P]),
+            "nvfp4_kv_cache_end_chunk": (i, [P]),
+            "nvfp4_kv_cache_key_ranges": (i, [P, P]),
+            "nvfp4_kv_cache_attention": (i, [P, P, sz, i, P, i, i, ctypes.c_float, P, P, P]),
             "nvfp4_diag_e2m1_encode": (i, [P, ll, P, P]),
             "nvfp4_diag_candidates": (i, [P, ll, P, P, P]),
             "nvfp4_diag_reciprocal": (i, [P, ll, P, P]),
@@ -188,6 +199,119 @@ def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=
         len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
     _check(rc, "nvfp4_kv_attention")
     return (out, lse_t) if lse else out
+
+
+def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False,
+                               stream=None):
+    """nvfp4_kv_attention over a chunk-major cache: cache arrays [n_chunks,
+    H_kv, chunk_len, ...] (each chunk as one quantize call writes it), tensor
+    scales [n_chunks], k_mean [n_chunks, H_kv, D]."""
+    _bf16_dev(q, "q")
+    H, Tq, D = q.shape
+    kc = cache["k_codes"]
+    nch, H_kv, L = kc.shape[0], kc.shape[1], kc.shape[2]
+    if L != chunk_len:
+        raise ValueError("k_codes chunk length differs from chunk_len")
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    rg = [(int(a), int(n)) for a, n in key_ranges]
+    arr = (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
+    if out is None:
+        out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
+    lse_t = torch.empty(H, Tq, dtype=torch.float32, device=q.device) if lse else None
+    rc = lib().nvfp4_kv_attention_chunked(
+        _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
+        _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, nch * L, chunk_len, arr,
+        len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
+    _check(rc, "nvfp4_kv_attention_chunked")
+    return (out, lse_t) if lse else out
+
+
+CACHE_MAX_SLOTS = 64
+
+
+class KVCacheState(ctypes.Structure):
+    """Mirror of nvfp4_kv_cache_t (include/nvfp4kv.h)."""
+    _fields_ = [(n, ctypes.c_int) for n in ("layers", "heads", "head_dim", "chunk_len", "capacity", "frame_tokens",
+                                            "sink_frames", "shot_frames", "window")] + [
+        ("chunks", ctypes.c_longlong), ("shot_chunk", ctypes.c_longlong), ("pending", ctypes.c_longlong),
+        ("pending_slot", ctypes.c_int), ("pending_new_shot", ctypes.c_int),
+        ("slot_chunk", ctypes.c_longlong * CACHE_MAX_SLOTS)]
+
+
+class KVCache:
+    """The streaming NVFP4 KV cache: a KVCacheState plus its device storage
+    (one uint8 tensor, allocated here when not given).  Methods map one to
+    one to the nvfp4_kv_cache_* entry points."""
+
+    def __init__(self, layers, heads, head_dim, chunk_len, capacity, frame_tokens, sink_frames, shot_frames, window,
+                 device="cuda", storage=None):
+        self.state = KVCacheState()
+        _check(lib().nvfp4_kv_cache_init(ctypes.byref(self.state), layers, heads, head_dim, chunk_len, capacity,
+                                         frame_tokens, sink_frames, shot_frames, window), "nvfp4_kv_cache_init")
+        self.layer_bytes = int(lib().nvfp4_kv_cache_layer_bytes(heads, head_dim, chunk_len, capacity))
+        self.storage_bytes = self.layer_bytes * layers
+        if storage is None and device is not None:
+            storage = torch.empty(self.storage_bytes, dtype=torch.uint8, device=device)
+        self.storage = storage
+        off = (ctypes.c_size_t * 7)()
+        _check(lib().nvfp4_kv_cache_offsets(ctypes.byref(self.state), off), "nvfp4_kv_cache_offsets")
+        self.offsets = list(off)
+
+    def begin_chunk(self, new_shot=False):
+        rc = lib().nvfp4_kv_cache_begin_chunk(ctypes.byref(self.state), 1 if new_shot else 0)
+        if rc < 0:
+            raise Nvfp4Error(rc, "nvfp4_kv_cache_begin_chunk")
+        return rc
+
+    def append(self, layer, k, v, mode=MODE_4OVER6, workspace=None, stream=None):
+        _bf16_dev(k, "k"); _bf16_dev(v, "v")
+        st = self.state
+        ws_bytes = nvfp4_kv_workspace_bytes(st.heads, st.chunk_len, st.head_dim, st.chunk_len)
+        if workspace is None:
+            workspace = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=k.device)
+        rc = lib().nvfp4_kv_cache_append(ctypes.byref(st), _ptr(self.storage), self.storage_bytes, layer, _ptr(k),
+                                         _ptr(v), mode, _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(rc, "nvfp4_kv_cache_append")
+
+    def end_chunk(self):
+        _check(lib().nvfp4_kv_cache_end_chunk(ctypes.byref(self.state)), "nvfp4_kv_cache_end_chunk")
+
+    def key_ranges(self):
+        arr = (ctypes.c_int * (2 * ATTN_MAX_RANGES))()
+        n = lib().nvfp4_kv_cache_key_ranges(ctypes.byref(self.state), arr)
+        if n < 0:
+            raise Nvfp4Error(n, "nvfp4_kv_cache_key_ranges")
+        return [(arr[2 * i], arr[2 * i + 1]) for i in range(n)]
+
+    def attention(self, layer, q, softmax_scale=None, out=None, lse=False, stream=None):
+        _bf16_dev(q, "q")
+        Hq, Tq, D = q.shape
+        if softmax_scale is None:
+            softmax_scale = D ** -0.5
+        if out is None:
+            out = torch.empty(Hq, Tq, D, dtype=torch.bfloat16, device=q.device)
+        lse_t = torch.empty(Hq, Tq, dtype=torch.float32, device=q.device) if lse else None
+        rc = lib().nvfp4_kv_cache_attention(ctypes.byref(self.state), _ptr(self.storage), self.storage_bytes, layer,
+                                            _ptr(q), Hq, Tq, float(softmax_scale), _ptr(out), _ptr(lse_t),
+                                            _stream(stream))
+        _check(rc, "nvfp4_kv_cache_attention")
+        return (out, lse_t) if lse else out
+
+    def slot_arrays(self, layer):
+        """Views of one layer's slot arrays (k_codes, v_codes [cap, H, L,
+        D/2], k_scales, v_scales [cap, H, L, D/16], k_tensor_scale,
+        v_tensor_scale [cap], k_mean [cap, H, D])."""
+        st = self.state
+        cap, H, L, D = st.capacity, st.heads, st.chunk_len, st.head_dim
+        base = layer * self.layer_bytes
+        o = self.offsets
+        n = cap * H * L * D
+        b = lambda i, nbytes: self.storage[base + o[i]: base + o[i] + nbytes]  # noqa: E731
+        return {"k_codes": b(0, n // 2).view(cap, H, L, D // 2), "v_codes": b(1, n // 2).view(cap, H, L, D // 2),
+                "k_scales": b(2, n // 16).view(cap, H, L, D // 16), "v_scales": b(3, n // 16).view(cap, H, L, D // 16),
+                "k_tensor_scale": b(4, cap * 4).view(torch.float32), "v_tensor_scale": b(5, cap * 4).view(torch.float32),
+                "k_mean": b(6, cap * H * D * 4).view(torch.float32).view(cap, H, D)}
 
 
 def nvfp4_quantize_1d(x, mode=MODE_4OVER6, hadamard=False, sign_mask=0, out=None, workspace=None, stream=None):

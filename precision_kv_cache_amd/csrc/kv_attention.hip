@@ -58,6 +58,7 @@ struct AttnParams {
   uint16_t* out;
   float* lse;
   int H, Tq, group, Hkv, T, L;
+  long long hstride, cstride;  // cache rows between heads / between chunks (head-major: T, L; chunk-major: L, H_kv L)
   int nr;
   int rstart[NVFP4_ATTN_MAX_RANGES], rlen[NVFP4_ATTN_MAX_RANGES];
   float sigma;  // softmax scale * log2(e)
@@ -98,7 +99,7 @@ struct TileRegs {
 // V^T row).
 __device__ __forceinline__ void load_tile(const AttnParams& p, int kvh, int start, int n, TileRegs& t) {
   const int tid = threadIdx.x;
-  const size_t row0 = (size_t)kvh * p.T + start;
+  const size_t row0 = (size_t)kvh * p.hstride + (size_t)(start / p.L) * p.cstride + start % p.L;
   {
     const int kk = tid & 63, b = tid >> 6;
     t.k0 = t.k1 = 0u;
@@ -389,16 +390,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
 }
 
 }  // namespace
-}  // namespace nvfp4
 
-using namespace nvfp4;
-
-extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
-                                              const uint8_t* k_scales, const float* k_tensor_scale,
-                                              const float* k_mean, const uint8_t* v_codes, const uint8_t* v_scales,
-                                              const float* v_tensor_scale, int H_kv, int T, int chunk_len,
-                                              const int* key_ranges, int n_ranges, float softmax_scale,
-                                              uint16_t* out, float* lse, void* stream) noexcept {
+// Shared host path of the two layouts.
+static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes, const uint8_t* k_scales,
+                     const float* k_tensor_scale, const float* k_mean, const uint8_t* v_codes,
+                     const uint8_t* v_scales, const float* v_tensor_scale, int H_kv, int T, int chunk_len,
+                     const int* key_ranges, int n_ranges, float softmax_scale, uint16_t* out, float* lse,
+                     void* stream, bool chunk_major) {
   if (H < 0 || Tq < 0 || T < 0 || H_kv < 1 || chunk_len < 1 || D != kD) return NVFP4_ERR_SHAPE;
   if (H % H_kv != 0 || T % chunk_len != 0) return NVFP4_ERR_SHAPE;
   if (n_ranges < 0 || n_ranges > NVFP4_ATTN_MAX_RANGES || !(softmax_scale > 0.f && softmax_scale <= 3.0e38f))
@@ -433,6 +431,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, 
   p.kg = k_tensor_scale; p.vg = v_tensor_scale; p.km = k_mean;
   p.out = out; p.lse = lse;
   p.H = H; p.Tq = Tq; p.group = H / H_kv; p.Hkv = H_kv; p.T = T; p.L = chunk_len;
+  p.hstride = chunk_major ? chunk_len : T;
+  p.cstride = chunk_major ? (long long)H_kv * chunk_len : chunk_len;
   p.nr = 0;
   for (int i = 0; i < n_ranges; ++i) {
     if (key_ranges[2 * i + 1] == 0) continue;
@@ -449,4 +449,29 @@ extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, 
   (void)hipGetLastError();
   attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, as_stream(stream)>>>(p);
   return launch_status();
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
+                                              const uint8_t* k_scales, const float* k_tensor_scale,
+                                              const float* k_mean, const uint8_t* v_codes, const uint8_t* v_scales,
+                                              const float* v_tensor_scale, int H_kv, int T, int chunk_len,
+                                              const int* key_ranges, int n_ranges, float softmax_scale,
+                                              uint16_t* out, float* lse, void* stream) noexcept {
+  return attention_launch(q, H, Tq, D, k_codes, k_scales, k_tensor_scale, k_mean, v_codes, v_scales, v_tensor_scale,
+                          H_kv, T, chunk_len, key_ranges, n_ranges, softmax_scale, out, lse, stream, false);
+}
+
+extern "C" NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, int Tq, int D,
+                                                      const uint8_t* k_codes, const uint8_t* k_scales,
+                                                      const float* k_tensor_scale, const float* k_mean,
+                                                      const uint8_t* v_codes, const uint8_t* v_scales,
+                                                      const float* v_tensor_scale, int H_kv, int T, int chunk_len,
+                                                      const int* key_ranges, int n_ranges, float softmax_scale,
+                                                      uint16_t* out, float* lse, void* stream) noexcept {
+  return attention_launch(q, H, Tq, D, k_codes, k_scales, k_tensor_scale, k_mean, v_codes, v_scales, v_tensor_scale,
+                          H_kv, T, chunk_len, key_ranges, n_ranges, softmax_scale, out, lse, stream, true);
 }

@@ -106,3 +106,63 @@ def check_kv(kb, vb, L, mode, res, dev_out=None, nthreads=0, check_dequant=True)
         assert np.array_equal(to_np(dk), rk), "dequantized K differs"
         assert np.array_equal(to_np(dv), rv), "dequantized V differs"
     return ref
+
+
+# ---- attention over the NVFP4 cache ----------------------------------------
+
+LOG2E = 1.4426950408889634
+
+
+def decode_exact(codes, scales, g, L):
+    """Exact decode (no mean) with numpy: [Hkv, T, D] float64."""
+    Hkv, T, D2 = codes.shape
+    lo, hi = codes & 15, codes >> 4
+    q = np.stack([lo, hi], axis=-1).reshape(Hkv, T, 2 * D2)
+    v = O.e2m1_decode(q).astype(np.float64)
+    S = np.repeat(O.e4m3_decode(scales).astype(np.float64), 16, axis=-1)
+    return v * S * np.asarray(g, np.float64)[np.arange(T) // L][None, :, None]
+
+
+
+def key_list(ranges):
+    return np.concatenate([np.arange(a, a + n) for a, n in ranges if n > 0]) if ranges else np.zeros(0, int)
+
+
+
+def attention_check(q_bits, cache, L, ranges, got, got_lse, rows, scale=None, rms_rel=2.0 ** -8):
+    """got [n, D], got_lse [n] for the flat rows `rows`; compare with the oracle."""
+    H, Tq, D = q_bits.shape
+    if scale is None:
+        scale = D ** -0.5
+    ref, ref_lse = O.kv_attention(q_bits, cache, L, ranges, scale=scale, rows=rows)
+    Hkv = cache["k_codes"].shape[0]
+    keys = key_list(ranges)
+    Kp = np.abs(decode_exact(cache["k_codes"], cache["k_scales"], cache["k_tensor_scale"], L)[:, keys])
+    if cache.get("k_mean") is not None:
+        Kp = Kp + np.abs(np.asarray(cache["k_mean"], np.float64)[keys // L].transpose(1, 0, 2))
+    Vx = decode_exact(cache["v_codes"], cache["v_scales"], cache["v_tensor_scale"], L)[:, keys]
+    qf = np.abs(W.from_bits(q_bits).float().numpy().astype(np.float64)).reshape(H * Tq, D)[rows]
+    heads = rows // Tq
+    kvh = heads // (H // Hkv)
+    tol = np.empty_like(ref)
+    eps = np.empty(len(rows))
+    for i, r in enumerate(rows):
+        delta = 2.0 ** -16 * scale * LOG2E * (Kp[kvh[i]] @ qf[i]).max()
+        eps[i] = np.log(2.0) * delta
+        vmax = np.abs(Vx[kvh[i]]).max(axis=0)
+        tol[i] = vmax * (np.expm1(2 * eps[i]) + 2.0 ** -8 + 2.0 ** -16) + 2.0 ** -8 * np.abs(ref[i])
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} elements out of bound; worst excess "
+                           f"{(err - tol).max():.3g} at {np.unravel_index(np.argmax(err - tol), err.shape)}")
+    lse_err = np.abs(got_lse - ref_lse)
+    assert np.all(lse_err <= eps + 2.0 ** -20 * np.abs(ref_lse) + 1e-5), lse_err.max()
+    rms = np.sqrt(np.mean(err ** 2))
+    rms_ref = np.sqrt(np.mean(ref ** 2))
+    ratio = np.divide(err, tol, out=np.zeros_like(err), where=tol > 0)
+    say(f"rms err {rms:.3g} = {rms / rms_ref:.3g} x rms(out); max err / bound {ratio.max():.3g}; "
+        f"max lse err {lse_err.max():.3g}")
+    assert rms <= rms_rel * rms_ref, (rms, rms_ref)
+
+
