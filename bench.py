@@ -19,6 +19,13 @@ With --op attention it measures the consumer of the cache instead: softmax
 attention of one chunk of queries (24 heads x 7040, bf16) over one layer's
 whole NVFP4 cache (56320 keys), dequantizing on load (nvfp4_kv_attention);
 value = 4 * heads * queries * keys * head_dim flops / time per call.
+
+With --op stream it measures the streaming cache: one step is one new chunk
+through 30 layers -- per layer, attention of the chunk's queries over the
+cache's key set (global sink, shot sink, last 3 chunks: 26400 keys) on the
+main stream, and the append of the chunk's K and V (quantized into a free
+slot) on a second stream, overlapping the next layers' attention; the chunk
+is committed at the end.  value = chunk tokens per second.
 """
 import argparse
 import json
@@ -78,8 +85,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
-    ap.add_argument("--op", choices=("kv", "attention"), default="kv",
-                    help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache")
+    ap.add_argument("--op", choices=("kv", "attention", "stream"), default="kv",
+                    help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache; "
+                         "stream: the streaming cache (attention + append per layer)")
     ap.add_argument("--layout", choices=("all", "sink"), default="all",
                     help="attention key set: every cache key, or the sink layout (global sink, shot sink, window)")
     return ap.parse_args()
@@ -105,6 +113,9 @@ def main():
         sys.exit(2)
     if a.op == "attention":
         attention_bench(a)
+        return
+    if a.op == "stream":
+        stream_bench(a)
         return
 
     import torch
@@ -455,6 +466,182 @@ def attention_bench(a):
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = attention_cpu_baseline(k, v, q, L, ranges, a.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+STREAM_METRIC = ("streaming NVFP4 cache: chunk tokens per second (30 layers x [attention over global sink + shot "
+                 "sink + 3-chunk window, append of the chunk's K and V])")
+
+
+def stream_bench(a):
+    """One step = one chunk through the layers: attention(l) on the main
+    stream, append(l) on a second stream after it (the pending slot is not in
+    the key set, so the append may overlap the next layers' attention), then
+    the commit.  The cache (8 slots per layer) is filled with 10 chunks and a
+    prompt switch first, so slots are reused and the shot sink is off chunk 0."""
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.CACHE_LAYER
+    H, D, L, F = s.H, s.D, s.chunk_len, W.TOKENS_PER_FRAME
+    nl = a.layers
+    sink, shot, window, cap = 3, 3, 3, 8
+    t0 = time.time()
+    cache = P.KVCache(nl, H, D, L, cap, F, sink, shot, window, device=dev)
+    # per-layer K and V of one chunk (reused by every appended chunk)
+    kv = [W.gaussian_kv(W.KVShape(H, L, D, L), 200000 + l, device=dev) for l in range(nl)]
+    q = W.queries(H, L, D, W.SEED_ATTN, device=dev)
+    out = torch.empty_like(q)
+    ws = [torch.empty(P.nvfp4_kv_workspace_bytes(H, L, D, L), dtype=torch.uint8, device=dev) for _ in range(2)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    for c in range(10):
+        cache.begin_chunk(new_shot=(c == 5))
+        for l in range(nl):
+            cache.append(l, kv[l][0], kv[l][1], workspace=ws[0], stream=main)
+        cache.end_chunk()
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    ranges = cache.key_ranges()
+    nk = sum(n for _, n in ranges)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(att_ev=None, app_ev=None):
+        cache.begin_chunk()
+        done = [E() for _ in range(nl)]
+        for l in range(nl):
+            if att_ev is not None:
+                att_ev[l][0].record(main)
+            cache.attention(l, q, out=out, stream=main)
+            if att_ev is not None:
+                att_ev[l][1].record(main)
+            done[l].record(main)  # the layer's K and V would come out of this layer's forward
+            side.wait_event(done[l])
+            if app_ev is not None:
+                app_ev[l][0].record(side)
+            cache.append(l, kv[l][0], kv[l][1], workspace=ws[1], stream=side)
+            if app_ev is not None:
+                app_ev[l][1].record(side)
+        main.wait_stream(side)
+        cache.end_chunk()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    # the appends of one chunk alone (no attention beside them), for the
+    # share of their time that the overlap hides
+    cache.begin_chunk()
+    a0, a1 = E(), E()
+    a0.record(main)
+    for l in range(nl):
+        cache.append(l, kv[l][0], kv[l][1], workspace=ws[0], stream=main)
+    a1.record(main)
+    torch.cuda.synchronize()
+    cache.end_chunk()
+    app_alone_ms = a0.elapsed_time(a1) / nl
+    att_ev = [(E(), E()) for _ in range(nl)]
+    app_ev = [(E(), E()) for _ in range(nl)]
+    start, stop = E(), E()
+    start.record(main)
+    for i in range(a.steps):
+        last = i == a.steps - 1
+        step(att_ev if last else None, app_ev if last else None)
+    stop.record(main)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / a.steps
+    att_ms = sum(e0.elapsed_time(e1) for e0, e1 in att_ev) / nl
+    app_ms = sum(e0.elapsed_time(e1) for e0, e1 in app_ev) / nl  # beside attention, waits for CUs included
+    # the overlapped quantize kernel's error word of the last append beside attention (0: no wait timed out)
+    off = P.nvfp4_kv_error_word_offset(H, L, D, L)
+    wait_errors = int(ws[1][off:off + 4].view(torch.int32).item()) if off >= 0 else 0
+    flops = 4.0 * H * L * nk * D
+    att_tflops = flops / (att_ms * 1e-3) / 1e12
+    result = {
+        "metric": STREAM_METRIC,
+        "value": round(L / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"streaming cache, one chunk (24 heads x 7040 tokens x 128) per step through {nl} layers: "
+                        f"attention over global sink {sink} frames + shot sink {shot} frames + window {window} "
+                        f"chunks ({nk} keys), append of the chunk into an 8-slot cache",
+            "layers": nl, "heads": H, "chunk_len": L, "frame_tokens": F, "keys": nk, "key_ranges": ranges,
+            "slots": cap,
+        },
+        "attention_call_ms": round(att_ms, 4),
+        "append_call_ms_alone": round(app_alone_ms, 4),
+        "append_call_ms_beside_attention": round(app_ms, 4),
+        "serial_sum_ms": round(nl * (att_ms + app_alone_ms), 3),
+        "append_wait_timeouts": wait_errors,
+        "append_hidden_frac": round(max(0.0, min(1.0, (nl * (att_ms + app_alone_ms) - ms_step) /
+                                                 (nl * app_alone_ms))), 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "nvfp4_kv_cache_attention (one layer)",
+            "achieved": round(att_tflops, 1),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(att_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops,
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = stream_cpu_baseline(kv[0], q, cache, ranges, nl, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def stream_cpu_baseline(kv0, q, cache, ranges, nl, target_s):
+    """The oracle on the host cores: one layer's append (smooth-quantize of
+    the chunk) timed once, attention of sampled query rows over the same key
+    set (as a logical head-major cache of the committed chunks) until about
+    target_s seconds; scaled to one chunk through nl layers."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    nt = O.default_threads()
+    st = cache.state
+    L = st.chunk_len
+    kb, vb = W.bf16_bits(kv0[0]), W.bf16_bits(kv0[1])
+    t0 = time.perf_counter()
+    one = O.smooth_quantize(kb, vb, L, nthreads=nt)
+    t_app = time.perf_counter() - t0
+    # the key set's chunks all hold this chunk's data: a logical cache of as many copies as slots
+    cap = st.capacity
+    logical = {key: np.concatenate([one[key]] * cap, axis=1 if one[key].ndim == 3 else 0)
+               for key in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tensor_scale", "v_tensor_scale",
+                           "k_mean")}
+    qb = W.bf16_bits(q)
+    H, Tq, D = qb.shape
+    rng = np.random.default_rng(0)
+    done, t_att = 0, 0.0
+    batch = 4 * nt
+    while t_att < target_s:
+        rows = rng.integers(0, H * Tq, batch)
+        t0 = time.perf_counter()
+        O.kv_attention(qb, logical, L, ranges, rows=rows, nthreads=nt)
+        t_att += time.perf_counter() - t0
+        done += batch
+    step_s = nl * (t_app + t_att / done * H * Tq)
+    return {"value": round(L / step_s, 4), "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"one layer's append of a [24, 7040, 128] chunk ({t_app:.2f} s) and {done} query rows of "
+                      f"attention over {sum(n for _, n in ranges)} keys ({t_att:.2f} s), scaled to {nl} layers x "
+                      f"24 x 7040 rows", "seconds": round(t_app + t_att, 2)}
 
 
 def attention_cpu_baseline(k, v, q, L, ranges, target_s):
