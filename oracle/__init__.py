@@ -47,6 +47,7 @@ def lib():
             "ora_e2m1_decode_array": (None, [P, l, P, i]),
             "ora_e4m3_decode_array": (None, [P, l, P, i]),
             "ora_candidate_codes": (None, [P, l, f, P]),
+            "ora_gemm_w4a4": (i, [P, P, P, i, i, P, P, P, i, i, P, i]),
             "ora_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_double, P, l, P, P,
                                      i]),
         }
@@ -299,3 +300,18 @@ def kv_cache_key_tokens(chunks, shot_chunk, chunk_len, frame_tokens, sink_frames
         w0 = max(0, chunks - window)
         keys.update(range(w0 * chunk_len, chunks * chunk_len))
     return sorted(keys)
+
+
+def gemm_w4a4(a, w, w2d, nthreads=0):
+    """out [M, N] float64 = sum over k of the exactly decoded operands:
+    a = (codes [M, K/2], scales [M, K/16], tensor_scale [1]) -- the activation
+    quantizer's output; w = (codes [N, K/2], scales [N, K/16] or, with w2d,
+    [N/16, K/16], tensor_scale [1])."""
+    ac, as_, ag = _c(a[0], np.uint8), _c(a[1], np.uint8), _c(a[2], np.float32)
+    wc, ws, wg = _c(w[0], np.uint8), _c(w[1], np.uint8), _c(w[2], np.float32)
+    M, K2 = ac.shape
+    N = wc.shape[0]
+    out = np.empty((M, N), np.float64)
+    _check(lib().ora_gemm_w4a4(_ptr(ac), _ptr(as_), _ptr(ag), M, 2 * K2, _ptr(wc), _ptr(ws), _ptr(wg), N,
+                               1 if w2d else 0, _ptr(out), _nt(nthreads)), "gemm_w4a4")
+    return out

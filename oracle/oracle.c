@@ -773,6 +773,69 @@ ORA_API int ora_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint
 }
 
 /* ------------------------------------------------------------------------ */
+/* W4A4 GEMM on NVFP4 operands ([LL2] training pipeline, step 4; inference   */
+/* pipeline, step 6)                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* The page runs its linear layers as NVFP4 GEMMs with 1D block scales on the
+ * activation and 2D block scales on the weight, and gives no formula.
+ * Reading (convention): the product of the two dequantized operands along
+ * their shared K axis, taken exactly,
+ *   out[m][n] = sum_k A[m][k] * W[n][k],
+ *   A[m][k] = v * S_A(m, k/16) * g_A,   W[n][k] = v * S_W(blk) * g_W,
+ * with blk = (n, k/16) for 1D weight blocks or (n/16, k/16) for 2D tiles.
+ * A rotation applied before quantization (the RHT) is not undone: the
+ * product is that of the stored operands.  Everything in double. */
+typedef struct {
+  const uint8_t *ac, *as, *wc, *ws;
+  double ga, gw;
+  int M, N, K, w2d;
+  double* out;
+} gemm_ctx;
+
+static void gemm_row(void* vctx, long m) {
+  gemm_ctx* c = (gemm_ctx*)vctx;
+  int K = c->K;
+  double* a = (double*)malloc(sizeof(double) * (size_t)K);
+  double* out = c->out + (size_t)m * c->N;
+  if (!a) {
+    for (int n = 0; n < c->N; ++n) out[n] = NAN;
+    return;
+  }
+  for (int k = 0; k < K; ++k) {
+    uint8_t byte = c->ac[(size_t)m * (K / 2) + k / 2];
+    uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15u);
+    a[k] = (double)ora_e2m1_decode(code) * (double)ora_e4m3_decode(c->as[(size_t)m * (K / 16) + k / 16]) * c->ga;
+  }
+  for (int n = 0; n < c->N; ++n) {
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) {
+      uint8_t byte = c->wc[(size_t)n * (K / 2) + k / 2];
+      uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15u);
+      size_t si = c->w2d ? (size_t)(n / 16) * (K / 16) + k / 16 : (size_t)n * (K / 16) + k / 16;
+      double w = (double)ora_e2m1_decode(code) * (double)ora_e4m3_decode(c->ws[si]) * c->gw;
+      acc += a[k] * w;
+    }
+    out[n] = acc;
+  }
+  free(a);
+}
+
+/* a: codes [M, K/2], scales [M, K/16], tensor scale; w: codes [N, K/2],
+ * scales [N, K/16] (w2d = 0) or [N/16, K/16] (w2d = 1), tensor scale.
+ * out double [M, N]. */
+ORA_API int ora_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale, int M,
+                          int K, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
+                          int N, int w2d, double* out, int nthreads) {
+  if (!a_codes || !a_scales || !a_tensor_scale || !w_codes || !w_scales || !w_tensor_scale || !out) return -1;
+  if (M < 0 || N < 0 || K <= 0 || K % 16 || (w2d && N % 16)) return -2;
+  gemm_ctx c = {a_codes, a_scales, w_codes, w_scales, (double)a_tensor_scale[0], (double)w_tensor_scale[0],
+                M, N, K, w2d != 0, out};
+  parallel_items(gemm_row, &c, M, nthreads);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array helpers for the tests                                              */
 /* ------------------------------------------------------------------------ */
 
