@@ -257,6 +257,35 @@ NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, int Tq, int
                                            const int* key_ranges, int n_ranges, float softmax_scale,
                                            uint16_t* out, float* lse, void* stream) NVFP4KV_NOEXCEPT;
 
+/*
+ * W4A4 GEMM on NVFP4 operands (training pipeline, step 4: weights with 2D
+ * block scales, activations with 1D block scales; inference pipeline, step
+ * 6: the W4A4 model).  The page gives no formula; the reading is the product
+ * of the two dequantized operands along their shared K axis:
+ *   out[m][n] = bf16( g_A g_W sum_k (v S)_A[m][k] (v S)_W[n][k] ),
+ * v the E2M1 values, S the E4M3 block scales, g the tensor scales.  A
+ * rotation applied before quantization (the random Hadamard transform) is
+ * not undone: rotate both operands along K with the same signs to get the
+ * unrotated product.
+ *
+ *   a_codes, a_scales  the activation as nvfp4_quantize_1d writes it: codes
+ *                      uint8 [M, K/2] (16-byte aligned), scales E4M3FN [M, K/16]
+ *                      (2-byte aligned); a_tensor_scale fp32 [1].
+ *   w_codes, w_scales  the weight [N, K]: codes uint8 [N, K/2] (16-byte
+ *                      aligned); scales [N/16, K/16] when w_2d != 0 (the 2D
+ *                      tiles of nvfp4_quantize_2d) or [N, K/16] (1D blocks of
+ *                      nvfp4_quantize_1d); w_tensor_scale fp32 [1].
+ *   K % 64 == 0 and K >= 64; N % 16 == 0; M >= 0.
+ *   out                bf16 [M, N], 8-byte aligned.
+ * Arithmetic: each operand element decodes exactly to bf16 (v * S has at
+ * most 6 significant bits), the products accumulate in fp32 on the matrix
+ * cores, g_A g_W multiplies the sum once, and the result rounds to bf16.
+ */
+NVFP4KV_API int nvfp4_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                                int M, int K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                const float* w_tensor_scale, int N, int w_2d, uint16_t* out,
+                                void* stream) NVFP4KV_NOEXCEPT;
+
 /* ---------------------------------------------------------------------------
  * Streaming NVFP4 KV cache (inference pipeline, steps 7 to 9 of the summary
  * page): chunks arrive one at a time and each is quantized (K smoothed, 4/6

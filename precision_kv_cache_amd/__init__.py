@@ -16,7 +16,7 @@ __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
-    "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
+    "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
 
@@ -55,6 +55,7 @@ def lib():
             "nvfp4_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P, P]),
             "nvfp4_kv_attention_chunked": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P,
                                                P]),
+            "nvfp4_gemm_w4a4": (i, [P, P, P, i, i, P, P, P, i, i, P, P]),
             "nvfp4_kv_cache_layer_bytes": (sz, [i, i, i, i]),
             "nvfp4_kv_cache_offsets": (i, [P, P]),
             "nvfp4_kv_cache_init": (i, [P, i, i, i, i, i, i, i, i, i]),
@@ -225,6 +226,25 @@ def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=No
         len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
     _check(rc, "nvfp4_kv_attention_chunked")
     return (out, lse_t) if lse else out
+
+
+def nvfp4_gemm_w4a4(a, w, w_2d, out=None, stream=None):
+    """out (bf16 [M, N]) = the product of two NVFP4 operands along K:
+    a = (codes [M, K/2], scales [M, K/16], tensor_scale [1]) as
+    nvfp4_quantize_1d returns them (a dict with those keys also works), w the
+    same for the weight [N, K] with scales [N/16, K/16] (w_2d) or [N, K/16]."""
+    def parts(x):
+        return (x["codes"], x["scales"], x["tensor_scale"]) if isinstance(x, dict) else x
+    ac, as_, ag = parts(a)
+    wc, ws, wg = parts(w)
+    M, K2 = ac.shape
+    N = wc.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=ac.device)
+    rc = lib().nvfp4_gemm_w4a4(_ptr(ac), _ptr(as_), _ptr(ag), M, 2 * K2, _ptr(wc), _ptr(ws), _ptr(wg), N,
+                               1 if w_2d else 0, _ptr(out), _stream(stream))
+    _check(rc, "nvfp4_gemm_w4a4")
+    return out
 
 
 CACHE_MAX_SLOTS = 64

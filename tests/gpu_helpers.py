@@ -150,7 +150,8 @@ def attention_check(q_bits, cache, L, ranges, got, got_lse, rows, scale=None, rm
         delta = 2.0 ** -16 * scale * LOG2E * (Kp[kvh[i]] @ qf[i]).max()
         eps[i] = np.log(2.0) * delta
         vmax = np.abs(Vx[kvh[i]]).max(axis=0)
-        tol[i] = vmax * (np.expm1(2 * eps[i]) + 2.0 ** -8 + 2.0 ** -16) + 2.0 ** -8 * np.abs(ref[i])
+        pre = vmax * (np.expm1(2 * eps[i]) + 2.0 ** -7 + 2.0 ** -16)   # error before the output rounding
+        tol[i] = pre + 2.0 ** -8 * (np.abs(ref[i]) + pre)
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got)), "non-finite output"
     bad = err > tol

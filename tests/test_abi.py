@@ -161,6 +161,26 @@ def test_attention_argument_errors():
     assert _att(Tq=0) == OK
 
 
+def _gemm(ac=FAKE, as_=FAKE + (1 << 30), ag=FAKE + (2 << 30), M=64, K=128, wc=FAKE + (3 << 30),
+          ws=FAKE + (4 << 30), wg=FAKE + (5 << 30), N=32, w2d=1, out=FAKE + (6 << 30)):
+    V = ctypes.c_void_p
+    return P.lib().nvfp4_gemm_w4a4(V(ac), V(as_), V(ag), M, K, V(wc), V(ws), V(wg), N, w2d, V(out), None)
+
+
+def test_gemm_argument_errors():
+    assert _gemm(K=96) == SHAPE          # K % 64
+    assert _gemm(K=0) == SHAPE
+    assert _gemm(N=40) == SHAPE          # N % 16
+    assert _gemm(M=-1) == SHAPE
+    assert _gemm(ac=None) == NULL
+    assert _gemm(wg=None) == NULL
+    assert _gemm(ac=FAKE + 8) == ALIGN   # codes 16-byte aligned
+    assert _gemm(out=FAKE + 4) == ALIGN
+    assert _gemm(out=FAKE + 64) == ALIAS  # output inside A's codes
+    assert _gemm(M=0, ac=None, out=None) == OK
+    assert _gemm(N=0) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(P, "_lib", None)
     monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))

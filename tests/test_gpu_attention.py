@@ -10,9 +10,10 @@ arithmetic, stated per row):
     sigma = scale * log2(e);
   - with eps = ln 2 * max_j delta the normalized weights move by at most
     exp(2 eps) - 1 in total; P and V~ = bf16(v S g_V) are rounded to bf16
-    (2^-9 each, at most 2^-9 max_j |V_jd| each on the output), exp2 is within
-    2^-20 relative, and out is rounded to bf16, so
-      |out - ref|_d <= max_j |V_jd| (exp(2 eps) - 1 + 2^-8 + 2^-16) + 2^-8 |ref_d|,
+    (unit roundoff 2^-8 each, so at most 2^-8 max_j |V_jd| each on the
+    output), exp2 is within 2^-20 relative, and out is rounded to bf16, so
+      pre = max_j |V_jd| (exp(2 eps) - 1 + 2^-7 + 2^-16),
+      |out - ref|_d <= pre + 2^-8 (|ref_d| + pre),
       |lse - ref|   <= eps + 2^-20 |ref| + 1e-5.
   The per-element bound assumes every rounding aligned, so each case also
   checks the RMS error against the bf16 rounding level, and the zero-query
@@ -60,7 +61,8 @@ def _full(q_bits, cache, L, ranges, scale=None, **kw):
 def test_zero_query_weights_every_listed_key_equally():
     """q = 0: every logit is exactly 0, so out is the mean of V~ over the key
     set (duplicates counted) and lse = ln N; V~ and out are bf16 roundings
-    (2^-9 each), so a dropped, extra or misplaced key (weight 1/N) shows."""
+    (unit roundoff 2^-8 each), so a dropped, extra or misplaced key (weight
+    1/N) shows."""
     H, Hkv, T, L, D, Tq = 4, 2, 600, 200, 128, 37
     say("zero query", H, Hkv, T, L, Tq)
     k, v = W.gaussian_kv(W.KVShape(Hkv, T, D, L), 21)
