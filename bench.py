@@ -26,6 +26,11 @@ cache's key set (global sink, shot sink, last 3 chunks: 26400 keys) on the
 main stream, and the append of the chunk's K and V (quantized into a free
 slot) on a second stream, overlapping the next layers' attention; the chunk
 is committed at the end.  value = chunk tokens per second.
+
+With --op gemm it measures the W4A4 GEMM: the [16384, 3072] activation
+(1D blocks after the random Hadamard transform) times the [3072, 3072]
+weight (2D tiles), both quantized on the GPU first; value = 2 M N K flops /
+time per call.
 """
 import argparse
 import json
@@ -85,9 +90,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
-    ap.add_argument("--op", choices=("kv", "attention", "stream"), default="kv",
+    ap.add_argument("--op", choices=("kv", "attention", "stream", "gemm"), default="kv",
                     help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache; "
-                         "stream: the streaming cache (attention + append per layer)")
+                         "stream: the streaming cache (attention + append per layer); gemm: the W4A4 GEMM")
     ap.add_argument("--layout", choices=("all", "sink"), default="all",
                     help="attention key set: every cache key, or the sink layout (global sink, shot sink, window)")
     return ap.parse_args()
@@ -116,6 +121,9 @@ def main():
         return
     if a.op == "stream":
         stream_bench(a)
+        return
+    if a.op == "gemm":
+        gemm_bench(a)
         return
 
     import torch
@@ -601,6 +609,98 @@ def stream_bench(a):
     }
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = stream_cpu_baseline(kv[0], q, cache, ranges, nl, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+GEMM_METRIC = "W4A4 NVFP4 GEMM TFLOP/s (2 M N K) and % of MI355X bf16 MFMA peak"
+
+
+def gemm_bench(a):
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    x, sm, wt = W.act_weight(device=dev)
+    act = P.nvfp4_quantize_1d(x, a.mode, hadamard=True, sign_mask=sm)
+    wq = P.nvfp4_quantize_2d(wt, a.mode)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    M, K = x.shape
+    N = wt.shape[0]
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        P.nvfp4_gemm_w4a4(act, wq, True, out=out, stream=stream)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(a.steps)]
+    start, stop = E(), E()
+    start.record(stream)
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        P.nvfp4_gemm_w4a4(act, wq, True, out=out, stream=stream)
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / a.steps
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    call_tflops = flops / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": GEMM_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "W4A4 GEMM: activation [16384, 3072] (NVFP4 1D blocks after the RHT) x weight "
+                        "[3072, 3072] (NVFP4 2D 16x16 tiles), out bf16 [16384, 3072]",
+            "M": M, "N": N, "K": K, "mode": ["4over6", "fixed6", "fixed4"][a.mode],
+        },
+        "pct_of_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+        "operand_bytes": M * K // 2 + M * K // 16 + N * K // 2 + (N // 16) * (K // 16) + 8,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "nvfp4_gemm_w4a4 (one call)",
+            "achieved": round(call_tflops, 1),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(call_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops,
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        import oracle as O
+        nt = O.default_threads()
+        ac, as_, ag = (act[k].cpu().numpy() for k in ("codes", "scales", "tensor_scale"))
+        wparts = tuple(wq[k].cpu().numpy() for k in ("codes", "scales", "tensor_scale"))
+        rows, t_cpu, done = 0, 0.0, 0
+        rng = __import__("numpy").random.default_rng(0)
+        while t_cpu < a.cpu_seconds:
+            r = rng.integers(0, M, nt)
+            t1 = time.perf_counter()
+            O.gemm_w4a4((ac[r], as_[r], ag), wparts, True, nthreads=nt)
+            t_cpu += time.perf_counter() - t1
+            done += nt
+        result["cpu_baseline"] = {"value": round(2.0 * done * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": nt, "kind": "oracle",
+                                  "sample": f"{done} random rows of the activation x the whole weight (fp64 over "
+                                            f"the exactly decoded operands)", "seconds": round(t_cpu, 2)}
     print(json.dumps(result), flush=True)
 
 
