@@ -286,6 +286,31 @@ NVFP4KV_API int nvfp4_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
                                 const float* w_tensor_scale, int N, int w_2d, uint16_t* out,
                                 void* stream) NVFP4KV_NOEXCEPT;
 
+/*
+ * V with its 16-element blocks along the token axis: block = 16 consecutive
+ * tokens of one (head, channel), so that a P V product can contract over
+ * blocks (the V-blocking variant of inference pipeline, step 7; same 4/6
+ * block scale and one tensor scale per (chunk, V) as nvfp4_kv_smooth_quantize).
+ *
+ *   v             bf16 [H, T, D], 16-byte aligned; D % 64 == 0, D <= 4096.
+ *   chunk_len     % 16 == 0; T % chunk_len == 0 (blocks never cross a chunk).
+ *   mode          nvfp4_mode.
+ *   codes         out, uint8 [H, D, T/2] (8-byte aligned): byte j of a row =
+ *                 token 2j (low nibble) | token 2j+1 << 4.
+ *   scales        out, E4M3FN [H, D, T/16].
+ *   tensor_scale  out, fp32 [T / chunk_len], g_dec per chunk.
+ *   workspace     >= nvfp4_kv_quantize_v_tblocks_workspace_bytes(), 256-byte
+ *                 aligned; contents on entry ignored.
+ * Every block is encoded exactly as the blocks of nvfp4_kv_smooth_quantize's
+ * V: z = fl(v * g_enc) with g_enc = fl(C / A), A the chunk's largest |V|, the
+ * 4/6 choice on fp32 errors, E2M1 round to nearest even.
+ */
+NVFP4KV_API size_t nvfp4_kv_quantize_v_tblocks_workspace_bytes(int H, int T, int D,
+                                                               int chunk_len) NVFP4KV_NOEXCEPT;
+NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H, int T, int D, int chunk_len, int mode,
+                                            uint8_t* codes, uint8_t* scales, float* tensor_scale, void* workspace,
+                                            size_t workspace_bytes, void* stream) NVFP4KV_NOEXCEPT;
+
 /* ---------------------------------------------------------------------------
  * Streaming NVFP4 KV cache (inference pipeline, steps 7 to 9 of the summary
  * page): chunks arrive one at a time and each is quantized (K smoothed, 4/6

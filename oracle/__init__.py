@@ -315,3 +315,25 @@ def gemm_w4a4(a, w, w2d, nthreads=0):
     _check(lib().ora_gemm_w4a4(_ptr(ac), _ptr(as_), _ptr(ag), M, 2 * K2, _ptr(wc), _ptr(ws), _ptr(wg), N,
                                1 if w2d else 0, _ptr(out), _nt(nthreads)), "gemm_w4a4")
     return out
+
+
+def quantize_v_tblocks(v, chunk_len, mode=MODE_4OVER6, nthreads=0):
+    """V (bf16 bits [H, T, D]) with 16-token blocks per (head, channel): each
+    chunk's [H, D, chunk_len] slab (the chunk transposed) is one 1D-blocked
+    tensor with its own tensor scale -- the same encoding as the KV V path
+    (inference pipeline, step 7; 4/6 block scale), blocked along tokens.
+    Returns codes [H, D, T/2], scales [H, D, T/16], tensor_scale [T/L]."""
+    v = _c(v, np.uint16)
+    H, T, D = v.shape
+    nc = T // chunk_len
+    codes = np.empty((H, D, T // 2), np.uint8)
+    scales = np.empty((H, D, T // 16), np.uint8)
+    ts = np.empty((nc,), np.float32)
+    for c in range(nc):
+        x = np.ascontiguousarray(v[:, c * chunk_len:(c + 1) * chunk_len, :].transpose(0, 2, 1)).reshape(H * D,
+                                                                                                        chunk_len)
+        q = quantize_1d(x, mode, nthreads=nthreads)
+        codes[:, :, c * chunk_len // 2:(c + 1) * chunk_len // 2] = q["codes"].reshape(H, D, chunk_len // 2)
+        scales[:, :, c * chunk_len // 16:(c + 1) * chunk_len // 16] = q["scales"].reshape(H, D, chunk_len // 16)
+        ts[c] = q["tensor_scale"][0]
+    return {"codes": codes, "scales": scales, "tensor_scale": ts}

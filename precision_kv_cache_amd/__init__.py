@@ -16,7 +16,7 @@ __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
-    "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
+    "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_kv_quantize_v_tblocks", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
 
@@ -56,6 +56,8 @@ def lib():
             "nvfp4_kv_attention_chunked": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P,
                                                P]),
             "nvfp4_gemm_w4a4": (i, [P, P, P, i, i, P, P, P, i, i, P, P]),
+            "nvfp4_kv_quantize_v_tblocks_workspace_bytes": (sz, [i, i, i, i]),
+            "nvfp4_kv_quantize_v_tblocks": (i, [P, i, i, i, i, i, P, P, P, P, sz, P]),
             "nvfp4_kv_cache_layer_bytes": (sz, [i, i, i, i]),
             "nvfp4_kv_cache_offsets": (i, [P, P]),
             "nvfp4_kv_cache_init": (i, [P, i, i, i, i, i, i, i, i, i]),
@@ -244,6 +246,26 @@ def nvfp4_gemm_w4a4(a, w, w_2d, out=None, stream=None):
     rc = lib().nvfp4_gemm_w4a4(_ptr(ac), _ptr(as_), _ptr(ag), M, 2 * K2, _ptr(wc), _ptr(ws), _ptr(wg), N,
                                1 if w_2d else 0, _ptr(out), _stream(stream))
     _check(rc, "nvfp4_gemm_w4a4")
+    return out
+
+
+def nvfp4_kv_quantize_v_tblocks(v, chunk_len, mode=MODE_4OVER6, out=None, workspace=None, stream=None):
+    """V bf16 [H, T, D] -> NVFP4 with 16-token blocks per (head, channel):
+    {"codes": [H, D, T/2], "scales": [H, D, T/16], "tensor_scale": [T/L]}."""
+    _bf16_dev(v, "v")
+    H, T, D = v.shape
+    nc = T // chunk_len if chunk_len > 0 else 0
+    if out is None:
+        out = {"codes": torch.empty(H, D, T // 2, dtype=torch.uint8, device=v.device),
+               "scales": torch.empty(H, D, T // 16, dtype=torch.uint8, device=v.device),
+               "tensor_scale": torch.empty(nc, dtype=torch.float32, device=v.device)}
+    if workspace is None:
+        workspace = torch.empty(max(1, int(lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, chunk_len))),
+                                dtype=torch.uint8, device=v.device)
+    rc = lib().nvfp4_kv_quantize_v_tblocks(_ptr(v), H, T, D, chunk_len, mode, _ptr(out["codes"]), _ptr(out["scales"]),
+                                           _ptr(out["tensor_scale"]), _ptr(workspace), workspace.numel(),
+                                           _stream(stream))
+    _check(rc, "nvfp4_kv_quantize_v_tblocks")
     return out
 
 

@@ -181,6 +181,27 @@ def test_gemm_argument_errors():
     assert _gemm(N=0) == OK
 
 
+def test_v_tblocks_argument_errors():
+    V = ctypes.c_void_p
+    L = P.lib()
+    args = lambda **k: [V(k.get("v", FAKE)), k.get("H", 2), k.get("T", 256), k.get("D", 128), k.get("L", 128),  # noqa: E731
+                        k.get("mode", 0), V(k.get("codes", FAKE + (1 << 30))), V(k.get("scales", FAKE + (2 << 30))),
+                        V(k.get("ts", FAKE + (3 << 30))), V(k.get("ws", FAKE + (4 << 30))), k.get("wsb", 1 << 20),
+                        None]
+    f = L.nvfp4_kv_quantize_v_tblocks
+    assert f(*args(D=96)) == SHAPE
+    assert f(*args(L=24)) == SHAPE
+    assert f(*args(T=200)) == SHAPE
+    assert f(*args(mode=5)) == MODE
+    assert f(*args(v=None)) == NULL
+    assert f(*args(ws=None)) == WORKSPACE
+    assert f(*args(wsb=8)) == WORKSPACE
+    assert f(*args(v=FAKE + 8)) == ALIGN
+    assert f(*args(codes=FAKE + 64)) == ALIAS
+    assert f(*args(H=0)) == OK
+    assert L.nvfp4_kv_quantize_v_tblocks_workspace_bytes(2, 256, 128, 100) == 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(P, "_lib", None)
     monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))
