@@ -31,6 +31,10 @@ With --op gemm it measures the W4A4 GEMM: the [16384, 3072] activation
 (1D blocks after the random Hadamard transform) times the [3072, 3072]
 weight (2D tiles), both quantized on the GPU first; value = 2 M N K flops /
 time per call.
+
+With --op vt it measures V of one 8-chunk layer quantized with 16-token
+blocks per channel (nvfp4_kv_quantize_v_tblocks); value = algorithmic bytes
+(bf16 in, codes and scales out) / time per call.
 """
 import argparse
 import json
@@ -90,9 +94,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
-    ap.add_argument("--op", choices=("kv", "attention", "stream", "gemm"), default="kv",
+    ap.add_argument("--op", choices=("kv", "attention", "stream", "gemm", "vt"), default="kv",
                     help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache; "
-                         "stream: the streaming cache (attention + append per layer); gemm: the W4A4 GEMM")
+                         "stream: the streaming cache (attention + append per layer); gemm: the W4A4 GEMM; "
+                         "vt: V blocked along tokens")
     ap.add_argument("--layout", choices=("all", "sink"), default="all",
                     help="attention key set: every cache key, or the sink layout (global sink, shot sink, window)")
     return ap.parse_args()
@@ -124,6 +129,9 @@ def main():
         return
     if a.op == "gemm":
         gemm_bench(a)
+        return
+    if a.op == "vt":
+        vt_bench(a)
         return
 
     import torch
@@ -701,6 +709,76 @@ def gemm_bench(a):
                                   "cores": nt, "kind": "oracle",
                                   "sample": f"{done} random rows of the activation x the whole weight (fp64 over "
                                             f"the exactly decoded operands)", "seconds": round(t_cpu, 2)}
+    print(json.dumps(result), flush=True)
+
+
+VT_METRIC = "V quantize with 16-token blocks per channel: GB/s (bytes in + out) and % of MI355X HBM peak"
+
+
+def vt_bench(a):
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.CACHE_LAYER
+    H, T, D, L = s.H, s.T, s.D, s.chunk_len
+    t0 = time.time()
+    _, v = W.gaussian_kv(s, W.cache_layer_seed(0), device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    out = P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode)
+    ws = torch.empty(P.lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(a.steps)]
+    start, stop = E(), E()
+    start.record(stream)
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode, out=out, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / a.steps
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
+    nbytes = kv_bytes(H, T, D, L, False)
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    call_gbps = nbytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": VT_METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "V of one 8-chunk cache layer, bf16 [24, 56320, 128], chunks of 7040, quantized "
+                               "with 16-token blocks per (head, channel)",
+                   "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
+                   "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": nbytes},
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "nvfp4_kv_quantize_v_tblocks (one layer's V)",
+                     "achieved": round(call_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(call_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes},
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        import oracle as O
+        nt = O.default_threads()
+        done, t_cpu = 0, 0.0
+        while t_cpu < a.cpu_seconds and done < T // L:
+            vb = W.bf16_bits(v[:, done * L:(done + 1) * L])
+            t1 = time.perf_counter()
+            O.quantize_v_tblocks(vb, L, a.mode, nthreads=nt)
+            t_cpu += time.perf_counter() - t1
+            done += 1
+        result["cpu_baseline"] = {"value": round(done * kv_bytes(H, L, D, L, False) / t_cpu / 1e9, 3), "unit": "GB/s",
+                                  "cores": nt, "kind": "oracle",
+                                  "sample": f"{done} chunks of V [24, 7040, 128] quantized with 16-token blocks",
+                                  "seconds": round(t_cpu, 2)}
     print(json.dumps(result), flush=True)
 
 
