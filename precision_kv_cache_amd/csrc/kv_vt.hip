@@ -4,7 +4,7 @@
 // NVFP4 V cache (inference pipeline, step 7) with the same 4/6 block scale
 // (full-stack NVFP4 section) and the same tensor scale per (chunk, tensor).
 //
-// Three launches: a maximum pass (one partial |V| maximum per tile, written,
+// Three launches: a maximum pass (one partial |V| maximum per token tile, written,
 // not accumulated, so nothing needs clearing), a per-chunk reduction that
 // writes g_dec = A / C, and the quantize pass, which stages a tile of up to
 // 128 tokens x 64 channels through LDS, so that each lane reads one
@@ -45,20 +45,32 @@ __device__ __forceinline__ float wave_max_f(float m) {
   return m;
 }
 
-// Partial maximum |V| of every tile (partial[tile]).
+// Partial maximum |V| per (chunk, 128-token tile, head): the tile's rows,
+// all channels, are one contiguous run, streamed with 16-byte loads.
+// partial[(c * tpc + j) * H + h].
 __global__ __launch_bounds__(kVtThreads) void vt_max_kernel(const uint16_t* v, VtGeom g, float* partial) {
   __shared__ float shw[kVtThreads / 64];
-  int c, j, h, cg;
-  vt_tile(g, blockIdx.x, c, j, h, cg);
+  const int h = blockIdx.x % g.H, jc = blockIdx.x / g.H, j = jc % g.tpc, c = jc / g.tpc;
   const int t0 = c * g.L + j * kVtTok;
   const int ntok = min(kVtTok, (c + 1) * g.L - t0);
+  const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)h * g.T + t0) * g.D);
+  const int n16 = ntok * g.D / 8;  // 16-byte pieces of the run
   float m = 0.0f;
-  // 8 lanes per token row (64 channels = 8 x 16 bytes), 32 rows per pass
-  for (int r = threadIdx.x >> 3; r < ntok; r += kVtThreads / 8) {
-    const uint4 a = *reinterpret_cast<const uint4*>(v + ((size_t)h * g.T + t0 + r) * g.D + cg * kVtCh +
-                                                    8 * (threadIdx.x & 7));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(a.x)), fabsf(bf16_hi(a.x))), fmaxf(fabsf(bf16_lo(a.y)), fabsf(bf16_hi(a.y)))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(a.z)), fabsf(bf16_hi(a.z))), fmaxf(fabsf(bf16_lo(a.w)), fabsf(bf16_hi(a.w)))));
+  // eight loads in flight per lane, then their maxima
+  for (int base = 0; base < n16; base += 8 * kVtThreads) {
+    uint4 a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kVtThreads + threadIdx.x;
+      a[u] = i < n16 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(a[u].x)), fabsf(bf16_hi(a[u].x))),
+                         fmaxf(fabsf(bf16_lo(a[u].y)), fabsf(bf16_hi(a[u].y)))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(a[u].z)), fabsf(bf16_hi(a[u].z))),
+                         fmaxf(fabsf(bf16_lo(a[u].w)), fabsf(bf16_hi(a[u].w)))));
+    }
   }
   m = wave_max_f(m);
   if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = m;
@@ -71,7 +83,7 @@ __global__ __launch_bounds__(kVtThreads) void vt_max_kernel(const uint16_t* v, V
 __global__ __launch_bounds__(kVtThreads) void vt_reduce_kernel(const float* partial, VtGeom g, float C,
                                                                uint32_t* amax_bits, float* tensor_scale) {
   __shared__ float shw[kVtThreads / 64];
-  const long long per_chunk = (long long)g.tpc * g.H * g.ncg;
+  const long long per_chunk = (long long)g.tpc * g.H;
   const float* p = partial + blockIdx.x * per_chunk;
   float m = 0.0f;
   for (long long i = threadIdx.x; i < per_chunk; i += blockDim.x) m = fmaxf(m, p[i]);
@@ -169,7 +181,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H,
   uint32_t* amax = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + align_up((size_t)g.ntiles * 4, 256));
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  vt_max_kernel<<<dim3((unsigned)g.ntiles), dim3(kVtThreads), 0, s>>>(v, g, partial);
+  vt_max_kernel<<<dim3((unsigned)(g.ntiles / g.ncg)), dim3(kVtThreads), 0, s>>>(v, g, partial);
   vt_reduce_kernel<<<dim3((unsigned)g.nc), dim3(kVtThreads), 0, s>>>(partial, g, mode_constant(mode), amax,
                                                                       tensor_scale);
   switch (mode) {
