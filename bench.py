@@ -620,7 +620,7 @@ def stream_bench(a):
     print(json.dumps(result), flush=True)
 
 
-GEMM_METRIC = "W4A4 NVFP4 GEMM TFLOP/s (2 M N K) and % of MI355X bf16 MFMA peak"
+GEMM_METRIC = "W4A4 NVFP4 GEMM TFLOP/s (2 M N K) and % of MI355X fp16/bf16 MFMA peak"
 
 
 def gemm_bench(a):
@@ -671,7 +671,7 @@ def gemm_bench(a):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": "W4A4 GEMM: activation [16384, 3072] (NVFP4 1D blocks after the RHT) x weight "

@@ -5,18 +5,22 @@
 //
 //   out[m][n] = bf16( g_A g_W sum_k (v S)_A[m][k] (v S)_W[n][k] )
 //
-// NVFP4 values v * S have at most 6 significant bits, so each operand decodes
-// exactly to bf16; the products are exact in fp32 and accumulate in fp32 on
-// v_mfma_f32_16x16x32_bf16; the two tensor scales multiply the result once.
+// NVFP4 values v * S have at most 6 significant bits and lie in
+// [2^-10, 2688], so each operand decodes exactly to fp16 (one conversion of
+// two E2M1 codes and one packed fp16 multiply by the E4M3 scale per two
+// elements); the products are exact in fp32 and accumulate in fp32 on
+// v_mfma_f32_16x16x32_f16; the two tensor scales multiply the result once.
 // gfx950's scaled FP4 matrix instructions take E8M0 scales per 32 elements,
-// not NVFP4's E4M3 scales per 16, hence decode on load to bf16.
+// not NVFP4's E4M3 scales per 16, hence decode on load.
 //
 // One workgroup (8 waves) computes a 256 x 256 output tile.  K advances in
 // tiles of 64: the workgroup decodes the A and W tiles once into double-
 // buffered LDS ([row][k], 144-byte rows), and each wave, owning 128 rows of
 // M and 64 columns of N, computes C^T = W A^T with W as the matrix
 // instruction's A operand, so that a lane ends with 4 consecutive output
-// columns of one row.
+// columns of one row.  The codes of tile k + 2 are loaded while tile k is
+// multiplied, two lanes per row (32 contiguous bytes), and the decode of tile
+// k + 1 is interleaved with tile k's matrix instructions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,9 +38,9 @@ constexpr int kOpBytes = 256 * kRow;
 constexpr int kGBuf = 2 * kOpBytes;  // A then W
 constexpr int kXcds = 8;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmParams {
   const uint8_t *ac, *as, *wc, *ws;
@@ -53,45 +57,44 @@ struct Unit {
   uint32_t s;
 };
 
-// Row r of the tile (thread t: r = t % 256, block pair t / 256): codes
-// [row][k0/2 + 16 bp .. +15], scales of blocks k0/16 + 2 bp, +1.
+// Thread t's unit of a tile: row t / 2, block pair t % 2 (the two lanes of
+// a row read its 32 contiguous code bytes).  Rows past the operand's end
+// re-read its last row; their products land in outputs that are not stored.
 __device__ __forceinline__ Unit load_unit(const uint8_t* codes, const uint8_t* scales, int rows, int row0, int K,
                                           int k0, bool s2d, int t) {
-  const int r = t & 255, bp = t >> 8;
+  const int bp = t & 1;
+  const int row = min(row0 + (t >> 1), rows - 1);
   Unit u;
-  u.c = make_uint4(0u, 0u, 0u, 0u);
-  u.s = 0u;
-  const int row = row0 + r;
-  if (row < rows) {
-    u.c = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K / 2) + k0 / 2 + 16 * bp);
-    const size_t si = (s2d ? (size_t)(row / 16) : (size_t)row) * (K / 16) + k0 / 16 + 2 * bp;
-    u.s = *reinterpret_cast<const uint16_t*>(scales + si);
-  }
+  u.c = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K / 2) + k0 / 2 + 16 * bp);
+  const size_t si = (s2d ? (size_t)(row / 16) : (size_t)row) * (K / 16) + k0 / 16 + 2 * bp;
+  u.s = *reinterpret_cast<const uint16_t*>(scales + si);
   return u;
 }
 
+// Two E2M1 codes (byte SEL of w) times the scale S, as packed fp16.
 template <int SEL>
-__device__ __forceinline__ f32x2 fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+__device__ __forceinline__ uint32_t fp4x2_scaled(uint32_t w, f16x2 S) {
+  const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL) * S;
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
 }
 
-// v * S of the unit's 32 codes (exact in bf16) into row t % 256 of the
-// operand tile at op.
+// v * S of the unit's 32 codes (exact in fp16) into row t / 2 of the operand
+// tile at op.
 __device__ __forceinline__ void store_unit(uint8_t* op, const Unit& u, int t) {
-  const int r = t & 255, bp = t >> 8;
-  const float S0 = __builtin_amdgcn_cvt_f32_fp8(u.s, 0), S1 = __builtin_amdgcn_cvt_f32_fp8(u.s, 1);
   const uint32_t w[4] = {u.c.x, u.c.y, u.c.z, u.c.w};
-  uint8_t* dst = op + r * kRow + 64 * bp;
+  uint8_t* dst = op + (t >> 1) * kRow + 64 * (t & 1);
+  const f16x2 S = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u.s, 1.0f, false);  // the two E4M3 scales
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float S = j < 2 ? S0 : S1;
-    const f32x2 a = fp4x2<0>(w[j]), b = fp4x2<1>(w[j]), c = fp4x2<2>(w[j]), d = fp4x2<3>(w[j]);
-    *reinterpret_cast<u32x4*>(dst + 16 * j) = u32x4{pack_bf16x2(a.x * S, a.y * S), pack_bf16x2(b.x * S, b.y * S),
-                                                    pack_bf16x2(c.x * S, c.y * S), pack_bf16x2(d.x * S, d.y * S)};
+    const f16x2 Sj = j < 2 ? f16x2{S.x, S.x} : f16x2{S.y, S.y};
+    *reinterpret_cast<u32x4*>(dst + 16 * j) = u32x4{fp4x2_scaled<0>(w[j], Sj), fp4x2_scaled<1>(w[j], Sj),
+                                                    fp4x2_scaled<2>(w[j], Sj), fp4x2_scaled<3>(w[j], Sj)};
   }
 }
 
-__device__ __forceinline__ bf16x8 frag(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f16x8 frag(const uint8_t* p) { return *reinterpret_cast<const f16x8*>(p); }
 
 __global__ __launch_bounds__(kGThreads) void gemm_w4a4_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kGBuf];
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_w4a4_kernel(GemmParams p) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;  // this wave: rows m0 + 128 wm .., columns n0 + 64 wn ..
+  const bool w2 = p.w2d != 0;
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -111,24 +115,31 @@ __global__ __launch_bounds__(kGThreads) void gemm_w4a4_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // tile 0 decoded, tile 1 (clamped to the last) loaded
   const int nk = p.K / kTK;
   Unit ua = load_unit(p.ac, p.as, p.M, m0, p.K, 0, false, t);
-  Unit uw = load_unit(p.wc, p.ws, p.N, n0, p.K, 0, p.w2d != 0, t);
+  Unit uw = load_unit(p.wc, p.ws, p.N, n0, p.K, 0, w2, t);
   store_unit(lds, ua, t);
   store_unit(lds + kOpBytes, uw, t);
+  ua = load_unit(p.ac, p.as, p.M, m0, p.K, min(1, nk - 1) * kTK, false, t);
+  uw = load_unit(p.wc, p.ws, p.N, n0, p.K, min(1, nk - 1) * kTK, w2, t);
   __syncthreads();
 
+  // Iteration kt multiplies tile kt, decodes tile kt + 1 into the other
+  // buffer (free since the previous barrier; after the last tile the decode
+  // is of a clamped repeat that nothing reads) and loads tile kt + 2.  No
+  // branches in the body, so that the scheduling groups below span it.
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      ua = load_unit(p.ac, p.as, p.M, m0, p.K, (kt + 1) * kTK, false, t);
-      uw = load_unit(p.wc, p.ws, p.N, n0, p.K, (kt + 1) * kTK, p.w2d != 0, t);
-    }
+    const Unit ca = ua, cw = uw;
+    const int kn = min(kt + 2, nk - 1) * kTK;
+    ua = load_unit(p.ac, p.as, p.M, m0, p.K, kn, false, t);
+    uw = load_unit(p.wc, p.ws, p.N, n0, p.K, kn, w2, t);
     const uint8_t* A = lds + (kt & 1) * kGBuf;
     const uint8_t* B = A + kOpBytes;
+    uint8_t* nb = lds + ((kt + 1) & 1) * kGBuf;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 wf[4], af[8];
+      f16x8 wf[4], af[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) wf[i] = frag(B + (64 * wn + 16 * i + l16) * kRow + 64 * ks + 16 * g);
 #pragma unroll
@@ -136,12 +147,26 @@ __global__ __launch_bounds__(kGThreads) void gemm_w4a4_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[i], af[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      uint8_t* nb = lds + ((kt + 1) & 1) * kGBuf;
-      store_unit(nb, ua, t);
-      store_unit(nb + kOpBytes, uw, t);
+    store_unit(nb, ca, t);
+    store_unit(nb + kOpBytes, cw, t);
+    // schedule: the loads, the first fragments, then each matrix instruction
+    // followed by a decode instruction (and the second fragments, then the
+    // LDS writes, spread among them)
+    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // global loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      if ((i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS writes
     }
     __syncthreads();
   }
