@@ -764,6 +764,8 @@ def vt_bench(a):
                      "achieved": round(call_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes},
         "input_generation_s": round(gen_s, 2),
+        # the single-launch kernel's error word after the timed calls (0: no wait timed out)
+        "quantize_wait_timeouts": int(ws[:4].view(torch.int32).item()),
     }
     if not a.no_cpu_baseline:
         import oracle as O

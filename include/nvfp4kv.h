@@ -277,9 +277,10 @@ NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, int Tq, int
  *                      nvfp4_quantize_1d); w_tensor_scale fp32 [1].
  *   K % 64 == 0 and K >= 64; N % 16 == 0; M >= 0.
  *   out                bf16 [M, N], 8-byte aligned.
- * Arithmetic: each operand element decodes exactly to bf16 (v * S has at
- * most 6 significant bits), the products accumulate in fp32 on the matrix
- * cores, g_A g_W multiplies the sum once, and the result rounds to bf16.
+ * Arithmetic: each operand element decodes exactly to fp16 (v * S has at
+ * most 6 significant bits and lies in [2^-10, 2688]), the products
+ * accumulate in fp32 on the matrix cores, g_A g_W multiplies the sum once,
+ * and the result rounds to bf16.
  */
 NVFP4KV_API int nvfp4_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                                 int M, int K, const uint8_t* w_codes, const uint8_t* w_scales,
@@ -300,7 +301,11 @@ NVFP4KV_API int nvfp4_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
  *   scales        out, E4M3FN [H, D, T/16].
  *   tensor_scale  out, fp32 [T / chunk_len], g_dec per chunk.
  *   workspace     >= nvfp4_kv_quantize_v_tblocks_workspace_bytes(), 256-byte
- *                 aligned; contents on entry ignored.
+ *                 aligned; contents on entry ignored.  Its first 32-bit word
+ *                 is the error word of the single-launch kernel: each call
+ *                 clears it, and once the call has completed a non-zero value
+ *                 means one of the kernel's bounded waits timed out and the
+ *                 outputs are invalid.
  * Every block is encoded exactly as the blocks of nvfp4_kv_smooth_quantize's
  * V: z = fl(v * g_enc) with g_enc = fl(C / A), A the chunk's largest |V|, the
  * 4/6 choice on fp32 errors, E2M1 round to nearest even.

@@ -4,11 +4,22 @@
 // NVFP4 V cache (inference pipeline, step 7) with the same 4/6 block scale
 // (full-stack NVFP4 section) and the same tensor scale per (chunk, tensor).
 //
-// Three launches: a maximum pass (one partial |V| maximum per token tile, written,
-// not accumulated, so nothing needs clearing), a per-chunk reduction that
-// writes g_dec = A / C, and the quantize pass, which stages a tile of up to
-// 128 tokens x 64 channels through LDS, so that each lane reads one
-// channel's tokens, and runs the shared 4/6 block routine.
+// One launch.  A chunk's tensor scale needs its largest |V| before any of its
+// blocks can be encoded, so each chunk is read twice: by statistics tiles
+// (512 rows of one head each, largest magnitude, published per tile; the
+// last tile of the chunk reduces them, writes g_dec = A / C and raises the
+// chunk's ready words) and by quantize tiles (up to 128 tokens x 64 channels
+// of one head, staged through LDS so that each lane reads one channel's
+// tokens, then the shared 4/6 block routine).  The grid is a sequence of
+// segments, segment s holding the statistics tiles of chunk s and then the
+// quantize tiles of chunk s - depth, so the second read comes from the
+// Infinity Cache and the memory-bound statistics run beside the VALU-bound
+// encoding.  A quantize tile waits only for statistics tiles of an earlier
+// segment (lower workgroup index), and statistics tiles never wait; with
+// in-order dispatch those are resident or finished whenever the quantize
+// tile runs, so the waits cannot cycle.  They are bounded all the same: on
+// time-out the error word (the first word of the workspace) is raised and
+// the tile leaves.  Hand-off between workgroups as in nvfp4_device.hpp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,48 +31,92 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kVtThreads = 256;
-constexpr int kVtTok = 128;  // tokens per tile
-constexpr int kVtCh = 64;    // channels per tile
+constexpr int kVtTok = 128;   // tokens per quantize tile
+constexpr int kVtCh = 64;     // channels per quantize tile
 constexpr int kVtRow = kVtCh * 2;
+constexpr int kVsRows = 512;  // token rows per statistics tile
+constexpr int kVtDepth = 1;   // segments between a chunk's statistics and its quantization
+constexpr int kVtReplicas = 32;
+constexpr int kVtReplicaStride = 32;  // 64-bit words between ready words (256 B)
+constexpr unsigned kVtSpinLimit = 1u << 22;
 
-struct VtGeom {
-  int H, T, D, L, nc, tpc, ncg;  // tiles per chunk, channel groups
-  long long ntiles;
+struct VtParams {
+  const uint16_t* v;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tscale;
+  float* partial;             // [nc][H][nst] largest |V| per statistics tile
+  unsigned long long* ready;  // [kVtReplicas][nc], 256 B apart: 1 << 32 | encode-scale bits once ready
+  unsigned* err;              // [1 + nc]: error word, then per-chunk finished statistics tiles
+  float C;
+  int H, T, D, L, nc, tpc, ncg, nst, depth;
+  unsigned spin_limit;
 };
 
-// tile index -> (chunk, tile in chunk, head, channel group)
-__device__ __forceinline__ void vt_tile(const VtGeom& g, long long i, int& c, int& j, int& h, int& cg) {
-  cg = (int)(i % g.ncg);
-  i /= g.ncg;
-  h = (int)(i % g.H);
-  i /= g.H;
-  j = (int)(i % g.tpc);
-  c = (int)(i / g.tpc);
+// Workspace: error word and counters, ready words, partial maxima.
+struct VtLayout {
+  size_t ready, partial, total;
+  int n_zero_words;  // error word .. end of the ready words, cleared before the launch
+};
+
+VtLayout vt_layout(int H, int nc, int nst) {
+  VtLayout l;
+  size_t off = align_up((size_t)(1 + nc) * sizeof(unsigned), 256);
+  l.ready = off;
+  off += (size_t)kVtReplicas * nc * kVtReplicaStride * sizeof(unsigned long long);
+  l.n_zero_words = (int)(off / sizeof(unsigned));
+  l.partial = off;
+  off = align_up(off + (size_t)nc * H * nst * sizeof(float), 256);
+  l.total = off;
+  return l;
 }
 
-__device__ __forceinline__ float wave_max_f(float m) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  return m;
+struct VtTile {
+  int stats;          // 1: statistics tile, 0: quantize tile
+  int c, h, j, cg;    // chunk, head, tile within (chunk, head), channel group
+};
+
+// Workgroup index -> tile.  Segment s holds H * nst statistics tiles of
+// chunk s (if s < nc), then tpc * H * ncg quantize tiles of chunk s - depth.
+__device__ __forceinline__ VtTile vt_decode(const VtParams& p, unsigned b) {
+  const unsigned NS = (unsigned)p.H * p.nst, NQ = (unsigned)p.tpc * p.H * p.ncg;
+  int s = 0;
+  unsigned ns = 0, nq = 0;
+  for (; s < p.nc + p.depth; ++s) {
+    ns = s < p.nc ? NS : 0u;
+    nq = (s >= p.depth && s - p.depth < p.nc) ? NQ : 0u;
+    if (b < ns + nq) break;
+    b -= ns + nq;
+  }
+  VtTile t;
+  t.stats = b < ns;
+  if (t.stats) {
+    t.c = s; t.h = (int)(b / p.nst); t.j = (int)(b % p.nst); t.cg = 0;
+  } else {
+    unsigned i = b - ns;
+    t.c = s - p.depth;
+    t.cg = (int)(i % p.ncg); i /= p.ncg;
+    t.h = (int)(i % p.H);
+    t.j = (int)(i / p.H);
+  }
+  return t;
 }
 
-// Partial maximum |V| per (chunk, 128-token tile, head): the tile's rows,
-// all channels, are one contiguous run, streamed with 16-byte loads.
-// partial[(c * tpc + j) * H + h].
-__global__ __launch_bounds__(kVtThreads) void vt_max_kernel(const uint16_t* v, VtGeom g, float* partial) {
-  __shared__ float shw[kVtThreads / 64];
-  const int h = blockIdx.x % g.H, jc = blockIdx.x / g.H, j = jc % g.tpc, c = jc / g.tpc;
-  const int t0 = c * g.L + j * kVtTok;
-  const int ntok = min(kVtTok, (c + 1) * g.L - t0);
-  const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)h * g.T + t0) * g.D);
-  const int n16 = ntok * g.D / 8;  // 16-byte pieces of the run
+// Statistics tile: the largest |V| of rows j * 512 .. of head h in chunk c
+// (one contiguous run, 16-byte loads, eight in flight per lane).  The last
+// tile of the chunk sets the tensor scales and raises the ready words.
+__device__ void vt_stats_tile(const VtParams& p, int c, int h, int j, float* shw, unsigned* sh_flag) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r0 = j * kVsRows;
+  const int nr = min(kVsRows, p.L - r0);
+  const uint4* src = reinterpret_cast<const uint4*>(p.v + ((size_t)h * p.T + (size_t)c * p.L + r0) * p.D);
+  const int n16 = nr * p.D / 8;
   float m = 0.0f;
-  // eight loads in flight per lane, then their maxima
   for (int base = 0; base < n16; base += 8 * kVtThreads) {
     uint4 a[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int i = base + u * kVtThreads + threadIdx.x;
+      const int i = base + u * kVtThreads + tid;
       a[u] = i < n16 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
@@ -72,55 +127,70 @@ __global__ __launch_bounds__(kVtThreads) void vt_max_kernel(const uint16_t* v, V
                          fmaxf(fabsf(bf16_lo(a[u].w)), fabsf(bf16_hi(a[u].w)))));
     }
   }
-  m = wave_max_f(m);
-  if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = m;
+  m = wave_max(m);
+  if (lane == 0) shw[wv] = m;
   __syncthreads();
-  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(shw[0], shw[1]), fmaxf(shw[2], shw[3]));
-}
-
-// One workgroup per chunk: A = the chunk's largest |V|; writes its bits
-// (for the quantize pass) and g_dec = A / C.
-__global__ __launch_bounds__(kVtThreads) void vt_reduce_kernel(const float* partial, VtGeom g, float C,
-                                                               uint32_t* amax_bits, float* tensor_scale) {
-  __shared__ float shw[kVtThreads / 64];
-  const long long per_chunk = (long long)g.tpc * g.H;
-  const float* p = partial + blockIdx.x * per_chunk;
-  float m = 0.0f;
-  for (long long i = threadIdx.x; i < per_chunk; i += blockDim.x) m = fmaxf(m, p[i]);
-  m = wave_max_f(m);
-  if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = m;
+  const unsigned per_chunk = (unsigned)p.H * p.nst;
+  if (tid == 0) {
+    uint32_t done = 0;
+    publish(&p.partial[((size_t)c * p.H + h) * p.nst + j], fmaxf(fmaxf(shw[0], shw[1]), fmaxf(shw[2], shw[3])), done);
+    wait_published(done);
+    *sh_flag = add_agent(&p.err[1 + c], 1u) == per_chunk - 1;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const float A = fmaxf(fmaxf(shw[0], shw[1]), fmaxf(shw[2], shw[3]));
-    amax_bits[blockIdx.x] = __float_as_uint(A);
-    tensor_scale[blockIdx.x] = A / C;
+  if (!*sh_flag) return;
+  float A = 0.0f;
+  for (unsigned i = tid; i < per_chunk; i += kVtThreads) A = fmaxf(A, fetch(&p.partial[(size_t)c * per_chunk + i]));
+  A = wave_max(A);
+  if (lane == 0) shw[wv] = A;
+  __syncthreads();
+  if (tid < kVtReplicas) {
+    const float Am = fmaxf(fmaxf(shw[0], shw[1]), fmaxf(shw[2], shw[3]));
+    const float g = Am > 0.0f ? p.C / Am : 0.0f;
+    if (tid == 0) p.tscale[c] = Am / p.C;  // output only: visible at kernel end
+    (void)__hip_atomic_exchange(p.ready + ((size_t)tid * p.nc + c) * kVtReplicaStride,
+                                (1ull << 32) | __float_as_uint(g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Quantize pass: the tile (up to 128 tokens x 64 channels) through LDS; lane
-// t takes the channel pair 2 (t % 32), +1 and the 16-token block t / 32, so
-// that one 4-byte LDS read serves two blocks.
+// Quantize tile: the tile (up to 128 tokens x 64 channels) through LDS --
+// staged before the wait for the chunk's scale, since V is an input; then
+// lane t takes the channel pair 2 (t % 32), +1 and the 16-token block t / 32,
+// so that one 4-byte LDS read serves two blocks.
 template <int MODE>
-__global__ __launch_bounds__(kVtThreads) void vt_quant_kernel(const uint16_t* v, VtGeom g,
-                                                              const uint32_t* amax_bits, uint8_t* codes,
-                                                              uint8_t* scales) {
-  __shared__ float2 sh_tab[128];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kVtTok * kVtRow];
-  fill_scale_table(sh_tab);
-  int c, j, h, cg;
-  vt_tile(g, blockIdx.x, c, j, h, cg);
-  const int t0 = c * g.L + j * kVtTok;
-  const int ntok = min(kVtTok, (c + 1) * g.L - t0);
-  for (int r = threadIdx.x >> 3; r < ntok; r += kVtThreads / 8) {
-    const uint4 a = *reinterpret_cast<const uint4*>(v + ((size_t)h * g.T + t0 + r) * g.D + cg * kVtCh +
-                                                    8 * (threadIdx.x & 7));
-    *reinterpret_cast<uint4*>(tile + r * kVtRow + 16 * (threadIdx.x & 7)) = a;
+__device__ void vt_quant_tile(const VtParams& p, int c, int j, int h, int cg, uint8_t* tile, const float2* tab,
+                              float* shw, unsigned* sh_flag) {
+  const int tid = threadIdx.x;
+  const int t0 = c * p.L + j * kVtTok;
+  const int ntok = min(kVtTok, (c + 1) * p.L - t0);
+  for (int r = tid >> 3; r < ntok; r += kVtThreads / 8) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p.v + ((size_t)h * p.T + t0 + r) * p.D + cg * kVtCh +
+                                                    8 * (tid & 7));
+    *reinterpret_cast<uint4*>(tile + r * kVtRow + 16 * (tid & 7)) = a;
   }
-  __syncthreads();
-  const int cp = threadIdx.x & 31, tb = threadIdx.x >> 5;  // channel pair, 16-token block
+  if (tid == 0) {
+    const unsigned long long* rw = p.ready + ((size_t)(blockIdx.x % kVtReplicas) * p.nc + c) * kVtReplicaStride;
+    unsigned long long w = __hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned it = 0;
+    bool ok = true;
+    while ((w >> 32) == 0ull) {
+      ++it;
+      if (it > p.spin_limit || ((it & 255u) == 0u && load_agent(p.err) != 0u)) {
+        atomicOr(p.err, 1u);
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(32);  // about 1 us: every poll is a device-scope access to a shared word
+      w = __hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *sh_flag = ok ? 1u : 0u;
+    shw[0] = __uint_as_float((uint32_t)w);
+  }
+  __syncthreads();  // the tile, the scale table and the chunk's scale
+  if (!*sh_flag) return;
+  const int cp = tid & 31, tb = tid >> 5;  // channel pair, 16-token block
   if (16 * tb >= ntok) return;
-  const float A = __uint_as_float(amax_bits[c]);
-  const float gz = A > 0.0f ? mode_constant(MODE) / A : 0.0f;
+  const float gz = shw[0];
   float z0[16], z1[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -128,15 +198,35 @@ __global__ __launch_bounds__(kVtThreads) void vt_quant_kernel(const uint16_t* v,
     z0[i] = bf16_lo(w) * gz;
     z1[i] = bf16_hi(w) * gz;
   }
-  const size_t row = (size_t)h * g.D + cg * kVtCh + 2 * cp;  // output row (head, channel) of z0
-  const size_t blk = row * (g.T / 16) + (t0 / 16) + tb;      // block index along that row
-  const Block46 q0 = quant_block16<MODE>(z0, sh_tab);
-  *reinterpret_cast<uint2*>(codes + blk * 8) = make_uint2(q0.lo, q0.hi);
-  scales[blk] = (uint8_t)q0.scale;
-  const Block46 q1 = quant_block16<MODE>(z1, sh_tab);
-  const size_t blk1 = blk + g.T / 16;
-  *reinterpret_cast<uint2*>(codes + blk1 * 8) = make_uint2(q1.lo, q1.hi);
-  scales[blk1] = (uint8_t)q1.scale;
+  const size_t row = (size_t)h * p.D + cg * kVtCh + 2 * cp;  // output row (head, channel) of z0
+  const size_t blk = row * (p.T / 16) + (t0 / 16) + tb;      // block index along that row
+  const Block46 q0 = quant_block16<MODE>(z0, tab);
+  *reinterpret_cast<uint2*>(p.codes + blk * 8) = make_uint2(q0.lo, q0.hi);
+  p.scales[blk] = (uint8_t)q0.scale;
+  const Block46 q1 = quant_block16<MODE>(z1, tab);
+  const size_t blk1 = blk + p.T / 16;
+  *reinterpret_cast<uint2*>(p.codes + blk1 * 8) = make_uint2(q1.lo, q1.hi);
+  p.scales[blk1] = (uint8_t)q1.scale;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kVtThreads) void vt_kernel(VtParams p) {
+  __shared__ float2 sh_tab[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kVtTok * kVtRow];
+  __shared__ float shw[kVtThreads / 64];
+  __shared__ unsigned sh_flag;
+  const VtTile t = vt_decode(p, blockIdx.x);
+  if (t.stats) {
+    vt_stats_tile(p, t.c, t.h, t.j, shw, &sh_flag);
+  } else {
+    fill_scale_table(sh_tab);
+    vt_quant_tile<MODE>(p, t.c, t.j, t.h, t.cg, tile, sh_tab, shw, &sh_flag);
+  }
+}
+
+__global__ void vt_zero_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 }  // namespace
@@ -147,9 +237,8 @@ using namespace nvfp4;
 extern "C" NVFP4KV_API size_t nvfp4_kv_quantize_v_tblocks_workspace_bytes(int H, int T, int D,
                                                                           int chunk_len) noexcept {
   if (H < 1 || T < 1 || D < kVtCh || D % kVtCh || chunk_len < 16 || chunk_len % 16 || T % chunk_len) return 0;
-  const long long nc = T / chunk_len, tpc = (chunk_len + kVtTok - 1) / kVtTok;
-  const long long ntiles = nc * tpc * H * (D / kVtCh);
-  return align_up((size_t)ntiles * 4, 256) + align_up((size_t)nc * 4, 256);
+  const int nc = T / chunk_len, nst = (chunk_len + kVsRows - 1) / kVsRows;
+  return vt_layout(H, nc, nst).total;
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H, int T, int D, int chunk_len,
@@ -167,33 +256,35 @@ extern "C" NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H,
   const size_t need = nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, chunk_len);
   if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   const size_t n = (size_t)H * T * D;
-  VtGeom g{};
-  g.H = H; g.T = T; g.D = D; g.L = chunk_len; g.nc = T / chunk_len;
-  g.tpc = (chunk_len + kVtTok - 1) / kVtTok;
-  g.ncg = D / kVtCh;
-  g.ntiles = (long long)g.nc * g.tpc * H * g.ncg;
-  if (g.ntiles >= (1LL << 31)) return NVFP4_ERR_SHAPE;
+  VtParams p{};
+  p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.nc = T / chunk_len;
+  p.tpc = (chunk_len + kVtTok - 1) / kVtTok;
+  p.ncg = D / kVtCh;
+  p.nst = (chunk_len + kVsRows - 1) / kVsRows;
+  p.depth = kVtDepth;
+  p.spin_limit = kVtSpinLimit;
+  p.C = mode_constant(mode);
+  // work-items of the launch and tile indices stay in 32 bits; a statistics
+  // run (512 rows) in 31-bit element offsets
+  const long long grid = (long long)p.nc * H * ((long long)p.nst + (long long)p.tpc * p.ncg);
+  if (grid >= (1LL << 24) || (long long)kVsRows * D >= (1LL << 31)) return NVFP4_ERR_SHAPE;
   const Range in[1] = {range_of(v, n * 2)};
-  const Range outr[4] = {range_of(codes, n / 2), range_of(scales, n / 16), range_of(tensor_scale, (size_t)g.nc * 4),
+  const Range outr[4] = {range_of(codes, n / 2), range_of(scales, n / 16), range_of(tensor_scale, (size_t)p.nc * 4),
                          range_of(workspace, need)};
   if (any_alias(in, 1, outr, 4)) return NVFP4_ERR_ALIAS;
-  float* partial = static_cast<float*>(workspace);
-  uint32_t* amax = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + align_up((size_t)g.ntiles * 4, 256));
+  const VtLayout l = vt_layout(H, p.nc, p.nst);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.v = v; p.codes = codes; p.scales = scales; p.tscale = tensor_scale;
+  p.err = reinterpret_cast<unsigned*>(ws);
+  p.ready = reinterpret_cast<unsigned long long*>(ws + l.ready);
+  p.partial = reinterpret_cast<float*>(ws + l.partial);
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  vt_max_kernel<<<dim3((unsigned)(g.ntiles / g.ncg)), dim3(kVtThreads), 0, s>>>(v, g, partial);
-  vt_reduce_kernel<<<dim3((unsigned)g.nc), dim3(kVtThreads), 0, s>>>(partial, g, mode_constant(mode), amax,
-                                                                      tensor_scale);
+  vt_zero_kernel<<<dim3((unsigned)((l.n_zero_words + 255) / 256)), dim3(256), 0, s>>>(p.err, l.n_zero_words);
   switch (mode) {
-    case kModeFixed6:
-      vt_quant_kernel<kModeFixed6><<<dim3((unsigned)g.ntiles), dim3(kVtThreads), 0, s>>>(v, g, amax, codes, scales);
-      break;
-    case kModeFixed4:
-      vt_quant_kernel<kModeFixed4><<<dim3((unsigned)g.ntiles), dim3(kVtThreads), 0, s>>>(v, g, amax, codes, scales);
-      break;
-    default:
-      vt_quant_kernel<kMode4over6><<<dim3((unsigned)g.ntiles), dim3(kVtThreads), 0, s>>>(v, g, amax, codes, scales);
-      break;
+    case kModeFixed6: vt_kernel<kModeFixed6><<<dim3((unsigned)grid), dim3(kVtThreads), 0, s>>>(p); break;
+    case kModeFixed4: vt_kernel<kModeFixed4><<<dim3((unsigned)grid), dim3(kVtThreads), 0, s>>>(p); break;
+    default: vt_kernel<kMode4over6><<<dim3((unsigned)grid), dim3(kVtThreads), 0, s>>>(p); break;
   }
   return launch_status();
 }

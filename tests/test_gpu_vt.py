@@ -1,7 +1,10 @@
 """GPU parity of nvfp4_kv_quantize_v_tblocks (V blocked along tokens) with the
 oracle: codes, scales and tensor scales bit-exact, for every mode, ragged
 tiles (chunks that are not a multiple of the 128-token tile), several channel
-groups, heavy-tailed values and the one-chunk workload."""
+groups, several 512-row statistics tiles per head with a ragged last one,
+more chunks than the launch's statistics-to-quantize distance, heavy-tailed
+values and the one-chunk workload; after every call the kernel's error word
+(no wait timed out) is checked."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +27,7 @@ def _run(vb, L, mode):
                     dtype=torch.uint8, device="cuda")
     P.nvfp4_kv_quantize_v_tblocks(v, L, mode, out=out, workspace=ws)
     torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0, "a wait of the single-launch kernel timed out"
     return {k: t.cpu().numpy() for k, t in out.items()}
 
 
@@ -36,7 +40,7 @@ def _compare(got, ref):
 
 
 @pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
-@pytest.mark.parametrize("H,T,D,L", [(2, 256, 128, 128), (3, 352, 64, 176), (1, 96, 192, 48)])
+@pytest.mark.parametrize("H,T,D,L", [(2, 256, 128, 128), (3, 352, 64, 176), (1, 96, 192, 48), (2, 4160, 128, 1040)])
 def test_gaussian(H, T, D, L, mode):
     say("v tblocks", H, T, D, L, mode)
     _, v = W.gaussian_kv(W.KVShape(H, T, D, L), 60 + T)
