@@ -92,36 +92,31 @@ struct TileRegs {
   uint32_t vscale[4];
 };
 
-// Thread roles for a tile, chosen so that the LDS writes of a wave hit
-// distinct banks: K -- key tid % 64, block tid / 64 (16 dims; eight lanes
-// write eight consecutive padded rows); V -- keys 4 (tid % 16) .. +3, dims
-// 4 (tid / 16) .. +3 (sixteen lanes write the sixteen 8-byte slots of one
-// V^T row).
+// Thread roles for a tile.  K -- key tid / 8, block tid % 8 (16 dims): the
+// eight lanes of a key read its 64 contiguous code bytes, and a wave covers
+// eight consecutive keys.  V -- keys 4 (tid % 16) .. +3, dims 4 (tid / 16)
+// .. +3, so that sixteen lanes write the sixteen 8-byte slots of one V^T row
+// (distinct banks).  Keys past the tile's end (n >= 1) load the tile's last
+// key instead, so the loads need no branches; those keys' logits are set to
+// -inf and their weights to 0 after the products, and their values are
+// finite, so they add nothing.
 __device__ __forceinline__ void load_tile(const AttnParams& p, int kvh, int start, int n, TileRegs& t) {
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)kvh * p.hstride + (size_t)(start / p.L) * p.cstride + start % p.L;
   {
-    const int kk = tid & 63, b = tid >> 6;
-    t.k0 = t.k1 = 0u;
-    t.kscale = 0u;
-    if (kk < n) {
-      const uint2 c = *reinterpret_cast<const uint2*>(p.kc + (row0 + kk) * (kD / 2) + 8 * b);
-      t.k0 = c.x;
-      t.k1 = c.y;
-      t.kscale = p.ks[(row0 + kk) * (kD / 16) + b];
-    }
+    const int kk = min(tid >> 3, n - 1), b = tid & 7;
+    const uint2 c = *reinterpret_cast<const uint2*>(p.kc + (row0 + kk) * (kD / 2) + 8 * b);
+    t.k0 = c.x;
+    t.k1 = c.y;
+    t.kscale = p.ks[(row0 + kk) * (kD / 16) + b];
   }
   {
     const int a = tid & 15, c = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kk = 4 * a + i;
-      t.v[i] = 0u;
-      t.vscale[i] = 0u;
-      if (kk < n) {
-        t.v[i] = *reinterpret_cast<const uint16_t*>(p.vc + (row0 + kk) * (kD / 2) + 2 * c);
-        t.vscale[i] = p.vs[(row0 + kk) * (kD / 16) + (c >> 2)];
-      }
+      const int kk = min(4 * a + i, n - 1);
+      t.v[i] = *reinterpret_cast<const uint16_t*>(p.vc + (row0 + kk) * (kD / 2) + 2 * c);
+      t.vscale[i] = p.vs[(row0 + kk) * (kD / 16) + (c >> 2)];
     }
   }
 }
@@ -133,12 +128,11 @@ __device__ __forceinline__ f32x2 fp4x2(uint32_t w) {
 }
 
 // Decode the tile's registers into LDS buffer `buf`: K~ = v * S (exact in
-// bf16), V~ = bf16(v * S * gv).  Keys past the tile's end are zeros (their
-// codes and scales were loaded as 0).
+// bf16), V~ = bf16(v * S * gv).
 __device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& t, float gv) {
   const int tid = threadIdx.x;
   {
-    const int kk = tid & 63, b = tid >> 6;
+    const int kk = tid >> 3, b = tid & 7;
     const float f = __builtin_amdgcn_cvt_f32_fp8(t.kscale, 0);
     f32x2 x[8];
     x[0] = fp4x2<0>(t.k0); x[1] = fp4x2<1>(t.k0); x[2] = fp4x2<2>(t.k0); x[3] = fp4x2<3>(t.k0);
