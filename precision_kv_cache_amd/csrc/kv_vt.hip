@@ -56,7 +56,7 @@ struct VtParams {
 // Workspace: error word and counters, ready words, partial maxima.
 struct VtLayout {
   size_t ready, partial, total;
-  int n_zero_words;  // error word .. end of the ready words, cleared before the launch
+  size_t n_zero_words;  // error word .. end of the ready words, cleared before the launch
 };
 
 VtLayout vt_layout(int H, int nc, int nst) {
@@ -64,7 +64,7 @@ VtLayout vt_layout(int H, int nc, int nst) {
   size_t off = align_up((size_t)(1 + nc) * sizeof(unsigned), 256);
   l.ready = off;
   off += (size_t)kVtReplicas * nc * kVtReplicaStride * sizeof(unsigned long long);
-  l.n_zero_words = (int)(off / sizeof(unsigned));
+  l.n_zero_words = off / sizeof(unsigned);
   l.partial = off;
   off = align_up(off + (size_t)nc * H * nst * sizeof(float), 256);
   l.total = off;
@@ -224,9 +224,9 @@ __global__ __launch_bounds__(kVtThreads) void vt_kernel(VtParams p) {
   }
 }
 
-__global__ void vt_zero_kernel(unsigned* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// grid-stride, so that any count is cleared by a bounded grid
+__global__ void vt_zero_kernel(unsigned* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 }  // namespace
@@ -280,7 +280,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H,
   p.partial = reinterpret_cast<float*>(ws + l.partial);
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  vt_zero_kernel<<<dim3((unsigned)((l.n_zero_words + 255) / 256)), dim3(256), 0, s>>>(p.err, l.n_zero_words);
+  const size_t zb = (l.n_zero_words + 255) / 256;
+  vt_zero_kernel<<<dim3((unsigned)(zb < 4096 ? zb : 4096)), dim3(256), 0, s>>>(p.err, l.n_zero_words);
   switch (mode) {
     case kModeFixed6: vt_kernel<kModeFixed6><<<dim3((unsigned)grid), dim3(kVtThreads), 0, s>>>(p); break;
     case kModeFixed4: vt_kernel<kModeFixed4><<<dim3((unsigned)grid), dim3(kVtThreads), 0, s>>>(p); break;

@@ -200,6 +200,10 @@ def test_v_tblocks_argument_errors():
     assert f(*args(codes=FAKE + 64)) == ALIAS
     assert f(*args(H=0)) == OK
     assert L.nvfp4_kv_quantize_v_tblocks_workspace_bytes(2, 256, 128, 100) == 0
+    # a million 16-token chunks: 32 ready words of 256 bytes per chunk, so the
+    # size passes 2^33 bytes and must come back whole (no 32-bit wrap)
+    big = L.nvfp4_kv_quantize_v_tblocks_workspace_bytes(1, 1 << 24, 64, 16)
+    assert big >= (1 << 20) * 32 * 256
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
