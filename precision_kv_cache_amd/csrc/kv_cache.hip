@@ -149,6 +149,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_cache_append(const nvfp4_kv_cache_t* c, void
   if (c->pending < 0 || layer < 0 || layer >= c->layers ||
       !geometry_ok(c->heads, c->head_dim, c->chunk_len, c->capacity))
     return NVFP4_ERR_SHAPE;
+  // the state is caller memory: a slot outside the storage is refused, not written
+  if (c->pending_slot < 0 || c->pending_slot >= c->capacity) return NVFP4_ERR_SHAPE;
   if (!aligned(storage, 256)) return NVFP4_ERR_ALIGN;
   const LayerLayout l = layout_of(c);
   if (storage_bytes < l.bytes * (size_t)c->layers) return NVFP4_ERR_SHAPE;

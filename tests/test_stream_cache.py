@@ -99,5 +99,10 @@ def test_cache_argument_errors():
                                    None) == SHAPE                             # storage too small
     assert L.nvfp4_kv_cache_append(s, ctypes.c_void_p(0x7f0000000010), 1 << 30, 0, None, None, 0, None, 0,
                                    None) == -3                                # storage not 256-byte aligned
+    good = st.pending_slot
+    st.pending_slot = 8                                                       # a corrupted state: past the slots
+    assert L.nvfp4_kv_cache_append(s, ctypes.c_void_p(0x7f0000000000), 1 << 30, 0, None, None, 0, None, 0,
+                                   None) == SHAPE
+    st.pending_slot = good
     assert L.nvfp4_kv_cache_end_chunk(s) == OK
     assert L.nvfp4_kv_cache_layer_bytes(1, 128, 64, 0) == 0
