@@ -36,7 +36,10 @@
  *     mutable global state.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     stream-ordered and asynchronous: a return of NVFP4_OK means the work
- *     was enqueued.
+ *     was enqueued.  They enqueue kernels only (workspace counters are
+ *     cleared by a kernel, never a memset), so they may be captured into a
+ *     HIP graph and replayed; a replay reuses the captured workspace, so
+ *     replays and other calls on that workspace must not overlap in time.
  *   - Argument errors return a negative status before any HIP call and with
  *     no side effects.  A launch failure returns NVFP4_ERR_HIP.  Nothing
  *     throws across the ABI.

@@ -175,6 +175,15 @@ def nvfp4_dequantize(codes, scales, tensor_scale, mean, chunk_len, out=None, str
 ATTN_MAX_RANGES = 8
 
 
+def _lse_out(lse, H, Tq, device):
+    """lse argument -> the fp32 [H, Tq] output tensor, or None."""
+    if isinstance(lse, torch.Tensor):
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (H, Tq) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous fp32 [H, Tq] tensor")
+        return lse
+    return torch.empty(H, Tq, dtype=torch.float32, device=device) if lse else None
+
+
 def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False, stream=None):
     """Softmax attention of q (bf16 [H, Tq, D]) over the keys listed in
     key_ranges ([(start, len), ...], at most ATTN_MAX_RANGES) of an NVFP4
@@ -182,7 +191,7 @@ def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=
     k_tensor_scale, k_mean (may be None), v_codes, v_scales, v_tensor_scale),
     for H_kv heads with H % H_kv == 0.  softmax_scale defaults to 1/sqrt(D).
     Returns out (bf16 [H, Tq, D]), or (out, lse fp32 [H, Tq]) when lse is
-    True."""
+    True or a preallocated fp32 [H, Tq] tensor (written in place)."""
     _bf16_dev(q, "q")
     if q.dim() != 3:
         raise ValueError("q must be [H, Tq, D]")
@@ -195,13 +204,13 @@ def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=
     arr = (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
     if out is None:
         out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
-    lse_t = torch.empty(H, Tq, dtype=torch.float32, device=q.device) if lse else None
+    lse_t = _lse_out(lse, H, Tq, q.device)
     rc = lib().nvfp4_kv_attention(
         _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
         _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, T, chunk_len, arr,
         len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
     _check(rc, "nvfp4_kv_attention")
-    return (out, lse_t) if lse else out
+    return (out, lse_t) if lse_t is not None else out
 
 
 def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False,
@@ -221,13 +230,13 @@ def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=No
     arr = (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
     if out is None:
         out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
-    lse_t = torch.empty(H, Tq, dtype=torch.float32, device=q.device) if lse else None
+    lse_t = _lse_out(lse, H, Tq, q.device)
     rc = lib().nvfp4_kv_attention_chunked(
         _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
         _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, nch * L, chunk_len, arr,
         len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
     _check(rc, "nvfp4_kv_attention_chunked")
-    return (out, lse_t) if lse else out
+    return (out, lse_t) if lse_t is not None else out
 
 
 def nvfp4_gemm_w4a4(a, w, w_2d, out=None, stream=None):
