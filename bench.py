@@ -94,10 +94,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
-    ap.add_argument("--op", choices=("kv", "attention", "stream", "gemm", "vt"), default="kv",
+    ap.add_argument("--op", choices=("kv", "attention", "stream", "gemm", "vt", "act", "weight"), default="kv",
                     help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache; "
                          "stream: the streaming cache (attention + append per layer); gemm: the W4A4 GEMM; "
-                         "vt: V blocked along tokens")
+                         "vt: V blocked along tokens; act: the activation quantizer (RHT + 1D blocks); "
+                         "weight: the weight quantizer (2D tiles)")
     ap.add_argument("--layout", choices=("all", "sink"), default="all",
                     help="attention key set: every cache key, or the sink layout (global sink, shot sink, window)")
     return ap.parse_args()
@@ -132,6 +133,9 @@ def main():
         return
     if a.op == "vt":
         vt_bench(a)
+        return
+    if a.op in ("act", "weight"):
+        act_weight_bench(a)
         return
 
     import torch
@@ -709,6 +713,107 @@ def gemm_bench(a):
                                   "cores": nt, "kind": "oracle",
                                   "sample": f"{done} random rows of the activation x the whole weight (fp64 over "
                                             f"the exactly decoded operands)", "seconds": round(t_cpu, 2)}
+    print(json.dumps(result), flush=True)
+
+
+AW_METRIC = {
+    "act": "activation quantize (16-point RHT + 1D NVFP4 4/6 blocks): GB/s (bytes in + out) and % of MI355X HBM peak",
+    "weight": "weight quantize (2D 16x16 NVFP4 4/6 tiles): GB/s (bytes in + out) and % of MI355X HBM peak",
+}
+
+
+def act_weight_bench(a):
+    """The GEMM-operand quantizers on their workload: the activation
+    [16384, 3072] with the RHT and 1D blocks (--op act), or the weight
+    [3072, 3072] with 2D tiles (--op weight).  Each step quantizes the next of
+    several seeded input copies (at least 400 MB in all), so no call finds its
+    input in the 256 MB Infinity Cache."""
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    x, sign_mask, w = W.act_weight(device=dev)
+    act = a.op == "act"
+    src = x if act else w
+    del x, w
+    copies = [src] + [src.clone() for _ in range((4 if act else 22) - 1)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    rows, cols = src.shape
+    n = src.numel()
+    ws = torch.empty(int((P.lib().nvfp4_quantize_1d_workspace_bytes if act else
+                          P.lib().nvfp4_quantize_2d_workspace_bytes)(rows, cols)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    if act:
+        out = P.nvfp4_quantize_1d(src, a.mode, hadamard=True, sign_mask=sign_mask)
+        call = lambda i: P.nvfp4_quantize_1d(copies[i % len(copies)], a.mode, hadamard=True,  # noqa: E731
+                                             sign_mask=sign_mask, out=out, workspace=ws, stream=stream)
+        nbytes = 2 * n + n // 2 + n // 16 + 4
+    else:
+        out = P.nvfp4_quantize_2d(src, a.mode)
+        call = lambda i: P.nvfp4_quantize_2d(copies[i % len(copies)], a.mode, out=out, workspace=ws,  # noqa: E731
+                                             stream=stream)
+        nbytes = 2 * n + n // 2 + n // 256 + 4
+    for i in range(a.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    # the calls run back to back on one stream (each is GPU-bound: a HIP
+    # graph replay of the same steps measured within 3 %); one event pair
+    # around all of them, none between calls, so the host never paces them
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, stop = E(), E()
+    start.record(stream)
+    for i in range(a.steps):
+        call(a.warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / a.steps
+    call_ms = ms_step
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    call_gbps = gbps
+    kind = "activation [16384, 3072] with the 16-point RHT, 1D blocks" if act else "weight [3072, 3072], 2D 16x16 tiles"
+    result = {
+        "metric": AW_METRIC[a.op], "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"NVFP4 4/6 quantize of a bf16 {kind}, one tensor scale; "
+                               f"{len(copies)} input copies rotated",
+                   "rows": rows, "cols": cols, "mode": ["4over6", "fixed6", "fixed4"][a.mode],
+                   "bytes_per_step": nbytes},
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm",
+                     "kernel": ("nvfp4_quantize_1d, hadamard (amax, reduce, quantize kernels)" if act else
+                                "nvfp4_quantize_2d (amax, reduce, quantize kernels)"),
+                     "achieved": round(call_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(call_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes},
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        import oracle as O
+        nt = O.default_threads()
+        step = 1024 if act else 3072  # rows per oracle call
+        done, t_cpu = 0, 0.0
+        while t_cpu < a.cpu_seconds and done < rows:
+            xb = W.bf16_bits(src[done:done + step])
+            t1 = time.perf_counter()
+            if act:
+                O.quantize_1d(xb, a.mode, True, sign_mask, nthreads=nt)
+            else:
+                O.quantize_2d(xb, a.mode, nthreads=nt)
+            t_cpu += time.perf_counter() - t1
+            done += xb.shape[0]
+        nb = done * cols
+        sample_bytes = 2 * nb + nb // 2 + (nb // 16 if act else nb // 256)
+        result["cpu_baseline"] = {"value": round(sample_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": nt,
+                                  "kind": "oracle",
+                                  "sample": (f"{done} of {rows} rows, {step} rows per oracle call (each call "
+                                             "with its own tensor scale)" if act else f"the whole {rows} x {cols} weight"),
+                                  "seconds": round(t_cpu, 2)}
     print(json.dumps(result), flush=True)
 
 
