@@ -430,9 +430,12 @@ def attention_bench(a):
     ranges = [(0, T)] if a.layout == "all" else W.sink_ranges(s.n_chunks)
     nk = sum(n for _, n in ranges)
     out = torch.empty_like(q)
+    # workspace that lets the call split each query block's keys over several
+    # workgroups (and merge them) where that fills the CUs better
+    aws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(H, Tq, D), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for _ in range(a.warmup):
-        P.nvfp4_kv_attention(q, cache, L, ranges, out=out, stream=stream)
+        P.nvfp4_kv_attention(q, cache, L, ranges, out=out, workspace=aws, stream=stream)
     torch.cuda.synchronize()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     ev = [(E(), E()) for _ in range(a.steps)]
@@ -440,7 +443,7 @@ def attention_bench(a):
     start.record(stream)
     for i in range(a.steps):
         ev[i][0].record(stream)
-        P.nvfp4_kv_attention(q, cache, L, ranges, out=out, stream=stream)
+        P.nvfp4_kv_attention(q, cache, L, ranges, out=out, workspace=aws, stream=stream)
         ev[i][1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
@@ -536,7 +539,10 @@ def stream_bench(a):
         for l in range(nl):
             if att_ev is not None:
                 att_ev[l][0].record(main)
-            cache.attention(l, q, out=out, stream=main)
+            # unsplit (no workspace): the appends on the side stream fill the CUs
+            # that attention's last round of workgroups leaves idle, which key
+            # splits would take from them (measured slower here)
+            cache.attention(l, q, out=out, workspace=False, stream=main)
             if att_ev is not None:
                 att_ev[l][1].record(main)
             done[l].record(main)  # the layer's K and V would come out of this layer's forward

@@ -229,19 +229,29 @@ NVFP4KV_API int nvfp4_dequantize_2d(const uint8_t* codes, const uint8_t* scales,
  *   softmax_scale finite and > 0; 1/sqrt(D) is the usual value.
  *   out           out, bf16 [H, Tq, D], 8-byte aligned.  With no keys: 0.
  *   lse           out, nullable fp32 [H, Tq] (natural log); -inf with no keys.
+ *   workspace     nullable, 256-byte aligned, workspace_bytes long: room to
+ *                 split each query block's key list over up to four
+ *                 workgroups (the split fills the GPU's CUs more evenly; a
+ *                 small kernel then merges the partial results per query
+ *                 row).  nvfp4_kv_attention_workspace_bytes() is enough for
+ *                 every split; NULL or less than two splits' worth runs
+ *                 unsplit.  Contents on entry ignored.
  *
  * Arithmetic: K is decoded to v * S, exact in bf16, so the logits are exact
  * up to fp32 accumulation (g_K, the softmax scale and the mean term
  * q . k_mean[c] are applied in fp32 per chunk); V is decoded to
  * bf16(v * S * g_V); P V accumulates in fp32 on the matrix cores with P
- * rounded to bf16, and out is rounded to bf16.
+ * rounded to bf16, and out is rounded to bf16.  With key splits each split
+ * keeps its fp32 sums and reference maximum; the merge rescales them in fp32
+ * and rounds out to bf16 once.
  */
+NVFP4KV_API size_t nvfp4_kv_attention_workspace_bytes(int H, int Tq, int D) NVFP4KV_NOEXCEPT;
 NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
                                    const uint8_t* k_scales, const float* k_tensor_scale, const float* k_mean,
                                    const uint8_t* v_codes, const uint8_t* v_scales, const float* v_tensor_scale,
                                    int H_kv, int T, int chunk_len, const int* key_ranges, int n_ranges,
-                                   float softmax_scale, uint16_t* out, float* lse,
-                                   void* stream) NVFP4KV_NOEXCEPT;
+                                   float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) NVFP4KV_NOEXCEPT;
 
 /*
  * The same attention over a chunk-major cache: codes uint8 [T / chunk_len,
@@ -258,7 +268,8 @@ NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, int Tq, int
                                            const float* k_mean, const uint8_t* v_codes, const uint8_t* v_scales,
                                            const float* v_tensor_scale, int H_kv, int T, int chunk_len,
                                            const int* key_ranges, int n_ranges, float softmax_scale,
-                                           uint16_t* out, float* lse, void* stream) NVFP4KV_NOEXCEPT;
+                                           uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                           void* stream) NVFP4KV_NOEXCEPT;
 
 /*
  * W4A4 GEMM on NVFP4 operands (training pipeline, step 4: weights with 2D
@@ -413,10 +424,12 @@ NVFP4KV_API int nvfp4_kv_cache_key_ranges(const nvfp4_kv_cache_t* c, int* ranges
 
 /* Attention of q (bf16 [Hq, Tq, head_dim], Hq a multiple of heads) over the
  * committed key set of one layer: nvfp4_kv_attention_chunked with that
- * layer's slot arrays, T = capacity * chunk_len and the ranges above. */
+ * layer's slot arrays, T = capacity * chunk_len and the ranges above
+ * (workspace as there: nullable). */
 NVFP4KV_API int nvfp4_kv_cache_attention(const nvfp4_kv_cache_t* c, const void* storage, size_t storage_bytes,
                                          int layer, const uint16_t* q, int Hq, int Tq, float softmax_scale,
-                                         uint16_t* out, float* lse, void* stream) NVFP4KV_NOEXCEPT;
+                                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) NVFP4KV_NOEXCEPT;
 
 #ifdef __cplusplus
 }

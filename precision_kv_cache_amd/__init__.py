@@ -16,6 +16,7 @@ __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
+    "nvfp4_kv_attention_workspace_bytes",
     "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_kv_quantize_v_tblocks", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
@@ -52,9 +53,11 @@ def lib():
             "nvfp4_quantize_1d": (i, [P, i, i, i, i, u32, P, P, P, P, sz, P]),
             "nvfp4_quantize_2d": (i, [P, i, i, i, P, P, P, P, sz, P]),
             "nvfp4_dequantize_2d": (i, [P, P, P, i, i, P, P]),
-            "nvfp4_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P, P]),
+            "nvfp4_kv_attention_workspace_bytes": (sz, [i, i, i]),
+            "nvfp4_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P, P, sz,
+                                       P]),
             "nvfp4_kv_attention_chunked": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P,
-                                               P]),
+                                               P, sz, P]),
             "nvfp4_gemm_w4a4": (i, [P, P, P, i, i, P, P, P, i, i, P, P]),
             "nvfp4_kv_quantize_v_tblocks_workspace_bytes": (sz, [i, i, i, i]),
             "nvfp4_kv_quantize_v_tblocks": (i, [P, i, i, i, i, i, P, P, P, P, sz, P]),
@@ -65,7 +68,7 @@ def lib():
             "nvfp4_kv_cache_append": (i, [P, P, sz, i, P, P, i, P, sz, P]),
             "nvfp4_kv_cache_end_chunk": (i, [P]),
             "nvfp4_kv_cache_key_ranges": (i, [P, P]),
-            "nvfp4_kv_cache_attention": (i, [P, P, sz, i, P, i, i, ctypes.c_float, P, P, P]),
+            "nvfp4_kv_cache_attention": (i, [P, P, sz, i, P, i, i, ctypes.c_float, P, P, P, sz, P]),
             "nvfp4_diag_e2m1_encode": (i, [P, ll, P, P]),
             "nvfp4_diag_candidates": (i, [P, ll, P, P, P]),
             "nvfp4_diag_reciprocal": (i, [P, ll, P, P]),
@@ -175,6 +178,25 @@ def nvfp4_dequantize(codes, scales, tensor_scale, mean, chunk_len, out=None, str
 ATTN_MAX_RANGES = 8
 
 
+def nvfp4_kv_attention_workspace_bytes(H, Tq, D):
+    """Workspace bytes that let an attention call split every query block's
+    key list as far as it helps (0 for an invalid shape)."""
+    return int(lib().nvfp4_kv_attention_workspace_bytes(H, Tq, D))
+
+
+def _attn_workspace(workspace, H, Tq, D, device):
+    """workspace argument -> (tensor or None, bytes): None allocates one big
+    enough for every key split, False runs unsplit, a uint8 tensor is used."""
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        n = nvfp4_kv_attention_workspace_bytes(H, Tq, D)
+        if n == 0:
+            return None, 0
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _lse_out(lse, H, Tq, device):
     """lse argument -> the fp32 [H, Tq] output tensor, or None."""
     if isinstance(lse, torch.Tensor):
@@ -184,14 +206,18 @@ def _lse_out(lse, H, Tq, device):
     return torch.empty(H, Tq, dtype=torch.float32, device=device) if lse else None
 
 
-def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False, stream=None):
+def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False, workspace=None,
+                       stream=None):
     """Softmax attention of q (bf16 [H, Tq, D]) over the keys listed in
     key_ranges ([(start, len), ...], at most ATTN_MAX_RANGES) of an NVFP4
     cache: the dict nvfp4_kv_smooth_quantize returns (k_codes, k_scales,
     k_tensor_scale, k_mean (may be None), v_codes, v_scales, v_tensor_scale),
     for H_kv heads with H % H_kv == 0.  softmax_scale defaults to 1/sqrt(D).
     Returns out (bf16 [H, Tq, D]), or (out, lse fp32 [H, Tq]) when lse is
-    True or a preallocated fp32 [H, Tq] tensor (written in place)."""
+    True or a preallocated fp32 [H, Tq] tensor (written in place).
+    workspace: None allocates one that allows key splits, False runs
+    unsplit, or a uint8 device tensor (at least
+    nvfp4_kv_attention_workspace_bytes for every split)."""
     _bf16_dev(q, "q")
     if q.dim() != 3:
         raise ValueError("q must be [H, Tq, D]")
@@ -205,16 +231,17 @@ def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=
     if out is None:
         out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
     lse_t = _lse_out(lse, H, Tq, q.device)
+    ws, ws_bytes = _attn_workspace(workspace, H, Tq, D, q.device)
     rc = lib().nvfp4_kv_attention(
         _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
         _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, T, chunk_len, arr,
-        len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
+        len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _ptr(ws), ws_bytes, _stream(stream))
     _check(rc, "nvfp4_kv_attention")
     return (out, lse_t) if lse_t is not None else out
 
 
 def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=None, out=None, lse=False,
-                               stream=None):
+                               workspace=None, stream=None):
     """nvfp4_kv_attention over a chunk-major cache: cache arrays [n_chunks,
     H_kv, chunk_len, ...] (each chunk as one quantize call writes it), tensor
     scales [n_chunks], k_mean [n_chunks, H_kv, D]."""
@@ -231,10 +258,11 @@ def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=No
     if out is None:
         out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
     lse_t = _lse_out(lse, H, Tq, q.device)
+    ws, ws_bytes = _attn_workspace(workspace, H, Tq, D, q.device)
     rc = lib().nvfp4_kv_attention_chunked(
         _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
         _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, nch * L, chunk_len, arr,
-        len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _stream(stream))
+        len(rg), float(softmax_scale), _ptr(out), _ptr(lse_t), _ptr(ws), ws_bytes, _stream(stream))
     _check(rc, "nvfp4_kv_attention_chunked")
     return (out, lse_t) if lse_t is not None else out
 
@@ -335,19 +363,20 @@ class KVCache:
             raise Nvfp4Error(n, "nvfp4_kv_cache_key_ranges")
         return [(arr[2 * i], arr[2 * i + 1]) for i in range(n)]
 
-    def attention(self, layer, q, softmax_scale=None, out=None, lse=False, stream=None):
+    def attention(self, layer, q, softmax_scale=None, out=None, lse=False, workspace=None, stream=None):
         _bf16_dev(q, "q")
         Hq, Tq, D = q.shape
         if softmax_scale is None:
             softmax_scale = D ** -0.5
         if out is None:
             out = torch.empty(Hq, Tq, D, dtype=torch.bfloat16, device=q.device)
-        lse_t = torch.empty(Hq, Tq, dtype=torch.float32, device=q.device) if lse else None
+        lse_t = _lse_out(lse, Hq, Tq, q.device)
+        ws, ws_bytes = _attn_workspace(workspace, Hq, Tq, D, q.device)
         rc = lib().nvfp4_kv_cache_attention(ctypes.byref(self.state), _ptr(self.storage), self.storage_bytes, layer,
                                             _ptr(q), Hq, Tq, float(softmax_scale), _ptr(out), _ptr(lse_t),
-                                            _stream(stream))
+                                            _ptr(ws), ws_bytes, _stream(stream))
         _check(rc, "nvfp4_kv_cache_attention")
-        return (out, lse_t) if lse else out
+        return (out, lse_t) if lse_t is not None else out
 
     def slot_arrays(self, layer):
         """Views of one layer's slot arrays (k_codes, v_codes [cap, H, L,

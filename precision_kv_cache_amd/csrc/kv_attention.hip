@@ -25,6 +25,7 @@
 // chunk edge, so the factors and the bias are uniform over a tile.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "host_common.hpp"
@@ -46,6 +47,7 @@ constexpr int kKBytes = kKT * kKRow;
 constexpr int kVBytes = kD * kVRow;
 constexpr int kBuf = kKBytes + kVBytes;
 constexpr int kXcds = 8;
+constexpr int kMaxSplit = 4;  // key splits per query block at most
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -63,8 +65,17 @@ struct AttnParams {
   int rstart[NVFP4_ATTN_MAX_RANGES], rlen[NVFP4_ATTN_MAX_RANGES];
   float sigma;  // softmax scale * log2(e)
   int nqb;      // query blocks per head
-  int total;    // H * nqb
+  int hq;       // H * nqb
+  int total;    // hq * ksplit
   int per_xcd;  // workgroup slots per XCD
+  // Key splits: workgroup (j, h, qb) takes split_tiles[j] tiles of the key
+  // list from the cursor (split_r[j], split_pos[j]).  With ksplit > 1 it
+  // writes its unnormalized O, its reference maximum M (base-2 logits) and
+  // its weight sum l to part_o / part_ml, and a combine kernel merges them.
+  int ksplit;
+  int split_r[kMaxSplit], split_pos[kMaxSplit], split_tiles[kMaxSplit];
+  float* part_o;   // [ksplit][H][Tq][D]
+  float* part_ml;  // [ksplit][H][Tq][2]
 };
 
 // Next tile of the key list: [start, start + n), n <= 64, inside one range
@@ -81,6 +92,13 @@ __device__ __forceinline__ bool next_tile(const AttnParams& p, int& r, int& pos,
   n = min(kKT, cend - pos);
   pos += n;
   return true;
+}
+
+// next_tile within a split's budget of tiles.
+__device__ __forceinline__ bool take_tile(const AttnParams& p, int& r, int& pos, int& start, int& n, int& left) {
+  if (left <= 0) return false;
+  --left;
+  return next_tile(p, r, pos, start, n);
 }
 
 // Raw cache bytes of one tile, held in registers between the global loads
@@ -189,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   // that XCD's L2 for the head's cache.
   const int w = (int)(blockIdx.x % kXcds) * p.per_xcd + (int)(blockIdx.x / kXcds);
   if (w >= p.total) return;
-  const int h = w / p.nqb, qb = w % p.nqb;
+  const int js = w / p.hq, hqi = w % p.hq;  // key split, (head, query block)
+  const int h = hqi / p.nqb, qb = hqi % p.nqb;
   const int kvh = h / p.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -216,9 +235,9 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   float kf = 0.f;
   int cur_chunk = -1;
 
-  int r = 0, pos = p.nr > 0 ? p.rstart[0] : 0;
+  int r = p.split_r[js], pos = p.split_pos[js], left = p.split_tiles[js];
   int t_start = 0, t_n = 0;
-  bool have = next_tile(p, r, pos, t_start, t_n);
+  bool have = take_tile(p, r, pos, t_start, t_n, left);
   TileRegs regs;
   if (have) {
     load_tile(p, kvh, t_start, t_n, regs);
@@ -229,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
 
   while (have) {
     int n_start = 0, n_n = 0;
-    const bool nhave = next_tile(p, r, pos, n_start, n_n);
+    const bool nhave = take_tile(p, r, pos, n_start, n_n, left);
     if (nhave) load_tile(p, kvh, n_start, n_n, regs);
 
     // this tile's chunk: logit factor g_K * sigma and bias sigma * (q . m_c)
@@ -363,7 +382,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
     have = nhave;
   }
 
-  // O = O^T / l, rows of 4 dims per lane; lse = ln 2 * (M + log2 l)
+  // O = O^T / l, rows of 4 dims per lane; lse = ln 2 * (M + log2 l).  A key
+  // split stores its O, M and l for the combine kernel instead.
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     float l = lsum[nt];
@@ -371,6 +391,14 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
     l += __shfl_xor(l, 32);
     const int qi = qw0 + 16 * nt + l16;
     if (qi >= p.Tq) continue;
+    if (p.ksplit > 1) {
+      const size_t row = ((size_t)js * p.H + h) * p.Tq + qi;
+      float* dst = p.part_o + row * kD + 4 * g;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) *reinterpret_cast<f32x4*>(dst + 16 * m) = o[m][nt];
+      if (g == 0) *reinterpret_cast<f32x2*>(p.part_ml + row * 2) = f32x2{M[nt], l};
+      continue;
+    }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     uint16_t* dst = p.out + ((size_t)h * p.Tq + qi) * kD + 4 * g;
 #pragma unroll
@@ -383,14 +411,96 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   }
 }
 
+// Merges the key splits of each query row: M* = max_j M_j, w_j = 2^(M_j - M*)
+// (0 for a split without keys), out = sum_j w_j O_j / sum_j w_j l_j, lse =
+// ln 2 (M* + log2 sum_j w_j l_j); in a fixed split order.  32 lanes per row,
+// 4 dims each.
+__global__ __launch_bounds__(256) void attention_combine_kernel(const float* part_o, const float* part_ml, int ksplit,
+                                                                long long rows, uint16_t* out, float* lse) {
+  const long long row = (long long)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;
+  const int d = 4 * (threadIdx.x & 31);
+  float Mj[kMaxSplit], lj[kMaxSplit];
+  float Ms = -INFINITY;
+  for (int j = 0; j < ksplit; ++j) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(part_ml + ((size_t)j * rows + row) * 2);
+    Mj[j] = ml[0];
+    lj[j] = ml[1];
+    Ms = fmaxf(Ms, ml[0]);
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int j = 0; j < ksplit; ++j) {
+    if (Mj[j] == -INFINITY) continue;  // no keys in this split
+    const float wj = __builtin_amdgcn_exp2f(Mj[j] - Ms);
+    const f32x4 oj = *reinterpret_cast<const f32x4*>(part_o + ((size_t)j * rows + row) * kD + d);
+    acc += oj * wj;
+    L = __builtin_fmaf(lj[j], wj, L);
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  *reinterpret_cast<u32x2*>(out + (size_t)row * kD + d) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (lse && d == 0) lse[row] = (Ms + __log2f(L)) * 0.69314718055994531f;
+}
+
 }  // namespace
+
+// Host replica of the kernel's tile walk: the number of tiles of the key
+// list, and the cursor (range, position) at which tile `at` starts.  Tiles
+// are at most 64 keys and never cross a chunk or range edge.
+static long long host_tiles(const AttnParams& p, long long at, int* cur_r, int* cur_pos) {
+  long long t = 0;
+  for (int r = 0; r < p.nr; ++r) {
+    long long pos = p.rstart[r];
+    const long long end = pos + p.rlen[r];
+    while (pos < end) {
+      const long long cend = std::min(end, (pos / p.L + 1) * (long long)p.L);  // this chunk piece's end
+      const long long nt = (cend - pos + kKT - 1) / kKT;
+      if (at >= t && at < t + nt) {
+        *cur_r = r;
+        *cur_pos = (int)(pos + (at - t) * kKT);
+        return t;
+      }
+      t += nt;
+      pos = cend;
+    }
+  }
+  return t;
+}
+
+// Workspace bytes of k key splits over `rows` query rows: the partial O,
+// then (M, l) per row.
+static size_t split_bytes(int k, size_t rows) {
+  return align_up((size_t)k * rows * kD * 4, 256) + align_up((size_t)k * rows * 8, 256);
+}
+
+// Key splits per query block: the count (at most kMaxSplit) that minimizes
+// the rounds of the grid over the CUs, per unit of work, when the workspace
+// holds it and every split gets at least 4 tiles.
+static int choose_ksplit(int hq, long long ntiles, size_t rows, size_t ws_bytes) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    return 1;
+  int best = 1;
+  double best_t = 1e30;
+  for (int k = 1; k <= kMaxSplit; ++k) {
+    if (k > 1 && (ntiles < 4LL * k || split_bytes(k, rows) > ws_bytes)) break;
+    const double rounds = (double)(((long long)hq * k + ncu - 1) / ncu) / k;
+    if (rounds < best_t - 1e-9) {
+      best_t = rounds;
+      best = k;
+    }
+  }
+  return best;
+}
 
 // Shared host path of the two layouts.
 static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes, const uint8_t* k_scales,
                      const float* k_tensor_scale, const float* k_mean, const uint8_t* v_codes,
                      const uint8_t* v_scales, const float* v_tensor_scale, int H_kv, int T, int chunk_len,
                      const int* key_ranges, int n_ranges, float softmax_scale, uint16_t* out, float* lse,
-                     void* stream, bool chunk_major) {
+                     void* workspace, size_t workspace_bytes, void* stream, bool chunk_major) {
   if (H < 0 || Tq < 0 || T < 0 || H_kv < 1 || chunk_len < 1 || D != kD) return NVFP4_ERR_SHAPE;
   if (H % H_kv != 0 || T % chunk_len != 0) return NVFP4_ERR_SHAPE;
   if (n_ranges < 0 || n_ranges > NVFP4_ATTN_MAX_RANGES || !(softmax_scale > 0.f && softmax_scale <= 3.0e38f))
@@ -405,7 +515,8 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   if (T > 0 && (!k_codes || !k_scales || !k_tensor_scale || !v_codes || !v_scales || !v_tensor_scale))
     return NVFP4_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 8) || !aligned(k_codes, 8) || !aligned(v_codes, 2) ||
-      !aligned(k_mean, 16) || !aligned(k_tensor_scale, 4) || !aligned(v_tensor_scale, 4) || !aligned(lse, 4))
+      !aligned(k_mean, 16) || !aligned(k_tensor_scale, 4) || !aligned(v_tensor_scale, 4) || !aligned(lse, 4) ||
+      !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   const size_t nq = (size_t)H * Tq * kD, nkv = (size_t)H_kv * T * kD, nc = (size_t)(T / chunk_len);
   const Range in[8] = {range_of(q, nq * 2),
@@ -416,8 +527,9 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
                        range_of(v_codes, nkv / 2),
                        range_of(v_scales, nkv / 16),
                        range_of(v_tensor_scale, nc * 4)};
-  const Range outr[2] = {range_of(out, nq * 2), range_of(lse, lse ? (size_t)H * Tq * 4 : 0)};
-  if (any_alias(in, 8, outr, 2)) return NVFP4_ERR_ALIAS;
+  const Range outr[3] = {range_of(out, nq * 2), range_of(lse, lse ? (size_t)H * Tq * 4 : 0),
+                         range_of(workspace, workspace ? workspace_bytes : 0)};
+  if (any_alias(in, 8, outr, 3)) return NVFP4_ERR_ALIAS;
 
   AttnParams p{};
   p.q = q;
@@ -436,12 +548,46 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   }
   p.sigma = softmax_scale * 1.4426950408889634f;
   p.nqb = (Tq + kQB - 1) / kQB;
-  const long long total = (long long)H * p.nqb;
-  if (total > (1LL << 28)) return NVFP4_ERR_SHAPE;
-  p.total = (int)total;
+  const long long hq = (long long)H * p.nqb;
+  if (hq > (1LL << 26)) return NVFP4_ERR_SHAPE;
+  p.hq = (int)hq;
+  // one split: the whole key list from its start, no tile budget
+  p.ksplit = 1;
+  p.split_r[0] = 0;
+  p.split_pos[0] = p.nr > 0 ? p.rstart[0] : 0;
+  p.split_tiles[0] = 0x7fffffff;
+  const size_t rows = (size_t)H * Tq;
+  if (workspace && workspace_bytes >= split_bytes(2, rows)) {
+    long long pieces = 0;  // chunk pieces of the key list: bounds the host walk
+    for (int r = 0; r < p.nr; ++r)
+      pieces += ((long long)p.rstart[r] + p.rlen[r] - 1) / chunk_len - p.rstart[r] / chunk_len + 1;
+    if (pieces <= (1 << 16)) {
+      int cr = 0, cpos = 0;
+      const long long ntiles = host_tiles(p, -1, &cr, &cpos);
+      const int k = choose_ksplit(p.hq, ntiles, rows, workspace_bytes);
+      if (k > 1) {
+        p.ksplit = k;
+        for (int j = 0; j < k; ++j) {
+          const long long t0 = ntiles * j / k, t1 = ntiles * (j + 1) / k;
+          host_tiles(p, t0, &p.split_r[j], &p.split_pos[j]);
+          p.split_tiles[j] = (int)(t1 - t0);
+        }
+        p.part_o = static_cast<float*>(workspace);
+        p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align_up((size_t)k * rows * kD * 4, 256));
+      }
+    }
+  }
+  p.total = p.hq * p.ksplit;
   p.per_xcd = (p.total + kXcds - 1) / kXcds;
+  hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, as_stream(stream)>>>(p);
+  attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
+  if (p.ksplit > 1) {
+    const long long nb = ((long long)rows + 7) / 8;
+    attention_combine_kernel<<<dim3((unsigned)nb), dim3(256), 0, s>>>(p.part_o, p.part_ml, p.ksplit, (long long)rows,
+                                                                     out, lse);
+  }
   return launch_status();
 }
 
@@ -449,14 +595,21 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
 
 using namespace nvfp4;
 
+extern "C" NVFP4KV_API size_t nvfp4_kv_attention_workspace_bytes(int H, int Tq, int D) noexcept {
+  if (H < 1 || Tq < 1 || D != kD) return 0;
+  return split_bytes(kMaxSplit, (size_t)H * Tq);
+}
+
 extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
                                               const uint8_t* k_scales, const float* k_tensor_scale,
                                               const float* k_mean, const uint8_t* v_codes, const uint8_t* v_scales,
                                               const float* v_tensor_scale, int H_kv, int T, int chunk_len,
                                               const int* key_ranges, int n_ranges, float softmax_scale,
-                                              uint16_t* out, float* lse, void* stream) noexcept {
+                                              uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                              void* stream) noexcept {
   return attention_launch(q, H, Tq, D, k_codes, k_scales, k_tensor_scale, k_mean, v_codes, v_scales, v_tensor_scale,
-                          H_kv, T, chunk_len, key_ranges, n_ranges, softmax_scale, out, lse, stream, false);
+                          H_kv, T, chunk_len, key_ranges, n_ranges, softmax_scale, out, lse, workspace,
+                          workspace_bytes, stream, false);
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, int Tq, int D,
@@ -465,7 +618,9 @@ extern "C" NVFP4KV_API int nvfp4_kv_attention_chunked(const uint16_t* q, int H, 
                                                       const uint8_t* v_codes, const uint8_t* v_scales,
                                                       const float* v_tensor_scale, int H_kv, int T, int chunk_len,
                                                       const int* key_ranges, int n_ranges, float softmax_scale,
-                                                      uint16_t* out, float* lse, void* stream) noexcept {
+                                                      uint16_t* out, float* lse, void* workspace,
+                                                      size_t workspace_bytes, void* stream) noexcept {
   return attention_launch(q, H, Tq, D, k_codes, k_scales, k_tensor_scale, k_mean, v_codes, v_scales, v_tensor_scale,
-                          H_kv, T, chunk_len, key_ranges, n_ranges, softmax_scale, out, lse, stream, true);
+                          H_kv, T, chunk_len, key_ranges, n_ranges, softmax_scale, out, lse, workspace,
+                          workspace_bytes, stream, true);
 }

@@ -213,7 +213,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_cache_key_ranges(const nvfp4_kv_cache_t* c, 
 extern "C" NVFP4KV_API int nvfp4_kv_cache_attention(const nvfp4_kv_cache_t* c, const void* storage,
                                                     size_t storage_bytes, int layer, const uint16_t* q, int Hq,
                                                     int Tq, float softmax_scale, uint16_t* out, float* lse,
-                                                    void* stream) noexcept {
+                                                    void* workspace, size_t workspace_bytes, void* stream) noexcept {
   if (!c || !storage) return NVFP4_ERR_NULL;
   if (layer < 0 || layer >= c->layers || !geometry_ok(c->heads, c->head_dim, c->chunk_len, c->capacity))
     return NVFP4_ERR_SHAPE;
@@ -229,5 +229,5 @@ extern "C" NVFP4KV_API int nvfp4_kv_cache_attention(const nvfp4_kv_cache_t* c, c
                                     reinterpret_cast<const float*>(base + l.off[6]), base + l.off[1],
                                     base + l.off[3], reinterpret_cast<const float*>(base + l.off[5]), c->heads,
                                     c->capacity * c->chunk_len, c->chunk_len, ranges, n, softmax_scale, out, lse,
-                                    stream);
+                                    workspace, workspace_bytes, stream);
 }

@@ -131,13 +131,13 @@ def test_dequant_and_1d_2d_argument_errors():
 
 def _att(q=FAKE, H=2, Tq=16, D=128, kc=FAKE + (1 << 30), ks=FAKE + (2 << 30), kg=FAKE + (3 << 30),
          km=FAKE + (4 << 30), vc=FAKE + (5 << 30), vs=FAKE + (6 << 30), vg=FAKE + (7 << 30), Hkv=1, T=64, L=32,
-         ranges=((0, 64),), n=None, scale=0.088, out=FAKE + (8 << 30), lse=FAKE + (9 << 30)):
+         ranges=((0, 64),), n=None, scale=0.088, out=FAKE + (8 << 30), lse=FAKE + (9 << 30), ws=None, wsb=0):
     V = ctypes.c_void_p
     flat = [x for r in (ranges or ()) for x in r]
     arr = (ctypes.c_int * max(1, len(flat)))(*flat) if ranges is not None else None
     n = len(ranges or ()) if n is None else n
     return P.lib().nvfp4_kv_attention(V(q), H, Tq, D, V(kc), V(ks), V(kg), V(km), V(vc), V(vs), V(vg), Hkv, T, L,
-                                      arr, n, scale, V(out), V(lse), None)
+                                      arr, n, scale, V(out), V(lse), V(ws), wsb, None)
 
 
 def test_attention_argument_errors():
@@ -157,8 +157,14 @@ def test_attention_argument_errors():
     assert _att(km=FAKE + (4 << 30) + 4) == ALIGN
     assert _att(out=FAKE + 64) == ALIAS            # output inside q
     assert _att(lse=FAKE + (8 << 30) + 32) == ALIAS  # lse inside out
+    assert _att(ws=FAKE + (10 << 30) + 64, wsb=1 << 20) == ALIGN  # workspace 256-byte aligned
+    assert _att(ws=FAKE + (8 << 30), wsb=1 << 20) == ALIAS           # workspace over out
     assert _att(H=0, q=None, out=None) == OK       # empty call
     assert _att(Tq=0) == OK
+    # workspace for every key split: partial O (fp32 D per row) and (M, l) per row, per split
+    wb = P.nvfp4_kv_attention_workspace_bytes(24, 7040, 128)
+    assert wb >= 4 * 24 * 7040 * (128 + 2) * 4
+    assert P.nvfp4_kv_attention_workspace_bytes(24, 7040, 64) == 0
 
 
 def _gemm(ac=FAKE, as_=FAKE + (1 << 30), ag=FAKE + (2 << 30), M=64, K=128, wc=FAKE + (3 << 30),

@@ -41,19 +41,26 @@ def _to_gpu(c):
     return {k: (None if c.get(k) is None else torch.from_numpy(np.ascontiguousarray(c[k])).cuda()) for k in keys}
 
 
-def _run_gpu(q_bits, cache, L, ranges, scale=None):
+def _run_gpu(q_bits, cache, L, ranges, scale=None, split=True):
+    """split: with a workspace (the call may split each query block's keys
+    over several workgroups and merge them), else without one (unsplit)."""
     q = W.from_bits(q_bits, "cuda")
     H, Tq, D = q.shape
     out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device="cuda")
     out.view(torch.uint8).fill_(0xFF)          # NaN: an unwritten output cannot pass
-    o, lse = P.nvfp4_kv_attention(q, _to_gpu(cache), L, ranges, softmax_scale=scale, out=out, lse=True)
+    ws = None
+    if split:
+        ws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(H, Tq, D), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)                         # garbage on entry
+    o, lse = P.nvfp4_kv_attention(q, _to_gpu(cache), L, ranges, softmax_scale=scale, out=out, lse=True,
+                                  workspace=ws if split else False)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _full(q_bits, cache, L, ranges, scale=None, **kw):
+def _full(q_bits, cache, L, ranges, scale=None, split=True, **kw):
     H, Tq, D = q_bits.shape
-    got, got_lse = _run_gpu(q_bits, cache, L, ranges, scale)
+    got, got_lse = _run_gpu(q_bits, cache, L, ranges, scale, split)
     rows = np.arange(H * Tq)
     _check(q_bits, cache, L, ranges, got.reshape(-1, D), got_lse.reshape(-1), rows, scale, **kw)
 
@@ -79,18 +86,19 @@ def test_zero_query_weights_every_listed_key_equally():
     np.testing.assert_allclose(got_lse, np.log(len(keys)), rtol=1e-6)
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "unsplit"])
 @pytest.mark.parametrize("H,Hkv,T,L,Tq,ranges", [
     (2, 2, 640, 128, 300, [(0, 640)]),                         # 5 chunks, ragged query block
     (4, 2, 640, 128, 256, [(0, 70), (200, 77), (383, 257)]),   # grouped heads, segment edges inside tiles
     (3, 1, 512, 64, 17, [(448, 64), (0, 64), (100, 1)]),       # one cache head, single-key range
     (1, 1, 96, 96, 513, [(0, 96)]),                            # one chunk shorter than two tiles
 ])
-def test_random_cache(H, Hkv, T, L, Tq, ranges):
-    say("random cache", H, Hkv, T, L, Tq, ranges)
+def test_random_cache(H, Hkv, T, L, Tq, ranges, split):
+    say("random cache", H, Hkv, T, L, Tq, ranges, "split" if split else "unsplit")
     k, v = W.gaussian_kv(W.KVShape(Hkv, T, 128, L), 22 + T + Tq)
     cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
     q = W.bf16_bits(W.queries(H, Tq, 128, 31 + Tq))
-    _full(q, cache, L, ranges)
+    _full(q, cache, L, ranges, split=split)
 
 
 def test_heavy_tail_cache_and_sharp_softmax():
@@ -114,6 +122,7 @@ def test_no_mean_single_key_and_empty():
     nomean = dict(cache)
     nomean["k_mean"] = None
     _full(q, nomean, L, [(0, T)])
+    _full(q, nomean, L, [(0, T)], split=False)
     _full(q, cache, L, [(77, 1)])
     got, got_lse = _run_gpu(q, cache, L, [])
     assert np.all(got == 0) and np.all(np.isneginf(got_lse))

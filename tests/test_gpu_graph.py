@@ -33,7 +33,8 @@ def test_quantize_dequantize_attention_replays():
     # eager reference
     ref = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, workspace=ws)
     ref_dk = P.nvfp4_dequantize(ref["k_codes"], ref["k_scales"], ref["k_tensor_scale"], ref["k_mean"], s.chunk_len)
-    ref_att, ref_lse = P.nvfp4_kv_attention(q, ref, s.chunk_len, ranges, lse=True)
+    aws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(s.H, 300, s.D), dtype=torch.uint8, device="cuda")
+    ref_att, ref_lse = P.nvfp4_kv_attention(q, ref, s.chunk_len, ranges, lse=True, workspace=aws)
     torch.cuda.synchronize()
 
     out = _empty_like_dict(ref)
@@ -49,7 +50,7 @@ def test_quantize_dequantize_attention_replays():
             P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, out=out, workspace=ws, stream=stream)
             P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len,
                                out=dk, stream=stream)
-            P.nvfp4_kv_attention(q, out, s.chunk_len, ranges, out=att, lse=lse, stream=stream)
+            P.nvfp4_kv_attention(q, out, s.chunk_len, ranges, out=att, lse=lse, workspace=aws, stream=stream)
     torch.cuda.synchronize()
 
     for rep in range(4):
