@@ -23,6 +23,12 @@
 // scale * log2(e) * (q . m_c), one value per (query, chunk).  For V the
 // factor S * g_V is applied before one rounding to bf16.  Tiles never cross a
 // chunk edge, so the factors and the bias are uniform over a tile.
+//
+// With a workspace, the host may split each query block's key list into up
+// to four parts of about equal tile counts, one workgroup each, when that
+// fills the CUs in fewer rounds; each part stores its unnormalized O, its
+// reference maximum and its weight sum, and a small kernel merges the parts
+// per query row in a fixed order.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <algorithm>
