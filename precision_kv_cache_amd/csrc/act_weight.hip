@@ -5,9 +5,11 @@
 //
 // Both need the tensor's largest magnitude before any block can be encoded,
 // so each is two passes: an amax pass (every workgroup stores its partial
-// maximum in its own workspace slot, one small workgroup combines them; a
-// shared atomic would serialize thousands of workgroups) and the quantize
-// pass, which recomputes the rotation in registers instead of storing it.
+// maximum in its own workspace slot; a shared atomic would serialize
+// thousands of workgroups) and the quantize pass, whose every workgroup
+// first reduces those partials itself (a few KB from L2, cheaper than a
+// separate reduction launch between the passes) and which recomputes the
+// rotation in registers instead of storing it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,7 +21,7 @@ namespace nvfp4 {
 
 constexpr int kAWThreads = 256;
 constexpr int kAmaxMaxWG = 2048;  // workgroups of the amax pass (grid-stride)
-// workspace: [0, 256) the tensor maximum's bits; [256, ...) partial maxima
+// workspace: [0, 256) unused; [256, ...) the amax pass's partial maxima
 constexpr size_t kAWWorkspace = 256 + (size_t)kAmaxMaxWG * sizeof(float);
 
 // 16-point random-sign Hadamard transform of one block, in place, without
@@ -100,30 +102,28 @@ __global__ __launch_bounds__(kAWThreads) void amax16_kernel(const uint16_t* x, l
   }
 }
 
-// The tensor maximum from n partial maxima (one workgroup).
-__global__ __launch_bounds__(kAWThreads) void amax_reduce_kernel(const float* partial, int n, uint32_t* amax_bits) {
-  __shared__ float shw[kAWThreads / 64];
+// The tensor maximum from the amax pass's n partial maxima, reduced by the
+// whole workgroup (at most 2048 floats, read from L2): every quantize
+// workgroup does this itself instead of waiting for a separate reduction
+// launch.  Ends with a barrier; shw is 4 floats of LDS.
+__device__ __forceinline__ float wg_partial_max(const float* partial, int n, float* shw) {
   float m = 0.0f;
   for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, partial[i]);
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) shw[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float a = 0.0f;
-    for (int w = 0; w < (int)(blockDim.x / 64); ++w) a = fmaxf(a, shw[w]);
-    *amax_bits = __float_as_uint(a);
-  }
+  return fmaxf(fmaxf(shw[0], shw[1]), fmaxf(shw[2], shw[3]));
 }
 
 // 1D quantize pass: one lane per 16-element block of the row-major tensor.
 template <int MODE, bool RHT>
 __global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, long long nblk, uint32_t sign_mask,
-                                                             const uint32_t* amax_bits, uint8_t* codes,
+                                                             const float* partial, int npart, uint8_t* codes,
                                                              uint8_t* scales, float* tensor_scale) {
   __shared__ float2 sh_tab[128];
+  __shared__ float shw[kAWThreads / 64];
   fill_scale_table(sh_tab);
-  __syncthreads();
-  const float A = __uint_as_float(*amax_bits);
+  const float A = wg_partial_max(partial, npart, shw);  // its barrier also orders the table's fill
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = A / C;
@@ -150,12 +150,12 @@ __global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, 
 // the 16-lane group, the error one pairwise tree over the tile rows.
 template <int MODE>
 __global__ __launch_bounds__(kAWThreads) void quant2d_kernel(const uint16_t* w, int rows, int cols,
-                                                             const uint32_t* amax_bits, uint8_t* codes,
+                                                             const float* partial, int npart, uint8_t* codes,
                                                              uint8_t* scales, float* tensor_scale) {
   __shared__ float2 sh_tab[128];
+  __shared__ float shw[kAWThreads / 64];
   fill_scale_table(sh_tab);
-  __syncthreads();
-  const float A = __uint_as_float(*amax_bits);
+  const float A = wg_partial_max(partial, npart, shw);  // its barrier also orders the table's fill
   const float C = mode_constant(MODE);
   const float g = A > 0.0f ? C / A : 0.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = A / C;
@@ -269,11 +269,10 @@ extern "C" NVFP4KV_API size_t nvfp4_quantize_2d_workspace_bytes(int rows, int co
   return aw_shape_ok(rows, cols, true) ? kAWWorkspace : 0;
 }
 
-// amax pass over nseg 16-element segments, then the reduction into the
-// workspace's first word.
-static void launch_amax(const uint16_t* x, long long nseg, bool rht, uint32_t sign_mask, void* workspace,
-                        hipStream_t s) {
-  uint32_t* amax = static_cast<uint32_t*>(workspace);
+// amax pass over nseg 16-element segments: one partial maximum per
+// workgroup into the workspace; returns their count.
+static int launch_amax(const uint16_t* x, long long nseg, bool rht, uint32_t sign_mask, void* workspace,
+                       hipStream_t s) {
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256);
   const unsigned g0 = grid_for(nseg, 4 * kAmaxUnroll);
   const unsigned ga = g0 < (unsigned)kAmaxMaxWG ? g0 : (unsigned)kAmaxMaxWG;
@@ -281,7 +280,7 @@ static void launch_amax(const uint16_t* x, long long nseg, bool rht, uint32_t si
     amax16_kernel<true><<<ga, kAWThreads, 0, s>>>(x, nseg, sign_mask, partial);
   else
     amax16_kernel<false><<<ga, kAWThreads, 0, s>>>(x, nseg, sign_mask, partial);
-  amax_reduce_kernel<<<1, kAWThreads, 0, s>>>(partial, (int)ga, amax);
+  return (int)ga;
 }
 
 extern "C" NVFP4KV_API int nvfp4_quantize_1d(const uint16_t* x, int rows, int cols, int mode, int hadamard,
@@ -301,16 +300,16 @@ extern "C" NVFP4KV_API int nvfp4_quantize_1d(const uint16_t* x, int rows, int co
                         range_of(workspace, kAWWorkspace)};
   if (any_alias(in, 1, out, 4)) return NVFP4_ERR_ALIAS;
   hipStream_t s = as_stream(stream);
-  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  const float* partial = reinterpret_cast<const float*>(static_cast<char*>(workspace) + 256);
   const long long nblk = (long long)(n / 16);
   (void)hipGetLastError();
-  launch_amax(x, nblk, hadamard != 0, sign_mask, workspace, s);
+  const int np = launch_amax(x, nblk, hadamard != 0, sign_mask, workspace, s);
   const unsigned gq = grid_for(nblk, 2);
-#define NVFP4_Q1D(MODE)                                                                                   \
-  (hadamard ? quant1d_kernel<MODE, true><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax, codes, scales, \
-                                                                   tensor_scale)                          \
-            : quant1d_kernel<MODE, false><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, amax, codes, scales, \
-                                                                    tensor_scale))
+#define NVFP4_Q1D(MODE)                                                                                      \
+  (hadamard ? quant1d_kernel<MODE, true><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, partial, np, codes,   \
+                                                                   scales, tensor_scale)                     \
+            : quant1d_kernel<MODE, false><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, partial, np, codes,  \
+                                                                    scales, tensor_scale))
   switch (mode) {
     case NVFP4_MODE_FIXED6: NVFP4_Q1D(kModeFixed6); break;
     case NVFP4_MODE_FIXED4: NVFP4_Q1D(kModeFixed4); break;
@@ -336,15 +335,21 @@ extern "C" NVFP4KV_API int nvfp4_quantize_2d(const uint16_t* w, int rows, int co
                         range_of(workspace, kAWWorkspace)};
   if (any_alias(in, 1, out, 4)) return NVFP4_ERR_ALIAS;
   hipStream_t s = as_stream(stream);
-  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  const float* partial = reinterpret_cast<const float*>(static_cast<char*>(workspace) + 256);
   (void)hipGetLastError();
-  launch_amax(w, (long long)(n / 16), false, 0u, workspace, s);
+  const int np = launch_amax(w, (long long)(n / 16), false, 0u, workspace, s);
   const long long ntiles = (long long)(rows / 16) * (cols / 16);
   const unsigned gq = grid_for((ntiles + 3) / 4 * 64, 1);
   switch (mode) {
-    case NVFP4_MODE_FIXED6: quant2d_kernel<kModeFixed6><<<gq, kAWThreads, 0, s>>>(w, rows, cols, amax, codes, scales, tensor_scale); break;
-    case NVFP4_MODE_FIXED4: quant2d_kernel<kModeFixed4><<<gq, kAWThreads, 0, s>>>(w, rows, cols, amax, codes, scales, tensor_scale); break;
-    default: quant2d_kernel<kMode4over6><<<gq, kAWThreads, 0, s>>>(w, rows, cols, amax, codes, scales, tensor_scale); break;
+    case NVFP4_MODE_FIXED6:
+      quant2d_kernel<kModeFixed6><<<gq, kAWThreads, 0, s>>>(w, rows, cols, partial, np, codes, scales, tensor_scale);
+      break;
+    case NVFP4_MODE_FIXED4:
+      quant2d_kernel<kModeFixed4><<<gq, kAWThreads, 0, s>>>(w, rows, cols, partial, np, codes, scales, tensor_scale);
+      break;
+    default:
+      quant2d_kernel<kMode4over6><<<gq, kAWThreads, 0, s>>>(w, rows, cols, partial, np, codes, scales, tensor_scale);
+      break;
   }
   return launch_status();
 }
