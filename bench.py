@@ -174,7 +174,7 @@ def main():
         deq.append((torch.empty(H, T, D, dtype=torch.bfloat16, device=dev),
                     torch.empty(H, T, D, dtype=torch.bfloat16, device=dev)))
     counts = torch.zeros(2, 2, dtype=torch.int64, device=dev)
-    ws = torch.empty(P.nvfp4_kv_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(P.nvfp4_kv_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)  # sticky error word 0
     stream = torch.cuda.current_stream()
 
     def quant(l, ev=None):
@@ -223,6 +223,13 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / a.steps
+    # every quantize call of the warm-up and timed steps shares ws: its sticky
+    # error word is non-zero if any of them had a wait time out
+    wait_errors = P.kv_error_word(ws)
+    if wait_errors:
+        print(f"bench.py: a quantize call's bounded wait timed out (error word {wait_errors}); "
+              "its outputs are invalid, so no result is reported", flush=True)
+        sys.exit(3)
     q_ms = sum(e0.elapsed_time(e1) for e0, e1 in qev) / nlayers    # one layer's quantize call (K and V)
     d_ms = sum(e0.elapsed_time(e1) for e0, e1 in dev_ev) / nlayers  # one layer's dequantize calls (K and V)
 
@@ -294,14 +301,21 @@ def main():
             "bytes_per_launch": qbytes_layer,
         },
         "input_generation_s": round(gen_s, 2),
+        "quantize_wait_timeouts": wait_errors,
     }
+    if not a.no_cpu_baseline:
+        # the oracle's leg: its rate on the host, and the last timed step's
+        # outputs of layer 0 chunk 0 compared with it bit for bit
+        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds, check=(outs[0], deq[0]))
+        if not result["cpu_baseline"]["parity_check"]["bit_exact"]:
+            print("bench.py: the sampled chunk differs from the oracle: " + json.dumps(result["cpu_baseline"]),
+                  flush=True)
+            sys.exit(3)
     outs.clear()
     deq.clear()
     torch.cuda.empty_cache()
     result["act_weight"] = act_weight_timing(P, W, a.mode, stream)
     result["heavy_tail_report"] = heavy_tail_report(P, W)
-    if not a.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -519,7 +533,7 @@ def stream_bench(a):
     kv = [W.gaussian_kv(W.KVShape(H, L, D, L), 200000 + l, device=dev) for l in range(nl)]
     q = W.queries(H, L, D, W.SEED_ATTN, device=dev)
     out = torch.empty_like(q)
-    ws = [torch.empty(P.nvfp4_kv_workspace_bytes(H, L, D, L), dtype=torch.uint8, device=dev) for _ in range(2)]
+    ws = [torch.zeros(P.nvfp4_kv_workspace_bytes(H, L, D, L), dtype=torch.uint8, device=dev) for _ in range(2)]
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     for c in range(10):
@@ -581,9 +595,13 @@ def stream_bench(a):
     ms_step = start.elapsed_time(stop) / a.steps
     att_ms = sum(e0.elapsed_time(e1) for e0, e1 in att_ev) / nl
     app_ms = sum(e0.elapsed_time(e1) for e0, e1 in app_ev) / nl  # beside attention, waits for CUs included
-    # the overlapped quantize kernel's error word of the last append beside attention (0: no wait timed out)
-    off = P.nvfp4_kv_error_word_offset(H, L, D, L)
-    wait_errors = int(ws[1][off:off + 4].view(torch.int32).item()) if off >= 0 else 0
+    # the sticky error words of both append workspaces: non-zero if any append
+    # (warm-up, alone or beside attention) had a wait time out
+    wait_errors = P.kv_error_word(ws[0]) | P.kv_error_word(ws[1])
+    if wait_errors:
+        print(f"bench.py: an append's bounded wait timed out (error word {wait_errors}); no result is reported",
+              flush=True)
+        sys.exit(3)
     flops = 4.0 * H * L * nk * D
     att_tflops = flops / (att_ms * 1e-3) / 1e12
     result = {
@@ -716,7 +734,7 @@ def gemm_bench(a):
             t_cpu += time.perf_counter() - t1
             done += nt
         result["cpu_baseline"] = {"value": round(2.0 * done * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s",
-                                  "cores": nt, "kind": "oracle",
+                                  "cores": nt, **host_cores(), "kind": "oracle",
                                   "sample": f"{done} random rows of the activation x the whole weight (fp64 over "
                                             f"the exactly decoded operands)", "seconds": round(t_cpu, 2)}
     print(json.dumps(result), flush=True)
@@ -816,6 +834,7 @@ def act_weight_bench(a):
         nb = done * cols
         sample_bytes = 2 * nb + nb // 2 + (nb // 16 if act else nb // 256)
         result["cpu_baseline"] = {"value": round(sample_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": nt,
+                                  **host_cores(),
                                   "kind": "oracle",
                                   "sample": (f"{done} of {rows} rows, {step} rows per oracle call (each call "
                                              "with its own tensor scale)" if act else f"the whole {rows} x {cols} weight"),
@@ -842,7 +861,7 @@ def vt_bench(a):
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     out = P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode)
-    ws = torch.empty(P.lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(P.lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for _ in range(a.warmup):
         P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode, out=out, workspace=ws, stream=stream)
@@ -875,9 +894,13 @@ def vt_bench(a):
                      "achieved": round(call_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes},
         "input_generation_s": round(gen_s, 2),
-        # the single-launch kernel's error word after the timed calls (0: no wait timed out)
-        "quantize_wait_timeouts": int(ws[:4].view(torch.int32).item()),
+        # the sticky error word after the warm-up and timed calls (0: no wait timed out)
+        "quantize_wait_timeouts": P.kv_error_word(ws),
     }
+    if result["quantize_wait_timeouts"]:
+        print(f"bench.py: a bounded wait timed out (error word {result['quantize_wait_timeouts']}); "
+              "no result is reported", flush=True)
+        sys.exit(3)
     if not a.no_cpu_baseline:
         import oracle as O
         nt = O.default_threads()
@@ -889,7 +912,7 @@ def vt_bench(a):
             t_cpu += time.perf_counter() - t1
             done += 1
         result["cpu_baseline"] = {"value": round(done * kv_bytes(H, L, D, L, False) / t_cpu / 1e9, 3), "unit": "GB/s",
-                                  "cores": nt, "kind": "oracle",
+                                  "cores": nt, **host_cores(), "kind": "oracle",
                                   "sample": f"{done} chunks of V [24, 7040, 128] quantized with 16-token blocks",
                                   "seconds": round(t_cpu, 2)}
     print(json.dumps(result), flush=True)
@@ -929,7 +952,7 @@ def stream_cpu_baseline(kv0, q, cache, ranges, nl, target_s):
         t_att += time.perf_counter() - t0
         done += batch
     step_s = nl * (t_app + t_att / done * H * Tq)
-    return {"value": round(L / step_s, 4), "unit": "tokens/s", "cores": nt, "kind": "oracle",
+    return {"value": round(L / step_s, 4), "unit": "tokens/s", "cores": nt, **host_cores(), "kind": "oracle",
             "sample": f"one layer's append of a [24, 7040, 128] chunk ({t_app:.2f} s) and {done} query rows of "
                       f"attention over {sum(n for _, n in ranges)} keys ({t_att:.2f} s), scaled to {nl} layers x "
                       f"24 x 7040 rows", "seconds": round(t_app + t_att, 2)}
@@ -959,41 +982,84 @@ def attention_cpu_baseline(k, v, q, L, ranges, target_s):
         t_total += time.perf_counter() - t0
         done += batch
     flops = 4.0 * done * nk * D
-    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": nt, **host_cores(), "kind": "oracle",
             "sample": f"{done} random query rows of [24, 7040, 128] over {nk} keys (fp64 attention over the "
                       f"exactly decoded cache)", "seconds": round(t_total, 2)}
 
 
-def cpu_baseline(ks, vs, L, mode, target_s):
+def host_cores():
+    """The host's CPU count as this process sees it: the CPUs it may run on
+    (scheduler affinity) and the machine's total."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"host_cores_usable": usable, "host_cores_total": os.cpu_count() or usable}
+
+
+def cpu_baseline(ks, vs, L, mode, target_s, check=None):
     """The oracle as it stands, on the host cores: K and V smooth-quantize +
     dequantize of whole chunks, layer 0 chunk 0 onwards, until about
-    target_s seconds of work."""
+    target_s seconds of work on all oracle threads; then the same chunks again
+    on one thread, until about target_s / 2 seconds.  With check = (the GPU
+    outputs of layer 0, its dequantized (K, V)), chunk 0 of that layer is
+    then compared with the oracle fed the GPU's K mean (untimed): codes,
+    scales, tensor scales and dequantized values bit for bit, the mean by the
+    1e-6 rule."""
     import oracle as O
     import workloads as W
 
-    nt = O.default_threads()
     H, T, D = ks[0].shape
-    done, t_total, nbytes, last = 0, 0.0, 0, (0, 0)
-    for l in range(len(ks)):
-        for c in range(T // L):
-            kb = W.bf16_bits(ks[l][:, c * L:(c + 1) * L])
-            vb = W.bf16_bits(vs[l][:, c * L:(c + 1) * L])
-            t0 = time.perf_counter()
-            r = O.smooth_quantize(kb, vb, L, mode, nthreads=nt)
-            O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], r["k_mean"], L, nthreads=nt)
-            O.dequantize(r["v_codes"], r["v_scales"], r["v_tensor_scale"], None, L, nthreads=nt)
-            t_total += time.perf_counter() - t0
-            done += 1
-            last = (l, c)
-            nbytes += 2 * (kv_bytes(H, L, D, L, True) + kv_bytes(H, L, D, L, False))
-            if t_total >= target_s:
-                break
-        if t_total >= target_s:
-            break
-    return {"value": round(nbytes / t_total / 1e9, 3), "unit": "GB/s", "cores": nt, "kind": "oracle",
-            "sample": f"{done} chunks of [24, 7040, 128] K and V (layer 0 chunk 0 to layer {last[0]} chunk "
-                      f"{last[1]}): smooth-quantize + dequantize",
-            "seconds": round(t_total, 2)}
+    chunk_bytes = 2 * (kv_bytes(H, L, D, L, True) + kv_bytes(H, L, D, L, False))
+
+    def run(nt, budget_s):
+        done, t_total, last = 0, 0.0, (0, 0)
+        for l in range(len(ks)):
+            for c in range(T // L):
+                kb = W.bf16_bits(ks[l][:, c * L:(c + 1) * L])
+                vb = W.bf16_bits(vs[l][:, c * L:(c + 1) * L])
+                t0 = time.perf_counter()
+                r = O.smooth_quantize(kb, vb, L, mode, nthreads=nt)
+                O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], r["k_mean"], L, nthreads=nt)
+                O.dequantize(r["v_codes"], r["v_scales"], r["v_tensor_scale"], None, L, nthreads=nt)
+                t_total += time.perf_counter() - t0
+                done += 1
+                last = (l, c)
+                if t_total >= budget_s:
+                    return done, t_total, last
+        return done, t_total, last
+
+    nt = O.default_threads()
+    done, t_total, last = run(nt, target_s)
+    done1, t1, last1 = run(1, target_s / 2)
+    sample = lambda n, lc: (f"{n} chunks of [{H}, {L}, {D}] K and V (layer 0 chunk 0 to layer {lc[0]} chunk "  # noqa: E731
+                            f"{lc[1]}): smooth-quantize + dequantize")
+    out = {"value": round(done * chunk_bytes / t_total / 1e9, 3), "unit": "GB/s", "cores": nt, **host_cores(),
+           "kind": "oracle", "sample": sample(done, last), "seconds": round(t_total, 2), "threads_used": nt}
+    out["single_thread"] = {"value": round(done1 * chunk_bytes / t1 / 1e9, 4), "unit": "GB/s", "threads_used": 1,
+                            "sample": sample(done1, last1), "seconds": round(t1, 2)}
+    if check is not None:
+        import numpy as np
+        o, (dk, dv) = check
+        rows = slice(0, L)
+        kb, vb = W.bf16_bits(ks[0][:, rows]), W.bf16_bits(vs[0][:, rows])
+        gm = o["k_mean"][0:1].cpu().numpy()
+        x = O.bf16_to_float(kb).astype(np.float64)
+        m_ref = x.mean(1)[None]
+        tol = 1e-6 * np.maximum(np.abs(m_ref), np.abs(x).mean(1)[None])
+        mean_ok = bool((np.abs(gm.astype(np.float64) - m_ref) <= tol).all())
+        r = O.smooth_quantize(kb, vb, L, mode, k_mean=gm, nthreads=nt)
+        same = {key: bool(np.array_equal(o[key][:, rows].cpu().numpy(), r[key]))
+                for key in ("k_codes", "v_codes", "k_scales", "v_scales")}
+        for key in ("k_tensor_scale", "v_tensor_scale"):
+            same[key] = bool(np.array_equal(o[key][0:1].cpu().numpy().view(np.uint32), r[key].view(np.uint32)))
+        rk = O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], gm, L, nthreads=nt)
+        rv = O.dequantize(r["v_codes"], r["v_scales"], r["v_tensor_scale"], None, L, nthreads=nt)
+        same["dequant_k"] = bool(np.array_equal(W.bf16_bits(dk[:, rows]), rk))
+        same["dequant_v"] = bool(np.array_equal(W.bf16_bits(dv[:, rows]), rv))
+        out["parity_check"] = {"sample": "layer 0, chunk 0 of the last timed step", "mean_rule": mean_ok,
+                               "bit_exact": mean_ok and all(same.values()), "fields": same}
+    return out
 
 
 if __name__ == "__main__":

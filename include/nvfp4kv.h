@@ -103,12 +103,14 @@ NVFP4KV_API const char* nvfp4_status_string(int status) NVFP4KV_NOEXCEPT;
  * invalid shape).  Host function, no HIP call. */
 NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int chunk_len) NVFP4KV_NOEXCEPT;
 
-/* Byte offset, inside the workspace of nvfp4_kv_smooth_quantize, of the
- * 32-bit error word of the default (overlapped) kernel for this shape, or -1
- * when the shape takes the two-pass kernels (which never wait).  Each call
- * clears the word; once the call has completed (the stream synchronized), a
- * non-zero value there means one of the kernel's bounded waits timed out and
- * the call's outputs are invalid.  Host function, no HIP call. */
+/* Byte offset, inside the workspace of nvfp4_kv_smooth_quantize, of its
+ * sticky 32-bit error word: 0 (the first word) for every valid shape, -1 for
+ * an invalid one.  The word belongs to the caller: the library never clears
+ * it.  A call whose overlapped kernel had one of its bounded waits time out
+ * sets it to non-zero, and that call's outputs are invalid; so a zero word,
+ * read once the stream has synchronized, vouches for every call on the
+ * workspace since the caller last zeroed it.  The two-pass kernels never wait
+ * and never set it.  Host function, no HIP call. */
 NVFP4KV_API long long nvfp4_kv_error_word_offset(int H, int T, int D, int chunk_len) NVFP4KV_NOEXCEPT;
 
 /*
@@ -124,18 +126,24 @@ NVFP4KV_API long long nvfp4_kv_error_word_offset(int H, int T, int D, int chunk_
  *   k_scales, v_scales   out, E4M3FN bytes [H, T, D/16].
  *   k_tensor_scale, v_tensor_scale  out, fp32 [n_chunks], g_dec per chunk.
  *   k_mean        out, fp32 [n_chunks, H, D]: the per-chunk channel mean of K
- *                 (sum over the chunk's tokens, rounded once to fp32), 16-byte
- *                 aligned.  Pass it to nvfp4_dequantize to restore K.
+ *                 over the chunk's tokens, 16-byte aligned.  The overlapped
+ *                 kernel adds the tokens in fp32 runs of 8 and the runs in
+ *                 fp64, so the mean is within 8 * 2^-24 * max(|m|, mean |K|)
+ *                 of the exact one (the two-pass kernels add every token in
+ *                 fp64).  Pass it to nvfp4_dequantize to restore K.
  *   choice_counts out, nullable, uint64 [2][2]: {K, V} x {blocks that kept +-6,
  *                 blocks that kept +-4}; overwritten by this call.
  *   workspace     device scratch of at least nvfp4_kv_workspace_bytes(),
- *                 256-byte aligned; contents on entry are ignored.  Calls
- *                 that share a workspace must be ordered on one stream.
+ *                 256-byte aligned.  Its first 256 bytes are a header whose
+ *                 first word is the sticky error word (zero it before the
+ *                 first call); the rest of the contents on entry are
+ *                 ignored.  Calls that share a workspace must be ordered on
+ *                 one stream.
  *
  * The overlapped kernel's quantize tiles wait, through words in the
  * workspace, for statistics tiles that precede them in the grid; each wait
- * is bounded, and if one ever timed out the tile would stop early and leave
- * its results invalid (the workspace's error word is then non-zero).
+ * is bounded, and if one ever timed out the tile would stop early, leave its
+ * results invalid and set the sticky error word.
  *
  * Smoothing: k' = fl(K - mean) in fp32.  V is quantized as is.
  */
@@ -195,7 +203,18 @@ NVFP4KV_API int nvfp4_quantize_2d(const uint16_t* w, int rows, int cols, int mod
                                   uint8_t* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
                                   void* stream) NVFP4KV_NOEXCEPT;
 
-/* Dequantize a 2D-tile tensor: out bf16 [rows, cols] (16-byte aligned). */
+/*
+ * Dequantize a weight quantized with 2D tiles (the inverse of
+ * nvfp4_quantize_2d; training pipeline, step 4: weights carry one block
+ * scale per 16x16 tile).  Every element of tile (r / 16, c / 16) decodes as
+ * bf16((v * S_tile) * g_dec), each step one fp32 rounding.
+ *
+ *   codes         uint8 [rows, cols/2] (8-byte aligned), low nibble = even column.
+ *   scales        E4M3FN bytes [rows/16, cols/16].
+ *   tensor_scale  fp32 [1], g_dec.
+ *   out           bf16 [rows, cols], 16-byte aligned; must not overlap an input.
+ * rows % 16 == 0 and cols % 16 == 0, else NVFP4_ERR_SHAPE.
+ */
 NVFP4KV_API int nvfp4_dequantize_2d(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                                     int rows, int cols, uint16_t* out, void* stream) NVFP4KV_NOEXCEPT;
 
@@ -315,11 +334,11 @@ NVFP4KV_API int nvfp4_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
  *   scales        out, E4M3FN [H, D, T/16].
  *   tensor_scale  out, fp32 [T / chunk_len], g_dec per chunk.
  *   workspace     >= nvfp4_kv_quantize_v_tblocks_workspace_bytes(), 256-byte
- *                 aligned; contents on entry ignored.  Its first 32-bit word
- *                 is the error word of the single-launch kernel: each call
- *                 clears it, and once the call has completed a non-zero value
- *                 means one of the kernel's bounded waits timed out and the
- *                 outputs are invalid.
+ *                 aligned.  Its first 32-bit word is a sticky error word that
+ *                 the library never clears (zero it before the first call):
+ *                 a call whose bounded waits timed out sets it, and that
+ *                 call's outputs are invalid.  The rest of the contents on
+ *                 entry are ignored.
  * Every block is encoded exactly as the blocks of nvfp4_kv_smooth_quantize's
  * V: z = fl(v * g_enc) with g_enc = fl(C / A), A the chunk's largest |V|, the
  * 4/6 choice on fp32 errors, E2M1 round to nearest even.

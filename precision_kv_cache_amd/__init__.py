@@ -110,9 +110,16 @@ def nvfp4_kv_workspace_bytes(H, T, D, chunk_len):
     return int(lib().nvfp4_kv_workspace_bytes(H, T, D, chunk_len))
 
 
+def kv_error_word(workspace):
+    """The sticky error word of a KV or V-tblocks workspace, read after a
+    synchronize (a device-to-host copy of its first 4 bytes)."""
+    return int(workspace[:4].view(torch.int32).cpu()[0])
+
+
 def nvfp4_kv_error_word_offset(H, T, D, chunk_len):
-    """Byte offset of the overlapped kernel's error word in the workspace, or
-    -1 for shapes that take the two-pass kernels."""
+    """Byte offset of the workspace's sticky error word (0; -1 for an invalid
+    shape).  The library never clears it; non-zero means some call on the
+    workspace since it was last zeroed had a wait time out."""
     return int(lib().nvfp4_kv_error_word_offset(H, T, D, chunk_len))
 
 
@@ -152,7 +159,7 @@ def nvfp4_kv_smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, choice_counts=Fa
             out["choice_counts"] = torch.empty(2, 2, dtype=torch.int64, device=dev)
     ws_bytes = nvfp4_kv_workspace_bytes(H, T, D, chunk_len)
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # sticky error word starts at 0
     rc = lib().nvfp4_kv_smooth_quantize(
         _ptr(k), _ptr(v), H, T, D, chunk_len, mode | (KV_TWO_PASS if two_pass else 0), _ptr(out["k_codes"]), _ptr(out["v_codes"]),
         _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
@@ -297,7 +304,7 @@ def nvfp4_kv_quantize_v_tblocks(v, chunk_len, mode=MODE_4OVER6, out=None, worksp
                "scales": torch.empty(H, D, T // 16, dtype=torch.uint8, device=v.device),
                "tensor_scale": torch.empty(nc, dtype=torch.float32, device=v.device)}
     if workspace is None:
-        workspace = torch.empty(max(1, int(lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, chunk_len))),
+        workspace = torch.zeros(max(1, int(lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, chunk_len))),
                                 dtype=torch.uint8, device=v.device)
     rc = lib().nvfp4_kv_quantize_v_tblocks(_ptr(v), H, T, D, chunk_len, mode, _ptr(out["codes"]), _ptr(out["scales"]),
                                            _ptr(out["tensor_scale"]), _ptr(workspace), workspace.numel(),
@@ -348,7 +355,7 @@ class KVCache:
         st = self.state
         ws_bytes = nvfp4_kv_workspace_bytes(st.heads, st.chunk_len, st.head_dim, st.chunk_len)
         if workspace is None:
-            workspace = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=k.device)
+            workspace = torch.zeros(max(1, ws_bytes), dtype=torch.uint8, device=k.device)
         rc = lib().nvfp4_kv_cache_append(ctypes.byref(st), _ptr(self.storage), self.storage_bytes, layer, _ptr(k),
                                          _ptr(v), mode, _ptr(workspace), workspace.numel(), _stream(stream))
         _check(rc, "nvfp4_kv_cache_append")

@@ -53,6 +53,15 @@ constexpr int kSBatch = 4;                            // rows in flight per stat
 constexpr int kQBatch = 2;                            // rows in flight per quantize lane
 constexpr int kReplicaStride = 32;                    // 64-bit words between ready words (256 B)
 constexpr int kWaves = kOvThreads / 64;
+// K channel sums: each lane adds its rows in fp32 runs of kRunBatches
+// batches (kRunBatches * kSBatch = 8 rows) and folds every run into fp64.  A
+// run of n rows has at most n - 1 fp32 roundings, each at most 2^-24 of the
+// run's magnitude sum, so the channel sum is within 7 * 2^-24 * sum |K| of
+// the exact one and the rounded mean within 8 * 2^-24 * max(|m|, mean |K|):
+// inside the 1e-6 acceptance of the mean, at a quarter of the per-element
+// issue cost of fp64 adds (the fp32 -> fp64 convert is a half-rate
+// instruction).
+constexpr int kRunBatches = 2;
 
 __device__ __forceinline__ unsigned long long load64_agent(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -131,9 +140,11 @@ __device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rs, uint32_t v
   __builtin_amdgcn_sched_barrier(0);  // all loads of the batch in flight before any use
 }
 
-// K statistics of one batch: fp64 channel sums, channel max and min.
+// K statistics of one batch: fp32 channel sums of the batch's rows added to
+// the running fp32 run sums r (a lane folds them into fp64 every
+// kRunBatches batches), channel max and min.
 template <bool GUARD>
-__device__ __forceinline__ void k_stats_batch(const uint4 (&a)[kSBatch], int r, int r1, double (&s)[8],
+__device__ __forceinline__ void k_stats_batch(const uint4 (&a)[kSBatch], int r, int r1, float (&rs)[8],
                                               float (&mx)[8], float (&mn)[8]) {
 #pragma unroll
   for (int q = 0; q < kSBatch; ++q) {
@@ -142,12 +153,21 @@ __device__ __forceinline__ void k_stats_batch(const uint4 (&a)[kSBatch], int r, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-      s[2 * j] += (double)lo;
-      s[2 * j + 1] += (double)hi;
+      rs[2 * j] += lo;
+      rs[2 * j + 1] += hi;
       mx[2 * j] = fmaxf(mx[2 * j], lo); mn[2 * j] = fminf(mn[2 * j], lo);
       mx[2 * j + 1] = fmaxf(mx[2 * j + 1], hi); mn[2 * j + 1] = fminf(mn[2 * j + 1], hi);
     }
     if (q & 1) __builtin_amdgcn_sched_barrier(0);  // two rows at a time: bounded live values
+  }
+}
+
+// fp64 channel sums += the fp32 run sums, which restart from 0.
+__device__ __forceinline__ void fold_runs(double (&s)[8], float (&rs)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s[i] += (double)rs[i];
+    rs[i] = 0.0f;
   }
 }
 
@@ -191,20 +211,25 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
 
   if (tau == 0) {
     double s[8];
-    float mx[8], mn[8];
+    float run[8], mx[8], mn[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { s[i] = 0.0; mx[i] = -INFINITY; mn[i] = INFINITY; }
+    for (int i = 0; i < 8; ++i) { s[i] = 0.0; run[i] = 0.0f; mx[i] = -INFINITY; mn[i] = INFINITY; }
     // whole batches unguarded (no per-row branch, so the compiler keeps the
     // running max / min as plain v_max3 / v_min3), then one guarded batch
     uint4 ld[kSBatch];
     for (int b = 0; b < nfull; ++b) {
       load_batch<false>(rs, voff, (uint32_t)(r0 + b * kBatchRows) * kD * 2, 0, 0, ld);
-      k_stats_batch<false>(ld, 0, 0, s, mx, mn);
+      k_stats_batch<false>(ld, 0, 0, run, mx, mn);
+      if (b % kRunBatches == kRunBatches - 1) fold_runs(s, run);
     }
+    // the open run holds at most kRunBatches - 1 = 1 batch, so the guarded
+    // batch keeps it within kRunBatches batches
+    static_assert(kRunBatches == 2, "the guarded batch joins the open run");
     if (rrest + roff < r1) {
       load_batch<true>(rs, voff, (uint32_t)rrest * kD * 2, rrest + roff, r1, ld);
-      k_stats_batch<true>(ld, rrest + roff, r1, s, mx, mn);
+      k_stats_batch<true>(ld, rrest + roff, r1, run, mx, mn);
     }
+    fold_runs(s, run);
     // the 4 rows of a wave (lanes hc, hc + 16, hc + 32, hc + 48), in a fixed order
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -370,6 +395,7 @@ __device__ void quant_tile(const OverlapParams& p, int u, int h, int qt, unsigne
       ++it;
       if (it > p.spin_limit || ((it & 255u) == 0u && load_agent(p.err) != 0u)) {
         atomicOr(p.err, 1u);
+        atomicOr(p.err_sticky, 1u);
         ok = false;
         break;
       }
@@ -436,7 +462,7 @@ OverlapLayout overlap_layout(int H, int nc, int nst, int nqt) {
   OverlapLayout l;
   const int U = 2 * nc;
   const size_t part = (size_t)nc * H * nst * kD;
-  size_t off = 0;
+  size_t off = kKvWorkspaceHeader;  // the sticky error word's block
   l.ksum = off;   off = align_up(off + part * sizeof(double), 256);
   l.kext = off;   off = align_up(off + part * sizeof(uint32_t), 256);
   l.vmax = off;   off = align_up(off + (size_t)nc * H * nst * sizeof(float), 256);
@@ -457,17 +483,6 @@ size_t overlap_workspace_bound(int H, int T, int D, int L) {
   const int nst = (L + kOvStatsRows - 1) / kOvStatsRows;
   const int nqt = (L + kOvQuantRows - 1) / kOvQuantRows;
   return overlap_layout(H, T / L, nst, nqt).total;
-}
-
-long long overlap_error_offset(int H, int T, int D, int L) {
-  if (D != kD || H <= 0 || L <= 0 || T <= 0 || T % L != 0) return -1;
-  const int nc = T / L;
-  const int nst = (L + kOvStatsRows - 1) / kOvStatsRows;
-  const int nqt = (L + kOvQuantRows - 1) / kOvQuantRows;
-  const long long grid = 2LL * nc * H * ((long long)nst + nqt);
-  if (grid >= (1LL << 24) || (long long)L * kD * 2 >= (1LL << 31)) return -1;  // as overlap_try_launch
-  const OverlapLayout l = overlap_layout(H, nc, nst, nqt);
-  return (long long)(l.counters + ((size_t)2 * nc * H + 2 * nc) * sizeof(unsigned));
 }
 
 __global__ void overlap_zero_kernel(unsigned* p, int n) {
@@ -498,6 +513,7 @@ int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_byt
   p.cnt_head = cnt;
   p.cnt_unit = cnt + (size_t)U * p.H;
   p.err = p.cnt_unit + U;
+  p.err_sticky = reinterpret_cast<unsigned*>(ws);
   p.choice = choice != nullptr;
   p.depth = kOvDepth;
   p.spin_limit = kOvSpinLimit;

@@ -29,7 +29,8 @@ struct OverlapParams {
   unsigned long long* ready; // [kOvReplicas][U], 256 bytes apart: 1 << 32 | encode-scale bits once the unit is ready
   unsigned* cnt_head;        // [U][H] finished statistics tiles of a head
   unsigned* cnt_unit;        // [U] finished heads of a unit
-  unsigned* err;             // [1] set when a wait timed out
+  unsigned* err;             // [1] set when a wait of this call timed out (cleared per call)
+  unsigned* err_sticky;      // [1] the workspace's first word: also set then, never cleared here
   uint32_t* tally;           // [U * nq][4] per-quantize-tile 4/6 choice counts (when choice)
   int choice;
   int H, T, L, nc, nst, nqt, depth;
@@ -43,8 +44,9 @@ struct OverlapLayout {
 
 OverlapLayout overlap_layout(int H, int nc, int nst, int nqt);
 size_t overlap_workspace_bound(int H, int T, int D, int L);
-// byte offset of the error word in the workspace, -1 when the form does not apply
-long long overlap_error_offset(int H, int T, int D, int L);
+// Bytes at the start of every KV workspace that no per-call clearing touches:
+// the sticky error word (offset 0) and padding to 256 bytes.
+constexpr size_t kKvWorkspaceHeader = 256;
 // NVFP4_OK after enqueueing (and the choice-count reduction when choice is
 // set), a positive value when this form does not apply to the shape, or
 // NVFP4_ERR_HIP.

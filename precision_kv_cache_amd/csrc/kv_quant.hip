@@ -73,7 +73,7 @@ struct KVWorkspace {
 static KVWorkspace kv_workspace_layout(const KVGeom& g) {
   KVWorkspace w;
   const size_t nch = (size_t)g.nc * g.H * g.nst * g.D;
-  size_t off = 0;
+  size_t off = kKvWorkspaceHeader;  // the sticky error word's block, shared with the overlapped form
   w.psum = off;  off = align_up(off + nch * sizeof(double), 256);
   w.pmax = off;  off = align_up(off + nch * sizeof(float), 256);
   w.pmin = off;  off = align_up(off + nch * sizeof(float), 256);
@@ -506,7 +506,7 @@ extern "C" NVFP4KV_API size_t nvfp4_kv_workspace_bytes(int H, int T, int D, int 
 
 extern "C" NVFP4KV_API long long nvfp4_kv_error_word_offset(int H, int T, int D, int chunk_len) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len) || H == 0 || T == 0) return -1;
-  return overlap_error_offset(H, T, D, chunk_len);
+  return 0;  // the first word of the header block, in both kernel forms' layouts
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
@@ -527,14 +527,15 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
     return NVFP4_ERR_ALIGN;
   const KVGeom g = kv_geom(H, T, D, chunk_len);
   const KVWorkspace wl = kv_workspace_layout(g);
-  if (!workspace || workspace_bytes < nvfp4_kv_workspace_bytes(H, T, D, chunk_len)) return NVFP4_ERR_WORKSPACE;
+  const size_t ws_need = nvfp4_kv_workspace_bytes(H, T, D, chunk_len);
+  if (!workspace || workspace_bytes < ws_need) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   const size_t n = (size_t)H * T * D;
   const Range in[2] = {range_of(k, n * 2), range_of(v, n * 2)};
   const Range out[10] = {range_of(k_codes, n / 2), range_of(v_codes, n / 2), range_of(k_scales, n / 16),
                          range_of(v_scales, n / 16), range_of(k_tensor_scale, (size_t)g.nc * 4),
                          range_of(v_tensor_scale, (size_t)g.nc * 4), range_of(k_mean, (size_t)g.nc * H * D * 4),
-                         range_of(choice_counts, 32), range_of(workspace, wl.total), Range{0, 0}};
+                         range_of(choice_counts, 32), range_of(workspace, ws_need), Range{0, 0}};
   if (any_alias(in, 2, out, 9)) return NVFP4_ERR_ALIAS;
 
   hipStream_t s = as_stream(stream);

@@ -47,24 +47,29 @@ struct VtParams {
   float* tscale;
   float* partial;             // [nc][H][nst] largest |V| per statistics tile
   unsigned long long* ready;  // [kVtReplicas][nc], 256 B apart: 1 << 32 | encode-scale bits once ready
-  unsigned* err;              // [1 + nc]: error word, then per-chunk finished statistics tiles
+  unsigned* err;              // [1 + nc]: this call's error word, then per-chunk finished statistics tiles
+  unsigned* err_sticky;       // the workspace's first word: set on a time-out too, never cleared here
   float C;
   int H, T, D, L, nc, tpc, ncg, nst, depth;
   unsigned spin_limit;
 };
 
-// Workspace: error word and counters, ready words, partial maxima.
+// Workspace: a 256-byte header (the sticky error word first), this call's
+// error word and counters, ready words, partial maxima.
 struct VtLayout {
-  size_t ready, partial, total;
-  size_t n_zero_words;  // error word .. end of the ready words, cleared before the launch
+  size_t err, ready, partial, total;
+  size_t n_zero_words;  // this call's error word .. end of the ready words, cleared before the launch
 };
+
+constexpr size_t kVtHeader = 256;
 
 VtLayout vt_layout(int H, int nc, int nst) {
   VtLayout l;
-  size_t off = align_up((size_t)(1 + nc) * sizeof(unsigned), 256);
+  l.err = kVtHeader;
+  size_t off = kVtHeader + align_up((size_t)(1 + nc) * sizeof(unsigned), 256);
   l.ready = off;
   off += (size_t)kVtReplicas * nc * kVtReplicaStride * sizeof(unsigned long long);
-  l.n_zero_words = off / sizeof(unsigned);
+  l.n_zero_words = (off - l.err) / sizeof(unsigned);
   l.partial = off;
   off = align_up(off + (size_t)nc * H * nst * sizeof(float), 256);
   l.total = off;
@@ -177,6 +182,7 @@ __device__ void vt_quant_tile(const VtParams& p, int c, int j, int h, int cg, ui
       ++it;
       if (it > p.spin_limit || ((it & 255u) == 0u && load_agent(p.err) != 0u)) {
         atomicOr(p.err, 1u);
+        atomicOr(p.err_sticky, 1u);
         ok = false;
         break;
       }
@@ -275,7 +281,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H,
   const VtLayout l = vt_layout(H, p.nc, p.nst);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   p.v = v; p.codes = codes; p.scales = scales; p.tscale = tensor_scale;
-  p.err = reinterpret_cast<unsigned*>(ws);
+  p.err = reinterpret_cast<unsigned*>(ws + l.err);
+  p.err_sticky = reinterpret_cast<unsigned*>(ws);
   p.ready = reinterpret_cast<unsigned long long*>(ws + l.ready);
   p.partial = reinterpret_cast<float*>(ws + l.partial);
   hipStream_t s = as_stream(stream);

@@ -53,12 +53,12 @@ def gpu_kv(kb, vb, L, mode=O.MODE_4OVER6, counts=True, path=None):
     v = W.from_bits(vb, "cuda")
     H, T, D = kb.shape
     ws = torch.full((max(1, P.nvfp4_kv_workspace_bytes(H, T, D, L)),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws[:4] = 0  # the sticky error word is the caller's to clear
     out = P.nvfp4_kv_smooth_quantize(k, v, L, mode, choice_counts=counts, **(path or {}),
                                      out=kv_outputs(H, T, D, L, counts), workspace=ws)
     torch.cuda.synchronize()
-    off = P.nvfp4_kv_error_word_offset(H, T, D, L)
-    if off >= 0 and not (path or {}).get("two_pass"):
-        assert int(ws[off:off + 4].cpu().view(torch.int32)[0]) == 0, "a wait of the overlapped kernel timed out"
+    assert P.nvfp4_kv_error_word_offset(H, T, D, L) == 0
+    assert P.kv_error_word(ws) == 0, "a wait of the overlapped kernel timed out"
     return {key: t.cpu().numpy() for key, t in out.items()}, out
 
 

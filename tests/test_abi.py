@@ -51,11 +51,11 @@ def test_workspace_sizes():
     assert P.nvfp4_kv_workspace_bytes(24, 56320, 128, 7040) > P.nvfp4_kv_workspace_bytes(24, 7040, 128, 7040)
     for bad in ((24, 7040, 100, 7040), (24, 7041, 128, 7040), (-1, 10, 16, 10), (1, 16, 8192, 16), (1, 16, 16, 0)):
         assert P.nvfp4_kv_workspace_bytes(*bad) == 0, bad
-    # the error word lies inside the workspace; shapes without the overlapped kernel have none
-    for shape in ((24, 7040, 128, 7040), (24, 56320, 128, 7040), (1, 256, 128, 256), (3, 77, 128, 7)):
-        off = P.nvfp4_kv_error_word_offset(*shape)
-        assert 0 <= off and off + 4 <= P.nvfp4_kv_workspace_bytes(*shape) and off % 4 == 0, shape
-    assert P.nvfp4_kv_error_word_offset(2, 96, 48, 32) == -1      # D != 128: two-pass kernels
+    # the sticky error word is the workspace's first word for every valid shape
+    for shape in ((24, 7040, 128, 7040), (24, 56320, 128, 7040), (1, 256, 128, 256), (3, 77, 128, 7),
+                  (2, 96, 48, 32)):
+        assert P.nvfp4_kv_error_word_offset(*shape) == 0, shape
+        assert P.nvfp4_kv_workspace_bytes(*shape) >= 256 + 4, shape
     assert P.nvfp4_kv_error_word_offset(24, 7041, 128, 7040) == -1  # invalid shape
     assert P.lib().nvfp4_quantize_1d_workspace_bytes(16, 48) > 0
     assert P.lib().nvfp4_quantize_2d_workspace_bytes(24, 48) == 0  # rows % 16
@@ -91,6 +91,19 @@ def test_kv_quantize_argument_errors():
     assert _kvq(vc=FAKE + (2 << 30) + 256) == ALIAS  # two outputs overlap
     assert _kvq(ws=FAKE + (1 << 30)) == ALIAS     # workspace inside V
     assert _kvq(cc=FAKE + (5 << 30)) == ALIAS     # counts inside v_scales
+
+
+def test_kv_quantize_output_in_workspace_tail_is_an_alias():
+    # The overlapped kernel uses more workspace than the two-pass kernels for
+    # small shapes; every byte nvfp4_kv_workspace_bytes covers is the
+    # library's, so an output anywhere in it is rejected.
+    H, T, D, L = 1, 256, 128, 256
+    need = P.nvfp4_kv_workspace_bytes(H, T, D, L)
+    ws = FAKE + (9 << 30)
+    assert need > 4096
+    for off in (0, 4096, need - 256):
+        assert _kvq(H=H, T=T, D=D, L=L, kc=ws + off, ws=ws, wsb=need) == ALIAS, off
+        assert _kvq(H=H, T=T, D=D, L=L, km=ws + off, ws=ws, wsb=need) == ALIAS, off
 
 
 def test_empty_calls_are_no_ops():

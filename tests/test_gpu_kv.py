@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import precision_kv_cache_amd as P
 import workloads as W
-from gpu_helpers import SENTINEL, check_kv, gpu_kv, kv_outputs, say, to_np
+from gpu_helpers import SENTINEL, check_kv, gpu_kv, kv_outputs, mean_rule, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -35,10 +35,17 @@ def test_tiny_workload(mode, path):
 def test_tiny_matches_golden_fixture():
     say("tiny KV vs golden fixture")
     g = np.load(__import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "tiny_kv_oracle.npz"))
-    res, _ = gpu_kv(g["k"], g["v"], W.TINY.chunk_len)
-    if np.array_equal(res["k_mean"], g["k_mean"]):  # same mean -> same bytes as the stored oracle run
-        for key in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tensor_scale", "v_tensor_scale"):
-            assert np.array_equal(res[key], g[key]), key
+    L = W.TINY.chunk_len
+    res, _ = gpu_kv(g["k"], g["v"], L)
+    ok, worst = mean_rule(g["k"], L, res["k_mean"])
+    assert ok, f"K mean outside the 1e-6 rule (worst ratio {worst:.3g})"
+    # The stored bytes are the oracle's with its own mean.  When the GPU mean
+    # differs (it only has to meet the 1e-6 rule), the oracle is run again
+    # with the GPU mean, as for every other parity case.
+    ref = g if np.array_equal(res["k_mean"], g["k_mean"]) else O.smooth_quantize(g["k"], g["v"], L,
+                                                                                 k_mean=res["k_mean"])
+    for key in ("k_codes", "v_codes", "k_scales", "v_scales", "k_tensor_scale", "v_tensor_scale"):
+        assert np.array_equal(res[key], ref[key]), key
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
@@ -75,14 +82,14 @@ def test_full_cache_layer_sampled(layer, path):
     say("full-cache layer", layer, s, "seed", W.cache_layer_seed(layer), "path", path)
     k, v = W.gaussian_kv(s, W.cache_layer_seed(layer), device="cuda")
     ws = torch.full((P.nvfp4_kv_workspace_bytes(s.H, s.T, s.D, s.chunk_len),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws[:4] = 0  # the sticky error word
     out = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, **path,
                                      out=kv_outputs(s.H, s.T, s.D, s.chunk_len), workspace=ws)
     dk = P.nvfp4_dequantize(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], s.chunk_len)
     dv = P.nvfp4_dequantize(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, s.chunk_len)
     torch.cuda.synchronize()
     if not path.get("two_pass"):
-        off = P.nvfp4_kv_error_word_offset(s.H, s.T, s.D, s.chunk_len)
-        assert int(ws[off:off + 4].cpu().view(torch.int32)[0]) == 0, "a wait of the overlapped kernel timed out"
+        assert P.kv_error_word(ws) == 0, "a wait of the overlapped kernel timed out"
     L = s.chunk_len
     for c in (0, 3, 7):
         say("  chunk", c)
@@ -161,9 +168,9 @@ def test_degenerate_values():
 
 
 def test_deterministic_and_stream_ordered():
-    """Repeated calls on a side stream give identical bytes, and the
-    overlapped and two-pass kernels agree, mean included (the same fp64
-    channel sums: exact for these inputs)."""
+    """Repeated calls on a side stream give identical bytes (each kernel form
+    adds in a fixed order), and both forms meet the mean rule; where their
+    means agree bit for bit, so does everything else."""
     s = W.KVShape(4, 2048, 128, 1024)
     say("determinism", s)
     k, v = W.gaussian_kv(s, 99, device="cuda")
@@ -181,6 +188,18 @@ def test_deterministic_and_stream_ordered():
     for key in a:
         assert torch.equal(a[key], b[key]), key
         assert torch.equal(c[key], d[key]), key
+    kb = W.bf16_bits(k)
+    for r in (a, c):
+        ok, worst = mean_rule(kb, s.chunk_len, r["k_mean"].cpu().numpy())
+        assert ok, worst
+    same = (a["k_mean"] == c["k_mean"]).all(dim=-1)  # [chunk, head]: the unit a tensor scale spans is the chunk
+    for ch in range(s.T // s.chunk_len):
+        if bool(same[ch].all()):
+            rows = slice(ch * s.chunk_len, (ch + 1) * s.chunk_len)
+            for key in ("k_codes", "k_scales"):
+                assert torch.equal(a[key][:, rows], c[key][:, rows]), (ch, key)
+            assert torch.equal(a["k_tensor_scale"][ch], c["k_tensor_scale"][ch]), ch
+    for key in ("v_codes", "v_scales", "v_tensor_scale"):  # V takes no mean
         assert torch.equal(a[key], c[key]), key
 
 

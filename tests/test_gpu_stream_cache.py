@@ -18,7 +18,7 @@ import torch
 import oracle as O
 import precision_kv_cache_amd as P
 import workloads as W
-from gpu_helpers import attention_check, say
+from gpu_helpers import attention_check, mean_rule, say
 
 pytestmark = pytest.mark.gpu
 
@@ -65,13 +65,15 @@ def test_streamed_chunks(geom):
             cache.append(layer, W.from_bits(kb, "cuda"), W.from_bits(vb, "cuda"))
         torch.cuda.synchronize()
         for layer, (kb, vb) in enumerate(inputs):
-            ref = O.smooth_quantize(kb, vb, L)
             got = {key: t[slot].cpu().numpy() for key, t in cache.slot_arrays(layer).items()
                    if key not in ("k_tensor_scale", "v_tensor_scale")}
             ts = cache.slot_arrays(layer)
             got["k_tensor_scale"] = ts["k_tensor_scale"][slot:slot + 1].cpu().numpy()
             got["v_tensor_scale"] = ts["v_tensor_scale"][slot:slot + 1].cpu().numpy()
             got["k_mean"] = got["k_mean"][None]
+            ok, worst = mean_rule(kb, L, got["k_mean"])
+            assert ok, (ch, layer, worst)
+            ref = O.smooth_quantize(kb, vb, L, k_mean=got["k_mean"])  # parity given the GPU mean
             for key in ("k_codes", "v_codes", "k_scales", "v_scales"):
                 assert np.array_equal(got[key], ref[key]), (ch, layer, key)
             for key in ("k_tensor_scale", "v_tensor_scale", "k_mean"):

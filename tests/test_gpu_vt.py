@@ -25,6 +25,7 @@ def _run(vb, L, mode):
            "tensor_scale": torch.full((T // L,), -1.0, dtype=torch.float32, device="cuda")}
     ws = torch.full((max(1, P.lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, L)),), 0xA5,
                     dtype=torch.uint8, device="cuda")
+    ws[:4] = 0  # the sticky error word is the caller's to clear
     P.nvfp4_kv_quantize_v_tblocks(v, L, mode, out=out, workspace=ws)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0, "a wait of the single-launch kernel timed out"
