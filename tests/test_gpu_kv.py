@@ -129,7 +129,7 @@ def test_full_cache_layer_sampled(layer, path):
     (600, 32, 128, 32),  # many heads, one short chunk
     (1, 204800, 128, 204800),  # one head, one 204800-row chunk (400 statistics tiles)
 ])
-@pytest.mark.parametrize("path", [{}, {"two_pass": True}], ids=["overlap", "two-pass"])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_ragged_and_odd_shapes(H, T, D, L, path):
     say("shape", (H, T, D, L), "path", path)
     shape = W.KVShape(H, T, D, L)
@@ -145,9 +145,10 @@ def _bits(a):
     return W.bf16_bits(torch.as_tensor(np.asarray(a, np.float32)).to(torch.bfloat16))
 
 
-def test_degenerate_values():
+@pytest.mark.parametrize("D", [32, 128])  # 128: the overlapped kernel takes it
+def test_degenerate_values(D):
     rng = np.random.default_rng(77)
-    H, T, D, L = 2, 64, 32, 32
+    H, T, L = 2, 64, 32
     cases = {
         "zeros": (np.zeros((H, T, D)), np.zeros((H, T, D))),
         "signed zeros": (-np.zeros((H, T, D)), -np.zeros((H, T, D))),
