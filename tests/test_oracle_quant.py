@@ -30,6 +30,120 @@ def _unpack(codes):
     return np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
 
 
+# ------------------------------------------- order of the fp32 error sum ----
+# The fixtures under "summation_order" are hand-derived (the golden file spells
+# out every partial sum): blocks whose exact errors tie or nearly tie, so the
+# fixed fp32 summation order of the convention decides the 4/6 choice, and a
+# different order (one 16-term chain for a 1D block, sequential tile rows for
+# a 2D tile) decides the other way.
+
+def _order_fixture():
+    return json.load(open(os.path.join(GOLDEN, "four_over_six_examples.json")))["summation_order"]
+
+
+def _hx(h):
+    return np.float32(float.fromhex(h))
+
+
+def test_summation_order_1d_block():
+    fx = _order_fixture()["block_1d"]
+    z = np.array([float.fromhex(h) for h in fx["z"]], np.float32)
+    x = np.zeros((1, 1, 32), np.uint16)
+    x[0, 0, :16] = _bits(np.array([1792.0] + [0.0] * 15))
+    mean = np.zeros((1, 1, 32), np.float32)
+    mean[0, 0, 16:] = -z  # smoothed value fl(0 - (-z)) = z exactly
+    q = O.quantize_chunks(x, 1, O.MODE_4OVER6, mean=mean, want_errors=True)
+    assert q["tensor_scale"][0] == 1.0  # g_enc = 1792 / 1792: the encode domain is z itself
+    assert q["err6"][0, 0, 1] == _hx(fx["err6"]) and q["err4"][0, 0, 1] == _hx(fx["err4"])
+    assert q["scales"][0, 0, 1] == fx["scale"] == 0x3C  # +-4 kept: err4 is one rounding step below err6
+    assert q["codes"][0, 0, 8:].tolist() == fx["codes"]
+
+
+def test_summation_order_2d_tile():
+    fx = _order_fixture()["tile_2d"]
+    w = np.zeros((16, 32), np.float32)
+    w[0, 0] = 1800.0
+    for r, c, v in fx["elements"]:
+        w[r, 16 + c] = v
+    wb = _bits(w)
+    assert np.array_equal(O.bf16_to_float(wb), w)  # every value is a bf16 value
+    q = O.quantize_2d(wb, O.MODE_4OVER6, want_errors=True)
+    assert q["tensor_scale"][0] == np.float32(1800.0) / np.float32(1792.0)
+    assert q["err6"][0, 1] == _hx(fx["err6"]) and q["err4"][0, 1] == _hx(fx["err4"])
+    assert q["scales"][0, 1] == fx["scale"] == 0x38  # +-6 kept
+    for r, codes in fx["codes_rows_0_2_8_12"].items():
+        assert q["codes"][int(r), 8:].tolist() == codes, r
+
+
+def test_summation_order_fixture_is_consistent():
+    """The fixtures' numbers re-derived in exact rational arithmetic, every
+    fp32 step rounded to nearest even: the convention's order gives the
+    stored errors, the other order gives the other choice."""
+    from fractions import Fraction as F
+
+    def f32(x):
+        x = F(x)
+        if x == 0:
+            return F(0)
+        a = abs(x)
+        e = a.numerator.bit_length() - a.denominator.bit_length()
+        while F(2) ** e > a:
+            e -= 1
+        while F(2) ** (e + 1) <= a:
+            e += 1
+        ulp = F(2) ** (e - 23)
+        q, r = divmod(a / ulp, 1)
+        q = int(q) + (1 if r > F(1, 2) or (r == F(1, 2) and int(q) % 2 == 1) else 0)
+        return (q * ulp) if x > 0 else -(q * ulp)
+
+    grid = [F(0), F(1, 2), F(1), F(3, 2), F(2), F(3), F(4), F(6)]
+
+    def nearest(y):
+        a, best = abs(y), 0
+        for k in range(1, 8):
+            if abs(a - grid[k]) < abs(a - grid[best]) or (abs(a - grid[k]) == abs(a - grid[best]) and k % 2 == 0):
+                best = k
+        return (-1 if y < 0 else 1) * (grid[7] if a >= 6 else grid[best])
+
+    def errors(z, S):
+        R = f32(1 / S)
+        return [f32(zi - nearest(f32(zi * R)) * S) for zi in z]
+
+    def chain(es):
+        acc = F(0)
+        for e in es:
+            acc = f32(e * e + acc)
+        return acc
+
+    fx = _order_fixture()
+    z = [F(float.fromhex(h)) for h in fx["block_1d"]["z"]]
+    halves = {S: f32(chain(errors(z, S)[:8]) + chain(errors(z, S)[8:])) for S in (F(1), F(3, 2))}
+    one = {S: chain(errors(z, S)) for S in (F(1), F(3, 2))}
+    assert halves[F(1)] == F(float.fromhex(fx["block_1d"]["err6"]))
+    assert halves[F(3, 2)] == F(float.fromhex(fx["block_1d"]["err4"]))
+    assert halves[F(3, 2)] < halves[F(1)] and not one[F(3, 2)] < one[F(1)]
+
+    t2 = fx["tile_2d"]
+    g = F(float.fromhex(t2["g_enc"]))
+    assert g == f32(F(1792) / 1800)
+    Z = [[F(0)] * 16 for _ in range(16)]
+    for r, c, v in t2["elements"]:
+        Z[r][c] = f32(F(v) * g)
+    tot = {}
+    for S in (F(1), F(3, 2)):
+        rows = [f32(chain(errors(Z[r], S)[:8]) + chain(errors(Z[r], S)[8:])) for r in range(16)]
+        w = rows
+        while len(w) > 1:
+            w = [f32(w[2 * i] + w[2 * i + 1]) for i in range(len(w) // 2)]
+        seq = rows[0]
+        for r in range(1, 16):
+            seq = f32(seq + rows[r])
+        tot[S] = (w[0], seq)
+    assert tot[F(1)][0] == F(float.fromhex(t2["err6"])) and tot[F(3, 2)][0] == F(float.fromhex(t2["err4"]))
+    assert not tot[F(3, 2)][0] < tot[F(1)][0]  # tree: +-6
+    assert tot[F(3, 2)][1] < tot[F(1)][1]      # sequential rows: +-4
+
+
 # ------------------------------------------------------- worked examples ----
 
 def test_worked_examples_from_the_75_percent_claim():
