@@ -153,6 +153,40 @@ NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, i
                                          float* k_mean, unsigned long long* choice_counts, void* workspace,
                                          size_t workspace_bytes, void* stream) NVFP4KV_NOEXCEPT;
 
+/* Bytes of the device array nvfp4_kv_smooth_quantize_noalloc uses instead of
+ * a workspace (one per GPU): enough for one layer of 24 heads x 56320 tokens
+ * x 128 channels in chunks of 7040 tokens. */
+#define NVFP4_KV_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * nvfp4_kv_smooth_quantize without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results and kernels as
+ * nvfp4_kv_smooth_quantize, except:
+ *   - no workspace: the kernels use a device array of this library, one per
+ *     GPU, of NVFP4_KV_NOALLOC_SCRATCH_BYTES bytes, held until the process
+ *     ends.  The call allocates and frees nothing.  A shape whose
+ *     nvfp4_kv_workspace_bytes() exceeds that size returns
+ *     NVFP4_ERR_WORKSPACE before any HIP call.
+ *   - every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams, or from several threads) race
+ *     and give invalid results.  Order them on one stream.  The array keeps
+ *     the last call's contents; each call clears the counters it needs.
+ *   - error_word: nullable device pointer to a caller-owned uint32 (4-byte
+ *     aligned, no overlap with the other arguments).  A call whose bounded
+ *     waits timed out ORs 1 into it (the library never clears it), and that
+ *     call's outputs are invalid.
+ *   - the first call on a GPU looks up the array's device address there
+ *     (hipGetSymbolAddress, with that GPU current) and keeps it; a failure
+ *     returns NVFP4_ERR_HIP.  `stream` must belong to the current device.
+ */
+NVFP4KV_API int nvfp4_kv_smooth_quantize_noalloc(const uint16_t* k, const uint16_t* v, int H, int T, int D,
+                                                 int chunk_len, int mode, uint8_t* k_codes, uint8_t* v_codes,
+                                                 uint8_t* k_scales, uint8_t* v_scales, float* k_tensor_scale,
+                                                 float* v_tensor_scale, float* k_mean,
+                                                 unsigned long long* choice_counts, unsigned* error_word,
+                                                 void* stream) NVFP4KV_NOEXCEPT;
+
 /*
  * Dequantize an NVFP4 cache tensor back to bf16 (the consumer side of
  * inference pipeline, step 7).

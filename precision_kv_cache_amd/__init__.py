@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
-    "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "nvfp4_quantize_1d",
+    "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_kv_smooth_quantize_noalloc", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
     "nvfp4_kv_attention_workspace_bytes",
     "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_kv_quantize_v_tblocks", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
@@ -47,6 +47,7 @@ def lib():
             "nvfp4_kv_workspace_bytes": (sz, [i, i, i, i]),
             "nvfp4_kv_error_word_offset": (ll, [i, i, i, i]),
             "nvfp4_kv_smooth_quantize": (i, [P, P, i, i, i, i, i, P, P, P, P, P, P, P, P, P, sz, P]),
+            "nvfp4_kv_smooth_quantize_noalloc": (i, [P, P, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P]),
             "nvfp4_dequantize": (i, [P, P, P, P, i, i, i, i, P, P]),
             "nvfp4_quantize_1d_workspace_bytes": (sz, [i, i]),
             "nvfp4_quantize_2d_workspace_bytes": (sz, [i, i]),
@@ -166,6 +167,27 @@ def nvfp4_kv_smooth_quantize(k, v, chunk_len, mode=MODE_4OVER6, choice_counts=Fa
         _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "nvfp4_kv_smooth_quantize")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # NVFP4_KV_NOALLOC_SCRATCH_BYTES
+
+
+def nvfp4_kv_smooth_quantize_noalloc(k, v, chunk_len, out, mode=MODE_4OVER6, error_word=None, stream=None):
+    """nvfp4_kv_smooth_quantize without a workspace (the library's per-GPU
+    device array instead), for callers that cannot allocate: ``out`` must hold
+    every output tensor (and "choice_counts" if wanted); ``error_word`` is an
+    optional int32 device tensor the call ORs 1 into if a wait timed out.
+    Allocates nothing."""
+    _bf16_dev(k, "k"); _bf16_dev(v, "v")
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [H, T, D]")
+    H, T, D = k.shape
+    rc = lib().nvfp4_kv_smooth_quantize_noalloc(
+        _ptr(k), _ptr(v), H, T, D, chunk_len, mode, _ptr(out["k_codes"]), _ptr(out["v_codes"]),
+        _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
+        _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(error_word), _stream(stream))
+    _check(rc, "nvfp4_kv_smooth_quantize_noalloc")
     return out
 
 

@@ -491,7 +491,7 @@ __global__ void overlap_zero_kernel(unsigned* p, int n) {
 }
 
 int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_bytes, unsigned long long* choice,
-                       hipStream_t s) {
+                       unsigned* err_word, hipStream_t s) {
   if (p.H <= 0 || p.nc <= 0 || p.L <= 0) return 1;
   p.nst = (p.L + kOvStatsRows - 1) / kOvStatsRows;
   p.nqt = (p.L + kOvQuantRows - 1) / kOvQuantRows;
@@ -513,7 +513,7 @@ int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_byt
   p.cnt_head = cnt;
   p.cnt_unit = cnt + (size_t)U * p.H;
   p.err = p.cnt_unit + U;
-  p.err_sticky = reinterpret_cast<unsigned*>(ws);
+  p.err_sticky = err_word;
   p.choice = choice != nullptr;
   p.depth = kOvDepth;
   p.spin_limit = kOvSpinLimit;

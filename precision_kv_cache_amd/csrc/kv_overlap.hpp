@@ -30,7 +30,8 @@ struct OverlapParams {
   unsigned* cnt_head;        // [U][H] finished statistics tiles of a head
   unsigned* cnt_unit;        // [U] finished heads of a unit
   unsigned* err;             // [1] set when a wait of this call timed out (cleared per call)
-  unsigned* err_sticky;      // [1] the workspace's first word: also set then, never cleared here
+  unsigned* err_sticky;      // [1] set then too, never cleared here (the workspace's first word, or the
+                             // caller's word for the call that has no workspace)
   uint32_t* tally;           // [U * nq][4] per-quantize-tile 4/6 choice counts (when choice)
   int choice;
   int H, T, L, nc, nst, nqt, depth;
@@ -50,7 +51,9 @@ constexpr size_t kKvWorkspaceHeader = 256;
 // NVFP4_OK after enqueueing (and the choice-count reduction when choice is
 // set), a positive value when this form does not apply to the shape, or
 // NVFP4_ERR_HIP.
+// err_word: where a timed-out wait is recorded besides this call's own word
+// (never cleared here).
 int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_bytes, unsigned long long* choice,
-                       hipStream_t s);
+                       unsigned* err_word, hipStream_t s);
 
 }  // namespace nvfp4

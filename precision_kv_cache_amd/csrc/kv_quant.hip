@@ -509,14 +509,16 @@ extern "C" NVFP4KV_API long long nvfp4_kv_error_word_offset(int H, int T, int D,
   return 0;  // the first word of the header block, in both kernel forms' layouts
 }
 
-extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
-                                                    int chunk_len, int mode, uint8_t* k_codes, uint8_t* v_codes,
-                                                    uint8_t* k_scales, uint8_t* v_scales, float* k_tensor_scale,
-                                                    float* v_tensor_scale, float* k_mean,
-                                                    unsigned long long* choice_counts, void* workspace,
-                                                    size_t workspace_bytes, void* stream) noexcept {
+namespace nvfp4 {
+
+// Argument checks of nvfp4_kv_smooth_quantize that do not involve the
+// workspace (no HIP call): NVFP4_OK, or the status to return.
+int kv_quantize_check(const uint16_t* k, const uint16_t* v, int H, int T, int D, int chunk_len, int mode,
+                      const uint8_t* k_codes, const uint8_t* v_codes, const uint8_t* k_scales,
+                      const uint8_t* v_scales, const float* k_tensor_scale, const float* v_tensor_scale,
+                      const float* k_mean, const unsigned long long* choice_counts, const void* workspace,
+                      size_t ws_range) {
   if (!kv_shape_ok(H, T, D, chunk_len)) return NVFP4_ERR_SHAPE;
-  const bool two_pass = (mode & NVFP4_KV_TWO_PASS) != 0;
   mode &= ~NVFP4_KV_TWO_PASS;
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
@@ -525,20 +527,30 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_codes, 8) || !aligned(v_codes, 8) || !aligned(k_mean, 16) ||
       !aligned(k_tensor_scale, 4) || !aligned(v_tensor_scale, 4) || !aligned(choice_counts, 8))
     return NVFP4_ERR_ALIGN;
+  const size_t n = (size_t)H * T * D;
+  const int nc = T / chunk_len;
+  const Range in[2] = {range_of(k, n * 2), range_of(v, n * 2)};
+  const Range out[9] = {range_of(k_codes, n / 2), range_of(v_codes, n / 2), range_of(k_scales, n / 16),
+                        range_of(v_scales, n / 16), range_of(k_tensor_scale, (size_t)nc * 4),
+                        range_of(v_tensor_scale, (size_t)nc * 4), range_of(k_mean, (size_t)nc * H * D * 4),
+                        range_of(choice_counts, 32), range_of(workspace, ws_range)};
+  if (any_alias(in, 2, out, 9)) return NVFP4_ERR_ALIAS;
+  return NVFP4_OK;
+}
+
+// The kernels of nvfp4_kv_smooth_quantize on a checked call, with the
+// workspace given (at least nvfp4_kv_workspace_bytes, 256-byte aligned);
+// err_word: where a timed-out wait is also recorded (the workspace's first
+// word for the ordinary entry point).
+int kv_quantize_launch(const uint16_t* k, const uint16_t* v, int H, int T, int D, int chunk_len, int mode,
+                       uint8_t* k_codes, uint8_t* v_codes, uint8_t* k_scales, uint8_t* v_scales,
+                       float* k_tensor_scale, float* v_tensor_scale, float* k_mean,
+                       unsigned long long* choice_counts, void* workspace, size_t workspace_bytes,
+                       unsigned* err_word, hipStream_t s) {
+  const bool two_pass = (mode & NVFP4_KV_TWO_PASS) != 0;
+  mode &= ~NVFP4_KV_TWO_PASS;
   const KVGeom g = kv_geom(H, T, D, chunk_len);
   const KVWorkspace wl = kv_workspace_layout(g);
-  const size_t ws_need = nvfp4_kv_workspace_bytes(H, T, D, chunk_len);
-  if (!workspace || workspace_bytes < ws_need) return NVFP4_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
-  const size_t n = (size_t)H * T * D;
-  const Range in[2] = {range_of(k, n * 2), range_of(v, n * 2)};
-  const Range out[10] = {range_of(k_codes, n / 2), range_of(v_codes, n / 2), range_of(k_scales, n / 16),
-                         range_of(v_scales, n / 16), range_of(k_tensor_scale, (size_t)g.nc * 4),
-                         range_of(v_tensor_scale, (size_t)g.nc * 4), range_of(k_mean, (size_t)g.nc * H * D * 4),
-                         range_of(choice_counts, 32), range_of(workspace, ws_need), Range{0, 0}};
-  if (any_alias(in, 2, out, 9)) return NVFP4_ERR_ALIAS;
-
-  hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();  // start from a clean error state
   if (!two_pass && D == 128) {
@@ -549,7 +561,7 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
     q.tscale[0] = k_tensor_scale; q.tscale[1] = v_tensor_scale;
     q.kmean = k_mean;
     q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
-    const int rc = overlap_try_launch(q, mode, workspace, workspace_bytes, choice_counts, s);
+    const int rc = overlap_try_launch(q, mode, workspace, workspace_bytes, choice_counts, err_word, s);
     if (rc <= 0) return rc;  // enqueued, or a launch error
   }
   KVParams p;
@@ -599,6 +611,30 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uin
   }
   if (choice_counts) launch_choice_reduce(p.tally, wl.n_tally, choice_counts, s);
   return launch_status();
+}
+
+}  // namespace nvfp4
+
+
+extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize(const uint16_t* k, const uint16_t* v, int H, int T, int D,
+                                                    int chunk_len, int mode, uint8_t* k_codes, uint8_t* v_codes,
+                                                    uint8_t* k_scales, uint8_t* v_scales, float* k_tensor_scale,
+                                                    float* v_tensor_scale, float* k_mean,
+                                                    unsigned long long* choice_counts, void* workspace,
+                                                    size_t workspace_bytes, void* stream) noexcept {
+  const size_t ws_need = nvfp4_kv_workspace_bytes(H, T, D, chunk_len);
+  int rc = kv_quantize_check(k, v, H, T, D, chunk_len, mode, k_codes, v_codes, k_scales, v_scales, k_tensor_scale,
+                             v_tensor_scale, k_mean, choice_counts, nullptr, 0);
+  if (rc != NVFP4_OK || H == 0 || T == 0) return rc;
+  if (!workspace || workspace_bytes < ws_need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  // the kernels may use every byte nvfp4_kv_workspace_bytes covers
+  rc = kv_quantize_check(k, v, H, T, D, chunk_len, mode, k_codes, v_codes, k_scales, v_scales, k_tensor_scale,
+                         v_tensor_scale, k_mean, choice_counts, workspace, ws_need);
+  if (rc != NVFP4_OK) return rc;
+  return kv_quantize_launch(k, v, H, T, D, chunk_len, mode, k_codes, v_codes, k_scales, v_scales, k_tensor_scale,
+                            v_tensor_scale, k_mean, choice_counts, workspace, workspace_bytes,
+                            static_cast<unsigned*>(workspace), as_stream(stream));
 }
 
 extern "C" NVFP4KV_API int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,

@@ -106,6 +106,32 @@ def test_kv_quantize_output_in_workspace_tail_is_an_alias():
         assert _kvq(H=H, T=T, D=D, L=L, km=ws + off, ws=ws, wsb=need) == ALIAS, off
 
 
+def test_noalloc_argument_errors_before_any_hip_call():
+    V = ctypes.c_void_p
+    L = P.lib()
+
+    def call(H=2, T=64, D=32, Lc=32, mode=0, ew=None, **kw):
+        a = dict(k=FAKE, v=FAKE + (1 << 30), kc=FAKE + (2 << 30), vc=FAKE + (3 << 30), ks=FAKE + (4 << 30),
+                 vs=FAKE + (5 << 30), kt=FAKE + (6 << 30), vt=FAKE + (7 << 30), km=FAKE + (8 << 30), cc=None)
+        a.update(kw)
+        return L.nvfp4_kv_smooth_quantize_noalloc(V(a["k"]), V(a["v"]), H, T, D, Lc, mode, V(a["kc"]), V(a["vc"]),
+                                                  V(a["ks"]), V(a["vs"]), V(a["kt"]), V(a["vt"]), V(a["km"]),
+                                                  V(a["cc"]), V(ew), None)
+    # the scratch holds one full-cache layer's workspace, not two layers' worth
+    assert P.nvfp4_kv_workspace_bytes(24, 56320, 128, 7040) <= P.NOALLOC_SCRATCH_BYTES
+    assert P.nvfp4_kv_workspace_bytes(48, 56320, 128, 7040) > P.NOALLOC_SCRATCH_BYTES
+    assert call(H=48, T=56320, D=128, Lc=7040) == WORKSPACE
+    assert call(k=None) == NULL
+    assert call(D=40) == SHAPE
+    assert call(mode=3) == MODE
+    assert call(kc=FAKE + 4) == ALIGN
+    assert call(ew=FAKE + (9 << 30) + 2) == ALIGN
+    assert call(ew=FAKE + 8) == ALIAS             # error word inside K
+    assert call(ew=FAKE + (2 << 30) + 8) == ALIAS  # error word inside k_codes
+    assert call(vc=FAKE + 64) == ALIAS
+    assert call(H=0, k=None, v=None) == OK
+
+
 def test_empty_calls_are_no_ops():
     assert _kvq(H=0, k=None, v=None) == OK
     assert _kvq(T=0, k=None) == OK
