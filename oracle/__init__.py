@@ -47,6 +47,11 @@ def lib():
             "ora_e2m1_decode_array": (None, [P, l, P, i]),
             "ora_e4m3_decode_array": (None, [P, l, P, i]),
             "ora_candidate_codes": (None, [P, l, f, P]),
+            "ora_lowbit_encode": (ctypes.c_uint8, [i, f]),
+            "ora_lowbit_decode": (f, [i, ctypes.c_uint8]),
+            "ora_lowbit_encode_array": (None, [i, P, l, P, i]),
+            "ora_quantize_chunks_lowbit": (i, [P, i, i, i, i, i, i, P, P, P, P, P, P, P, i]),
+            "ora_dequantize_lowbit": (i, [P, P, P, P, i, i, i, i, i, P, i]),
             "ora_gemm_w4a4": (i, [P, P, P, i, i, P, P, P, i, i, P, i]),
             "ora_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_double, P, l, P, P,
                                      i]),
@@ -203,6 +208,73 @@ def dequantize(codes, scales, tensor_scale, mean, chunk_len, nthreads=0):
     out = np.empty((H, T, D), np.uint16)
     _check(lib().ora_dequantize(_ptr(codes), _ptr(scales), _ptr(ts), _ptr(m), H, T, D, chunk_len, _ptr(out),
                                 _nt(nthreads)), "dequantize")
+    return out
+
+
+# ---- 3-bit and 2-bit KV --------------------------------------------------
+
+def lowbit_encode(bits, y, nthreads=0):
+    """Element codes of the 3-bit (E1M1) or 2-bit (E1M0) grid for fp32 y."""
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().ora_lowbit_encode_array(int(bits), _ptr(y), y.size, _ptr(out), _nt(nthreads))
+    return out
+
+
+def lowbit_decode(bits, q):
+    return np.array([lib().ora_lowbit_decode(int(bits), int(c)) for c in np.asarray(q).ravel()],
+                    np.float32).reshape(np.shape(q))
+
+
+def quantize_chunks_lowbit(x, chunk_len, bits, mode=MODE_4OVER6, mean=None, want_errors=False, nthreads=0):
+    """3-bit / 2-bit quantization of x [H, T, D] (bf16 bits) chunk by chunk;
+    see ora_quantize_chunks_lowbit.  codes [H, T, D * bits / 8]."""
+    x = _c(x, np.uint16)
+    H, T, D = x.shape
+    nc = T // chunk_len
+    codes = np.empty((H, T, D * bits // 8), np.uint8)
+    scales = np.empty((H, T, D // 16), np.uint8)
+    ts = np.empty((nc,), np.float32)
+    ea = np.empty((H, T, D // 16), np.float32) if want_errors else None
+    eb = np.empty((H, T, D // 16), np.float32) if want_errors else None
+    nb = ctypes.c_longlong(0)
+    m = None if mean is None else _c(mean, np.float32)
+    rc = lib().ora_quantize_chunks_lowbit(_ptr(x), H, T, D, chunk_len, int(bits), mode, _ptr(m), _ptr(codes),
+                                          _ptr(scales), _ptr(ts), _ptr(ea), _ptr(eb), ctypes.byref(nb),
+                                          _nt(nthreads))
+    _check(rc, "quantize_chunks_lowbit")
+    out = {"codes": codes, "scales": scales, "tensor_scale": ts, "useb": int(nb.value)}
+    if want_errors:
+        out["erra"], out["errb"] = ea, eb
+    return out
+
+
+def smooth_quantize_lowbit(k, v, chunk_len, bits, mode=MODE_4OVER6, k_mean=None, want_errors=False, nthreads=0):
+    """The KV step at 3 or 2 bits: per-chunk K mean (or the given one),
+    smoothed K and raw V quantized per chunk."""
+    if k_mean is None:
+        k_mean = kv_mean(k, chunk_len, nthreads)
+    qk = quantize_chunks_lowbit(k, chunk_len, bits, mode, mean=k_mean, want_errors=want_errors, nthreads=nthreads)
+    qv = quantize_chunks_lowbit(v, chunk_len, bits, mode, mean=None, want_errors=want_errors, nthreads=nthreads)
+    out = {"k_codes": qk["codes"], "v_codes": qv["codes"], "k_scales": qk["scales"], "v_scales": qv["scales"],
+           "k_tensor_scale": qk["tensor_scale"], "v_tensor_scale": qv["tensor_scale"],
+           "k_mean": np.asarray(k_mean, np.float32), "k_useb": qk["useb"], "v_useb": qv["useb"]}
+    if want_errors:
+        out.update(k_erra=qk["erra"], k_errb=qk["errb"], v_erra=qv["erra"], v_errb=qv["errb"])
+    return out
+
+
+def dequantize_lowbit(codes, scales, tensor_scale, mean, chunk_len, bits, nthreads=0):
+    """codes [H, T, D * bits / 8], scales [H, T, D/16] -> bf16 bits [H, T, D]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    ts = _c(tensor_scale, np.float32)
+    m = None if mean is None else _c(mean, np.float32)
+    H, T, _ = codes.shape
+    D = scales.shape[2] * 16
+    out = np.empty((H, T, D), np.uint16)
+    _check(lib().ora_dequantize_lowbit(_ptr(codes), _ptr(scales), _ptr(ts), _ptr(m), H, T, D, chunk_len, int(bits),
+                                       _ptr(out), _nt(nthreads)), "dequantize_lowbit")
     return out
 
 

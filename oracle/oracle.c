@@ -646,6 +646,261 @@ ORA_API int ora_dequantize_2d(const uint8_t* codes, const uint8_t* scales, const
 }
 
 /* ------------------------------------------------------------------------ */
+/* 3-bit and 2-bit KV ([LL2] directions to extend, item 6: a 3-bit / 2-bit  */
+/* KV cache)                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* The page names a 3-bit / 2-bit KV cache as a direction without defining a
+ * format.  Reading (convention): the NVFP4 layout with fewer element bits.
+ *   element: sign bit + (bits - 1) magnitude bits, a minifloat grid:
+ *            3 bits: E1M1 (bias 1, with subnormal), magnitudes {0, .5, 1, 1.5};
+ *            2 bits: E1M0, magnitudes {0, 1};
+ *            nearest magnitude, ties to the even code, saturating at the
+ *            largest, sign bit = y's sign bit (so -0 is possible).
+ *   block  : 16 consecutive channels, one E4M3FN scale, fp32 tensor scale per
+ *            (chunk, tensor), the same smoothing as the 4-bit path.
+ *   choice : two candidate scales t_b / c for divisors c_a (maps the block
+ *            maximum onto the grid's largest magnitude) and c_b = c_a / 1.5
+ *            (3 bits: 1.5 and 1) or c_a * 1.5 (2 bits: 1 and 1.5), the same
+ *            3 : 2 ratio as 6 : 4; the lower fp32 error wins, ties keep c_a;
+ *            mode 1 uses c_a only, mode 2 c_b only.
+ *   C      : 448 * the smallest divisor the mode uses (the largest candidate
+ *            scale stays within E4M3's 448).
+ *   codes  : element i of a block at bits [bits*i, bits*i + bits) of the
+ *            block's little-endian bit field: 6 bytes per block (3 bits), 4
+ *            bytes (2 bits); rows of D / 16 blocks.
+ * The error, its summation order, the encode domain and the dequantize are
+ * those of the 4-bit path. */
+
+static const double FP3_MAG[4] = {0.0, 0.5, 1.0, 1.5};
+static const double FP2_MAG[2] = {0.0, 1.0};
+
+static int lowbit_nmag(int bits) { return bits == 3 ? 4 : 2; }
+static const double* lowbit_mag(int bits) { return bits == 3 ? FP3_MAG : FP2_MAG; }
+
+ORA_API float ora_lowbit_decode(int bits, uint8_t code) {
+  int sbit = bits - 1;
+  double m = lowbit_mag(bits)[code & ((1u << sbit) - 1u)];
+  return (float)(((code >> sbit) & 1u) ? -m : m);
+}
+
+ORA_API uint8_t ora_lowbit_encode(int bits, float y) {
+  int sbit = bits - 1, n = lowbit_nmag(bits);
+  const double* mag = lowbit_mag(bits);
+  uint8_t sign = signbit(y) ? (uint8_t)(1u << sbit) : 0u;
+  double a = fabs((double)y);
+  if (a >= mag[n - 1]) return (uint8_t)(sign | (n - 1));
+  int best = 0;
+  double bestd = a;
+  for (int k = 1; k < n; ++k) {
+    double d = fabs(a - mag[k]);
+    if (d < bestd || (d == bestd && (k % 2) == 0)) {
+      best = k;
+      bestd = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+static void lowbit_divisors(int bits, float* ca, float* cb) {
+  *ca = bits == 3 ? 1.5f : 1.0f;
+  *cb = bits == 3 ? 1.0f : 1.5f;
+}
+
+static float lowbit_constant(int bits, int mode) {
+  float ca, cb;
+  lowbit_divisors(bits, &ca, &cb);
+  float c = mode == ORA_MODE_FIXED6 ? ca : (mode == ORA_MODE_FIXED4 ? cb : (ca < cb ? ca : cb));
+  return 448.0f * c;
+}
+
+/* One 16-element block in the encode domain under scale S (reciprocal R):
+ * codes q[16] and the fp32 error, two sequential fused halves added. */
+static float lowbit_encode16(int bits, const float* z, float S, float R, uint8_t* q) {
+  float lo = 0.0f, hi = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    float y = z[i] * R;
+    q[i] = ora_lowbit_encode(bits, y);
+    float v = ora_lowbit_decode(bits, q[i]);
+    float vs = v * S;
+    float e = z[i] - vs;
+    if (i < 8)
+      lo = fmaf(e, e, lo);
+    else
+      hi = fmaf(e, e, hi);
+  }
+  return lo + hi;
+}
+
+static void lowbit_pack(int bits, const uint8_t* q, uint8_t* out) {
+  int nbytes = 2 * bits;
+  for (int j = 0; j < nbytes; ++j) out[j] = 0;
+  for (int i = 0; i < 16; ++i)
+    for (int b = 0; b < bits; ++b)
+      if ((q[i] >> b) & 1u) {
+        int pos = bits * i + b;
+        out[pos / 8] |= (uint8_t)(1u << (pos % 8));
+      }
+}
+
+/* Returns 1 when the c_b candidate was kept. */
+static int lowbit_block16(int bits, const float* x, float g_enc, int mode, uint8_t* code_bytes, uint8_t* scale,
+                          float* erra_out, float* errb_out) {
+  float z[16], t_b = 0.0f, ca, cb;
+  lowbit_divisors(bits, &ca, &cb);
+  for (int i = 0; i < 16; ++i) {
+    z[i] = x[i] * g_enc;
+    float a = fabsf(z[i]);
+    if (a > t_b) t_b = a;
+  }
+  uint8_t sa = 0, sb = 0, qa[16], qb[16];
+  float erra = NAN, errb = NAN;
+  if (mode != ORA_MODE_FIXED4) {
+    float S, R;
+    candidate_scale(t_b, ca, &sa, &S, &R);
+    erra = lowbit_encode16(bits, z, S, R, qa);
+  }
+  if (mode != ORA_MODE_FIXED6) {
+    float S, R;
+    candidate_scale(t_b, cb, &sb, &S, &R);
+    errb = lowbit_encode16(bits, z, S, R, qb);
+  }
+  int useb = (mode == ORA_MODE_FIXED4) || (mode == ORA_MODE_4OVER6 && errb < erra);
+  lowbit_pack(bits, useb ? qb : qa, code_bytes);
+  *scale = useb ? sb : sa;
+  if (erra_out) *erra_out = erra;
+  if (errb_out) *errb_out = errb;
+  return useb;
+}
+
+typedef struct {
+  int bits, mode, D, L, T, H, chunk, items_per_head;
+  const float* xp;  /* prepared (smoothed) fp32 chunk [H, L, D] */
+  float g_enc;
+  uint8_t *codes, *scales;
+  float *erra, *errb;
+  long* item_useb;
+} lowbit_ctx;
+
+static void lowbit_item(void* vctx, long item) {
+  lowbit_ctx* c = (lowbit_ctx*)vctx;
+  int h = (int)(item / c->items_per_head);
+  int r0 = (int)(item % c->items_per_head) * ROWS_PER_ITEM;
+  int r1 = r0 + ROWS_PER_ITEM < c->L ? r0 + ROWS_PER_ITEM : c->L;
+  int nb = c->D / 16, cb = 2 * c->bits;
+  long useb = 0;
+  for (int r = r0; r < r1; ++r) {
+    size_t row = (size_t)h * c->T + (size_t)c->chunk * c->L + r;
+    const float* src = c->xp + ((size_t)h * c->L + r) * c->D;
+    for (int b = 0; b < nb; ++b) {
+      size_t blk = row * nb + b;
+      float ea, eb;
+      useb += lowbit_block16(c->bits, src + 16 * b, c->g_enc, c->mode, c->codes + blk * cb, c->scales + blk, &ea,
+                             &eb);
+      if (c->erra) c->erra[blk] = ea;
+      if (c->errb) c->errb[blk] = eb;
+    }
+  }
+  c->item_useb[item] = useb;
+}
+
+/*
+ * 3-bit / 2-bit quantization of x [H, T, D] (bf16 bits), chunk by chunk,
+ * smoothed by `mean` when given (as ora_quantize_chunks).
+ *   codes [H, T, D * bits / 8], scales [H, T, D / 16], tensor_scale [T / L].
+ *   erra / errb: NULL or per-block errors of the c_a / c_b candidates.
+ */
+ORA_API int ora_quantize_chunks_lowbit(const uint16_t* x, int H, int T, int D, int L, int bits, int mode,
+                                       const float* mean, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                       float* erra, float* errb, long long* useb_count, int nthreads) {
+  if (!x || !codes || !scales || !tensor_scale) return -1;
+  if (H <= 0 || T <= 0 || D <= 0 || L <= 0 || T % L || D % 16) return -2;
+  if (bits != 3 && bits != 2) return -2;
+  if (mode < 0 || mode > 2) return -6;
+  int items_per_head = (L + ROWS_PER_ITEM - 1) / ROWS_PER_ITEM;
+  long nitems = (long)H * items_per_head;
+  float* xp = (float*)malloc(sizeof(float) * (size_t)H * L * D);
+  float* amax = (float*)malloc(sizeof(float) * (size_t)nitems);
+  long* ub = (long*)malloc(sizeof(long) * (size_t)nitems);
+  if (!xp || !amax || !ub) {
+    free(xp);
+    free(amax);
+    free(ub);
+    return -5;
+  }
+  float C = lowbit_constant(bits, mode);
+  long long total = 0;
+  for (int ch = 0; ch < T / L; ++ch) {
+    /* step 1: smoothing and the chunk's largest magnitude, as the 4-bit path */
+    chunk_ctx pc;
+    memset(&pc, 0, sizeof pc);
+    pc.x = x;
+    pc.H = H;
+    pc.T = T;
+    pc.D = D;
+    pc.L = L;
+    pc.chunk = ch;
+    pc.mean = mean ? mean + (size_t)ch * H * D : NULL;
+    pc.xp = xp;
+    pc.item_amax = amax;
+    pc.items_per_head = items_per_head;
+    parallel_items(prepare_item, &pc, nitems, nthreads);
+    float A = 0.0f;
+    for (long i = 0; i < nitems; ++i)
+      if (amax[i] > A) A = amax[i];
+    /* step 2: the blocks */
+    lowbit_ctx c = {bits, mode, D, L, T, H, ch, items_per_head, xp, A > 0.0f ? C / A : 0.0f,
+                    codes, scales, erra, errb, ub};
+    tensor_scale[ch] = A / C;
+    parallel_items(lowbit_item, &c, nitems, nthreads);
+    for (long i = 0; i < nitems; ++i) total += ub[i];
+  }
+  if (useb_count) *useb_count = total;
+  free(xp);
+  free(amax);
+  free(ub);
+  return 0;
+}
+
+/* x_hat = bf16( ((v * S) * g_dec) [+ m] ), as the 4-bit dequantize. */
+typedef struct {
+  const uint8_t *codes, *scales;
+  const float *tensor_scale, *mean;
+  int H, T, D, L, bits;
+  uint16_t* out;
+} deq_lowbit_ctx;
+
+static void deq_lowbit_item(void* vctx, long row) {
+  deq_lowbit_ctx* c = (deq_lowbit_ctx*)vctx;
+  int h = (int)(row / c->T), t = (int)(row % c->T), ch = t / c->L;
+  float g = c->tensor_scale[ch];
+  int rowbytes = c->D * c->bits / 8;
+  for (int d = 0; d < c->D; ++d) {
+    int pos = c->bits * d, q = 0;
+    for (int b = 0; b < c->bits; ++b) {
+      int bit = pos + b;
+      q |= ((c->codes[(size_t)row * rowbytes + bit / 8] >> (bit % 8)) & 1) << b;
+    }
+    float S = ora_e4m3_decode(c->scales[(size_t)row * (c->D / 16) + d / 16]);
+    float v = ora_lowbit_decode(c->bits, (uint8_t)q);
+    float vs = v * S;
+    float xh = vs * g;
+    if (c->mean) xh = xh + c->mean[((size_t)ch * c->H + h) * c->D + d];
+    c->out[(size_t)row * c->D + d] = ora_float_to_bf16(xh);
+  }
+}
+
+ORA_API int ora_dequantize_lowbit(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                  const float* mean, int H, int T, int D, int L, int bits, uint16_t* out,
+                                  int nthreads) {
+  if (!codes || !scales || !tensor_scale || !out) return -1;
+  if (H <= 0 || T <= 0 || D <= 0 || L <= 0 || T % L || D % 16 || (bits != 3 && bits != 2)) return -2;
+  deq_lowbit_ctx c = {codes, scales, tensor_scale, mean, H, T, D, L, bits, out};
+  parallel_items(deq_lowbit_item, &c, (long)H * T, nthreads);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Attention over the NVFP4 cache (consumer of [LL2] inference pipeline,     */
 /* steps 7 and 9)                                                            */
 /* ------------------------------------------------------------------------ */
@@ -857,6 +1112,8 @@ static void arr_item(void* vctx, long item) {
       case 2: ((uint16_t*)c->out)[i] = ora_float_to_bf16(((const float*)c->in)[i]); break;
       case 3: ((float*)c->out)[i] = ora_e2m1_decode(((const uint8_t*)c->in)[i]); break;
       case 4: ((float*)c->out)[i] = ora_e4m3_decode(((const uint8_t*)c->in)[i]); break;
+      case 5: ((uint8_t*)c->out)[i] = ora_lowbit_encode(3, ((const float*)c->in)[i]); break;
+      case 6: ((uint8_t*)c->out)[i] = ora_lowbit_encode(2, ((const float*)c->in)[i]); break;
       default: break;
     }
   }
@@ -872,6 +1129,9 @@ ORA_API void ora_e4m3_encode_array(const float* r, long n, uint8_t* out, int nt)
 ORA_API void ora_float_to_bf16_array(const float* x, long n, uint16_t* out, int nt) { run_array(x, out, n, 2, nt); }
 ORA_API void ora_e2m1_decode_array(const uint8_t* q, long n, float* out, int nt) { run_array(q, out, n, 3, nt); }
 ORA_API void ora_e4m3_decode_array(const uint8_t* s, long n, float* out, int nt) { run_array(s, out, n, 4, nt); }
+ORA_API void ora_lowbit_encode_array(int bits, const float* y, long n, uint8_t* out, int nt) {
+  run_array(y, out, n, bits == 3 ? 5 : 6, nt);
+}
 
 /* E4M3 code of the candidate t / c (c = 6 or 4), as the quantizer forms it. */
 ORA_API void ora_candidate_codes(const float* t, long n, float c, uint8_t* out) {
