@@ -383,6 +383,52 @@ NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H, int T, int
                                             uint8_t* codes, uint8_t* scales, float* tensor_scale, void* workspace,
                                             size_t workspace_bytes, void* stream) NVFP4KV_NOEXCEPT;
 
+/*
+ * 3-bit / 2-bit KV cache (directions to extend, item 6: compress the KV
+ * cache further to 3 or 2 bits; the smoothing and the cache as inference
+ * pipeline, step 7; the two-candidate block scale as full-stack NVFP4).  The
+ * page defines no format; the one here keeps the NVFP4 layout:
+ *   element  sign bit + magnitude: 3 bits {0, 0.5, 1, 1.5} (E1M1), 2 bits
+ *            {0, 1} (E1M0); nearest magnitude, ties to the even code,
+ *            saturating, sign bit = the sign bit of y (so -0 is possible);
+ *   block    16 consecutive channels, one E4M3FN scale; one fp32 g_dec per
+ *            (chunk, tensor); the K mean and smoothing of the 4-bit path;
+ *   choice   (mode NVFP4_MODE_4OVER6) of the candidates t_b / c_a and
+ *            t_b / c_b the one with the lower fp32 error, ties keep c_a:
+ *            3 bits: c_a = 1.5, c_b = 1; 2 bits: c_a = 1, c_b = 1.5 (c_a maps
+ *            the block maximum onto the largest magnitude).
+ *            NVFP4_MODE_FIXED6 keeps c_a only, NVFP4_MODE_FIXED4 c_b only;
+ *   C        the encode scale maps the largest |value| to 448 * the smallest
+ *            divisor the mode uses;
+ *   codes    [H, T, D * bits / 8]: element i of a block at bits
+ *            [bits * i, bits * i + bits) of its 2 * bits bytes, least
+ *            significant bit first; blocks in channel order.
+ *
+ *   k, v, H, T, D, chunk_len, k_mean, tensor scales, scales: as
+ *                 nvfp4_kv_smooth_quantize.
+ *   bits          3 or 2 (else NVFP4_ERR_SHAPE).
+ *   k_codes, v_codes  out, [H, T, D * bits / 8], 2-byte (3 bits) or 4-byte
+ *                 (2 bits) aligned.
+ *   choice_counts out, nullable, uint64 [2][2]: {K, V} x {kept c_a, kept c_b}.
+ *   workspace     >= nvfp4_kv_workspace_bytes(), 256-byte aligned; its
+ *                 contents on entry are ignored (these kernels never wait).
+ */
+NVFP4KV_API int nvfp4_kv_smooth_quantize_lowbit(const uint16_t* k, const uint16_t* v, int H, int T, int D,
+                                                int chunk_len, int bits, int mode, uint8_t* k_codes,
+                                                uint8_t* v_codes, uint8_t* k_scales, uint8_t* v_scales,
+                                                float* k_tensor_scale, float* v_tensor_scale, float* k_mean,
+                                                unsigned long long* choice_counts, void* workspace,
+                                                size_t workspace_bytes, void* stream) NVFP4KV_NOEXCEPT;
+
+/* Dequantize a 3-bit / 2-bit cache tensor: x = bf16( ((v * S) * g_dec)
+ * [+ mean] ), each step one fp32 rounding.  codes [H, T, D * bits / 8]
+ * (aligned as above), scales [H, T, D / 16], tensor_scale [T / chunk_len],
+ * mean nullable [T / chunk_len, H, D] (16-byte aligned), out bf16 [H, T, D]
+ * (16-byte aligned). */
+NVFP4KV_API int nvfp4_dequantize_lowbit(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                        const float* mean, int H, int T, int D, int chunk_len, int bits,
+                                        uint16_t* out, void* stream) NVFP4KV_NOEXCEPT;
+
 /* ---------------------------------------------------------------------------
  * Streaming NVFP4 KV cache (inference pipeline, steps 7 to 9 of the summary
  * page): chunks arrive one at a time and each is quantized (K smoothed, 4/6

@@ -14,7 +14,8 @@ import torch
 
 __all__ = [
     "MODE_4OVER6", "MODE_FIXED6", "MODE_FIXED4", "KV_TWO_PASS", "Nvfp4Error", "lib", "nvfp4_status_string",
-    "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_kv_smooth_quantize_noalloc", "nvfp4_dequantize", "nvfp4_quantize_1d",
+    "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_kv_smooth_quantize_noalloc", "nvfp4_kv_smooth_quantize_lowbit",
+    "nvfp4_dequantize_lowbit", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
     "nvfp4_kv_attention_workspace_bytes",
     "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_kv_quantize_v_tblocks", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
@@ -48,6 +49,8 @@ def lib():
             "nvfp4_kv_error_word_offset": (ll, [i, i, i, i]),
             "nvfp4_kv_smooth_quantize": (i, [P, P, i, i, i, i, i, P, P, P, P, P, P, P, P, P, sz, P]),
             "nvfp4_kv_smooth_quantize_noalloc": (i, [P, P, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P]),
+            "nvfp4_kv_smooth_quantize_lowbit": (i, [P, P, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, sz, P]),
+            "nvfp4_dequantize_lowbit": (i, [P, P, P, P, i, i, i, i, i, P, P]),
             "nvfp4_dequantize": (i, [P, P, P, P, i, i, i, i, P, P]),
             "nvfp4_quantize_1d_workspace_bytes": (sz, [i, i]),
             "nvfp4_quantize_2d_workspace_bytes": (sz, [i, i]),
@@ -188,6 +191,54 @@ def nvfp4_kv_smooth_quantize_noalloc(k, v, chunk_len, out, mode=MODE_4OVER6, err
         _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
         _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(error_word), _stream(stream))
     _check(rc, "nvfp4_kv_smooth_quantize_noalloc")
+    return out
+
+
+def lowbit_outputs(H, T, D, chunk_len, bits, device, choice_counts=False):
+    nc = T // chunk_len
+    out = {"k_codes": torch.empty(H, T, D * bits // 8, dtype=torch.uint8, device=device),
+           "v_codes": torch.empty(H, T, D * bits // 8, dtype=torch.uint8, device=device),
+           "k_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=device),
+           "v_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=device),
+           "k_tensor_scale": torch.empty(nc, dtype=torch.float32, device=device),
+           "v_tensor_scale": torch.empty(nc, dtype=torch.float32, device=device),
+           "k_mean": torch.empty(nc, H, D, dtype=torch.float32, device=device)}
+    if choice_counts:
+        out["choice_counts"] = torch.empty(2, 2, dtype=torch.int64, device=device)
+    return out
+
+
+def nvfp4_kv_smooth_quantize_lowbit(k, v, chunk_len, bits, mode=MODE_4OVER6, choice_counts=False, out=None,
+                                    workspace=None, stream=None):
+    """K smoothing + 3-bit or 2-bit quantization of K, V bf16 [H, T, D]: the
+    outputs of nvfp4_kv_smooth_quantize with codes [H, T, D * bits / 8] and
+    choice_counts {K, V} x {kept c_a, kept c_b}."""
+    _bf16_dev(k, "k"); _bf16_dev(v, "v")
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [H, T, D]")
+    H, T, D = k.shape
+    if out is None:
+        out = lowbit_outputs(H, T, D, chunk_len, bits, k.device, choice_counts)
+    if workspace is None:
+        workspace = torch.empty(max(1, nvfp4_kv_workspace_bytes(H, T, D, chunk_len)), dtype=torch.uint8,
+                                device=k.device)
+    rc = lib().nvfp4_kv_smooth_quantize_lowbit(
+        _ptr(k), _ptr(v), H, T, D, chunk_len, bits, mode, _ptr(out["k_codes"]), _ptr(out["v_codes"]),
+        _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
+        _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "nvfp4_kv_smooth_quantize_lowbit")
+    return out
+
+
+def nvfp4_dequantize_lowbit(codes, scales, tensor_scale, mean, chunk_len, bits, out=None, stream=None):
+    """codes [H, T, D * bits / 8], scales [H, T, D/16] -> bf16 [H, T, D]."""
+    H, T, NB = scales.shape
+    D = NB * 16
+    if out is None:
+        out = torch.empty(H, T, D, dtype=torch.bfloat16, device=codes.device)
+    rc = lib().nvfp4_dequantize_lowbit(_ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(mean), H, T, D, chunk_len,
+                                       bits, _ptr(out), _stream(stream))
+    _check(rc, "nvfp4_dequantize_lowbit")
     return out
 
 

@@ -1,0 +1,368 @@
+// kv_lowbit.hip -- 3-bit and 2-bit KV cache: per-chunk K smoothing and the
+// two-candidate block scale at 3 or 2 bits per element, and the matching
+// dequantize (LongLive-2.0 summary page: directions to extend, item 6, a
+// 3-bit / 2-bit KV cache; inference pipeline, step 7 for the smoothing and
+// the cache; full-stack NVFP4 for the adaptive block scale).
+//
+// The page gives no format.  The one taken (shared with the CPU reference):
+//   element  sign bit + E1M1 magnitude {0, 0.5, 1, 1.5} (3 bits), or sign
+//            bit + E1M0 magnitude {0, 1} (2 bits); nearest magnitude, ties
+//            to the even code, saturating, sign bit = the sign bit of y;
+//   block    16 consecutive channels, one E4M3FN scale; one fp32 tensor
+//            scale per (chunk, tensor), as the 4-bit cache;
+//   choice   candidates t_b / c_a and t_b / c_b: c_a maps the block maximum
+//            onto the largest magnitude, c_b = c_a / 1.5 (3 bits: 1.5, 1)
+//            or c_a * 1.5 (2 bits: 1, 1.5); the lower fp32 error (two
+//            8-element fused halves added) wins, ties keep c_a;
+//   C        448 * the smallest divisor the mode uses;
+//   codes    element i of a block at bits [b*i, b*i + b) of the block's
+//            little-endian bit field: 6 bytes per block at 3 bits, 4 at 2.
+//
+// Kernels: the two-pass statistics kernel of the 4-bit path (its K mean,
+// channel max and min, and V largest magnitude are the same), then a
+// quantize kernel per (chunk, tensor, head, row tile) whose lanes each
+// encode one 16-element block per row: there is no hardware conversion for
+// these grids, so a magnitude is rint(2|y|) capped at 3 (3 bits) or
+// |y| > 0.5 (2 bits), which is exactly round to nearest with ties to the
+// even code.  The dequantize decodes one block per lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "host_common.hpp"
+#include "kv_two_pass.hpp"
+#include "nvfp4_device.hpp"
+#include "nvfp4kv.h"
+
+namespace nvfp4 {
+namespace {
+
+template <int BITS>
+struct LowBit {
+  static constexpr float ca = BITS == 3 ? 1.5f : 1.0f;  // maps the block maximum onto the top magnitude
+  static constexpr float cb = BITS == 3 ? 1.0f : 1.5f;  // the 3 : 2 companion
+  static constexpr int bytes = 2 * BITS;                // code bytes per block
+};
+
+template <int BITS>
+__host__ __device__ constexpr float lowbit_constant(int mode) {
+  return 448.0f * (mode == kModeFixed6 ? LowBit<BITS>::ca
+                                       : mode == kModeFixed4 ? LowBit<BITS>::cb
+                                                             : (LowBit<BITS>::ca < LowBit<BITS>::cb ? LowBit<BITS>::ca
+                                                                                                    : LowBit<BITS>::cb));
+}
+
+// One candidate on a block z (encode domain) with scale S and reciprocal R:
+// the packed codes (lo: bits 0..31, hi: bits 32..47) and the fp32 error.
+template <int BITS>
+__device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S, float R, uint32_t& lo,
+                                                  uint32_t& hi) {
+  float elo = 0.0f, ehi = 0.0f;
+  lo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float y = z[i] * R;
+    const float a = fabsf(y);
+    float k;  // magnitude index, as a float
+    if (BITS == 3)
+      k = fminf(__builtin_rintf(a * 2.0f), 3.0f);  // rint: nearest, ties to even
+    else
+      k = a > 0.5f ? 1.0f : 0.0f;                 // the tie 0.5 goes to the even code 0
+    const float v = BITS == 3 ? k * 0.5f : k;      // magnitude value, exact
+    const uint32_t neg = __float_as_uint(y) >> 31;
+    const float vs = __uint_as_float(__float_as_uint(v) | (neg << 31));  // signed value (-0 kept)
+    const float e = __builtin_fmaf(-vs, S, z[i]);  // v * S is exact: fl(z - v S)
+    if (i < 8)
+      elo = __builtin_fmaf(e, e, elo);
+    else
+      ehi = __builtin_fmaf(e, e, ehi);
+    const uint32_t code = (uint32_t)k | (neg << (BITS - 1));
+    const int pos = BITS * i;
+    if (pos < 32) lo |= code << pos;
+    if (pos + BITS > 32) hi |= code >> (32 - pos > 0 ? 32 - pos : 0) << (pos > 32 ? pos - 32 : 0);
+  }
+  return elo + ehi;
+}
+
+struct LowBitBlock {
+  uint32_t lo, hi, scale, useb;
+};
+
+template <int BITS, int MODE>
+__device__ __forceinline__ LowBitBlock lowbit_block16(const float (&z)[16], const float2* tab) {
+  const float t = block_absmax(z);
+  // both candidate scales in one conversion: byte 0 = E4M3(t / ca), byte 1 = E4M3(t / cb);
+  // the division by 1.5 is the IEEE quotient (correctly rounded division)
+  const float ra = LowBit<BITS>::ca == 1.0f ? t : t / LowBit<BITS>::ca;
+  const float rb = LowBit<BITS>::cb == 1.0f ? t : t / LowBit<BITS>::cb;
+  const uint32_t s = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, __float_as_int(t), false) & 0xffffu;
+  LowBitBlock out;
+  if (MODE == kModeFixed6) {
+    const float2 c = tab[s & 0xffu];
+    (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
+    out.scale = s & 0xffu;
+    out.useb = 0;
+  } else if (MODE == kModeFixed4) {
+    const float2 c = tab[s >> 8];
+    (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
+    out.scale = s >> 8;
+    out.useb = 1;
+  } else {
+    const float2 c0 = tab[s & 0xffu], c1 = tab[s >> 8];
+    uint32_t la, ha, lb, hb;
+    const float ea = lowbit_candidate<BITS>(z, c0.x, c0.y, la, ha);
+    const float eb = lowbit_candidate<BITS>(z, c1.x, c1.y, lb, hb);
+    const bool useb = eb < ea;
+    out.lo = useb ? lb : la;
+    out.hi = useb ? hb : ha;
+    out.scale = useb ? (s >> 8) : (s & 0xffu);
+    out.useb = useb ? 1u : 0u;
+  }
+  return out;
+}
+
+// One (chunk, tensor, head, row tile) of the quantize: lane (roff, col)
+// takes rows r0 + roff, + RP, ... of column block col.
+template <int BITS, int MODE>
+__global__ __launch_bounds__(kMaxThreads) void kv_lowbit_quant_kernel(KVParams p) {
+  __shared__ unsigned sh_tally[4 * (kMaxThreads / 64)];
+  __shared__ float2 sh_tab[128];
+  fill_scale_table(sh_tab);
+  __syncthreads();
+  unsigned idx = blockIdx.x;
+  const int qt = idx % p.nqt;
+  idx /= p.nqt;
+  const int h = idx % p.H;
+  idx /= p.H;
+  const int c = p.q0 + (int)(idx >> 1), tau = (int)(idx & 1);
+  // tensor scale of (tau, chunk) from the heads' maxima
+  float A = 0.0f;
+  const float* ha = p.hamax + ((size_t)tau * p.nc + c) * p.H;
+  for (int i = 0; i < p.H; ++i) A = fmaxf(A, ha[i]);
+  const float C = lowbit_constant<BITS>(MODE);
+  const float g = A > 0.0f ? C / A : 0.0f;
+  if (qt == 0 && h == 0 && threadIdx.x == 0) p.tscale[tau][c] = A / C;
+
+  const int tid = threadIdx.x, col = tid % p.NB, roff = tid / p.NB;
+  const bool active = roff < p.RP;
+  float m[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m[i] = 0.0f;
+  if (tau == 0 && active) {
+    const float4* mp = reinterpret_cast<const float4*>(p.kmean + ((size_t)c * p.H + h) * p.D + (size_t)col * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = mp[j];
+      m[4 * j] = v.x; m[4 * j + 1] = v.y; m[4 * j + 2] = v.z; m[4 * j + 3] = v.w;
+    }
+  }
+  const int r0 = qt * p.rows_q;
+  const int r1 = active ? min(r0 + p.rows_q, p.L) : r0;  // idle lanes take no rows
+  const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
+  unsigned nb = 0, n = 0;
+  for (int r = r0 + roff; r < r1; r += p.RP) {
+    const size_t blk = (row0 + r) * p.NB + col;
+    const uint16_t* px = p.x[tau] + blk * 16;
+    const uint4 a = load_nt(px), b = load_nt(px + 8);
+    float z[16];
+    unpack16(a, b, z);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float xs = tau == 0 ? z[i] - m[i] : z[i];  // k' = fl(K - m)
+      z[i] = xs * g;                                   // z = fl(k' * g_enc)
+    }
+    const LowBitBlock q = lowbit_block16<BITS, MODE>(z, sh_tab);
+    uint8_t* pc = p.codes[tau] + blk * LowBit<BITS>::bytes;
+    if (BITS == 3) {  // 6 bytes, 2-byte aligned
+      uint16_t* pw = reinterpret_cast<uint16_t*>(pc);
+      __builtin_nontemporal_store((uint16_t)(q.lo & 0xffffu), pw);
+      __builtin_nontemporal_store((uint16_t)(q.lo >> 16), pw + 1);
+      __builtin_nontemporal_store((uint16_t)(q.hi & 0xffffu), pw + 2);
+    } else {
+      __builtin_nontemporal_store(q.lo, reinterpret_cast<uint32_t*>(pc));
+    }
+    store_nt(p.scales[tau] + blk, (uint8_t)q.scale);
+    nb += q.useb;
+    n += 1;
+  }
+  if (p.choice) {
+    const unsigned t[4] = {tau == 0 ? nb : 0u, tau == 0 ? n : 0u, tau == 1 ? nb : 0u, tau == 1 ? n : 0u};
+    store_wg_tally(p.tally + ((((size_t)c * 2 + tau) * p.H + h) * p.nqt + qt) * 4, t, sh_tally);
+  }
+}
+
+struct LowBitDeq {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tscale;
+  const float* mean;
+  uint16_t* out;
+  int H, T, D, L, NB;
+  long long nblocks;
+};
+
+// One 16-element block per lane: x = bf16((v * S) * g_dec [+ m]).
+template <int BITS, bool MEAN>
+__global__ __launch_bounds__(256) void kv_lowbit_dequant_kernel(LowBitDeq p) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long b = blockIdx.x * (long long)blockDim.x + threadIdx.x; b < p.nblocks; b += stride) {
+    const long long row = b / p.NB;
+    const int col = (int)(b % p.NB);
+    const int t = (int)(row % p.T), h = (int)(row / p.T), c = t / p.L;
+    const uint8_t* pc = p.codes + b * LowBit<BITS>::bytes;
+    uint32_t lo, hi = 0u;
+    if (BITS == 3) {
+      const uint16_t* pw = reinterpret_cast<const uint16_t*>(pc);
+      lo = (uint32_t)pw[0] | ((uint32_t)pw[1] << 16);
+      hi = pw[2];
+    } else {
+      lo = *reinterpret_cast<const uint32_t*>(pc);
+    }
+    const float S = __builtin_amdgcn_cvt_f32_fp8((int)p.scales[b], 0);
+    const float g = p.tscale[c];
+    float m[16];
+    if (MEAN) {
+      const float4* mp = reinterpret_cast<const float4*>(p.mean + ((size_t)c * p.H + h) * p.D + (size_t)col * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = mp[j];
+        m[4 * j] = v.x; m[4 * j + 1] = v.y; m[4 * j + 2] = v.z; m[4 * j + 3] = v.w;
+      }
+    }
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      float x2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pos = BITS * (i + u);
+        uint32_t code;
+        if (pos + BITS <= 32) code = (lo >> pos) & ((1u << BITS) - 1u);
+        else if (pos >= 32) code = (hi >> (pos - 32)) & ((1u << BITS) - 1u);
+        else code = ((lo >> pos) | (hi << (32 - pos))) & ((1u << BITS) - 1u);
+        const uint32_t k = code & ((1u << (BITS - 1)) - 1u);
+        const float v = BITS == 3 ? (float)k * 0.5f : (float)k;
+        const float vs = __uint_as_float(__float_as_uint(v) | ((code >> (BITS - 1)) << 31));
+        float xh = (vs * S) * g;  // two fp32 roundings (v * S is exact)
+        if (MEAN) xh = xh + m[i + u];
+        x2[u] = xh;
+      }
+      o[i / 2] = pack_bf16x2(x2[0], x2[1]);
+    }
+    uint4* po = reinterpret_cast<uint4*>(p.out + b * 16);
+    po[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+template <int BITS>
+void launch_lowbit_quant(const KVParams& p, int mode, unsigned nq, int threads, hipStream_t s) {
+  switch (mode) {
+    case kModeFixed6: kv_lowbit_quant_kernel<BITS, kModeFixed6><<<nq, threads, 0, s>>>(p); break;
+    case kModeFixed4: kv_lowbit_quant_kernel<BITS, kModeFixed4><<<nq, threads, 0, s>>>(p); break;
+    default: kv_lowbit_quant_kernel<BITS, kMode4over6><<<nq, threads, 0, s>>>(p); break;
+  }
+}
+
+}  // namespace
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize_lowbit(const uint16_t* k, const uint16_t* v, int H, int T, int D,
+                                                           int chunk_len, int bits, int mode, uint8_t* k_codes,
+                                                           uint8_t* v_codes, uint8_t* k_scales, uint8_t* v_scales,
+                                                           float* k_tensor_scale, float* v_tensor_scale,
+                                                           float* k_mean, unsigned long long* choice_counts,
+                                                           void* workspace, size_t workspace_bytes,
+                                                           void* stream) noexcept {
+  if (!kv_shape_ok(H, T, D, chunk_len) || (bits != 3 && bits != 2)) return NVFP4_ERR_SHAPE;
+  if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
+  if (H == 0 || T == 0) return NVFP4_OK;
+  if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
+    return NVFP4_ERR_NULL;
+  const size_t calign = bits == 3 ? 2 : 4;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_codes, calign) || !aligned(v_codes, calign) ||
+      !aligned(k_mean, 16) || !aligned(k_tensor_scale, 4) || !aligned(v_tensor_scale, 4) ||
+      !aligned(choice_counts, 8))
+    return NVFP4_ERR_ALIGN;
+  const KVGeom g = kv_geom(H, T, D, chunk_len);
+  const KVWorkspace wl = kv_workspace_layout(g);
+  if (!workspace || workspace_bytes < wl.total) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  const size_t n = (size_t)H * T * D;
+  const Range in[2] = {range_of(k, n * 2), range_of(v, n * 2)};
+  const Range out[9] = {range_of(k_codes, n * bits / 8), range_of(v_codes, n * bits / 8),
+                        range_of(k_scales, n / 16), range_of(v_scales, n / 16),
+                        range_of(k_tensor_scale, (size_t)g.nc * 4), range_of(v_tensor_scale, (size_t)g.nc * 4),
+                        range_of(k_mean, (size_t)g.nc * H * D * 4), range_of(choice_counts, 32),
+                        range_of(workspace, wl.total)};
+  if (any_alias(in, 2, out, 9)) return NVFP4_ERR_ALIAS;
+
+  hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  (void)hipGetLastError();
+  KVParams p;
+  p.x[0] = k; p.x[1] = v;
+  p.codes[0] = k_codes; p.codes[1] = v_codes;
+  p.scales[0] = k_scales; p.scales[1] = v_scales;
+  p.tscale[0] = k_tensor_scale; p.tscale[1] = v_tensor_scale;
+  p.kmean = k_mean;
+  p.psum = reinterpret_cast<double*>(ws + wl.psum);
+  p.pmax = reinterpret_cast<float*>(ws + wl.pmax);
+  p.pmin = reinterpret_cast<float*>(ws + wl.pmin);
+  p.pvabs = reinterpret_cast<float*>(ws + wl.pvabs);
+  p.hamax = reinterpret_cast<float*>(ws + wl.hamax);
+  p.cnt = reinterpret_cast<unsigned*>(ws + wl.counters);
+  p.tally = reinterpret_cast<uint32_t*>(ws + wl.tally);
+  p.choice = choice_counts;
+  p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.nc = g.nc; p.NB = g.NB; p.RP = g.RP;
+  p.rows_s = g.rows_s; p.rows_q = g.rows_q; p.nst = g.nst; p.nqt = g.nqt;
+  launch_kv_zero_counters(p.cnt, wl.n_counters, s);
+  const long long per_chunk_wgs = 2LL * H * (g.nst > g.nqt ? g.nst : g.nqt);
+  int group = (int)(kMaxLaunchWGs / per_chunk_wgs);
+  group = group < 1 ? 1 : (group > g.nc ? g.nc : group);
+  for (int c0 = 0; c0 < g.nc; c0 += group) {
+    p.s0 = p.q0 = c0;
+    p.s1 = p.q1 = c0 + group < g.nc ? c0 + group : g.nc;
+    const long long ns = (long long)(p.s1 - p.s0) * 2 * H * g.nst;
+    const long long nq = (long long)(p.q1 - p.q0) * 2 * H * g.nqt;
+    launch_kv_stats(p, (unsigned)ns, g.threads, s);
+    if (bits == 3) launch_lowbit_quant<3>(p, mode, (unsigned)nq, g.threads, s);
+    else launch_lowbit_quant<2>(p, mode, (unsigned)nq, g.threads, s);
+  }
+  if (choice_counts) launch_choice_reduce(p.tally, wl.n_tally, choice_counts, s);
+  return launch_status();
+}
+
+extern "C" NVFP4KV_API int nvfp4_dequantize_lowbit(const uint8_t* codes, const uint8_t* scales,
+                                                   const float* tensor_scale, const float* mean, int H, int T, int D,
+                                                   int chunk_len, int bits, uint16_t* out, void* stream) noexcept {
+  if (!kv_shape_ok(H, T, D, chunk_len) || (bits != 3 && bits != 2)) return NVFP4_ERR_SHAPE;
+  if (H == 0 || T == 0) return NVFP4_OK;
+  if (!codes || !scales || !tensor_scale || !out) return NVFP4_ERR_NULL;
+  if (!aligned(codes, bits == 3 ? 2 : 4) || !aligned(out, 16) || !aligned(tensor_scale, 4) || !aligned(mean, 16))
+    return NVFP4_ERR_ALIGN;
+  const size_t n = (size_t)H * T * D;
+  const int nc = T / chunk_len;
+  const Range in[4] = {range_of(codes, n * bits / 8), range_of(scales, n / 16), range_of(tensor_scale, (size_t)nc * 4),
+                       range_of(mean, mean ? (size_t)nc * H * D * 4 : 0)};
+  const Range outr[1] = {range_of(out, n * 2)};
+  if (any_alias(in, 4, outr, 1)) return NVFP4_ERR_ALIAS;
+  LowBitDeq p;
+  p.codes = codes; p.scales = scales; p.tscale = tensor_scale; p.mean = mean; p.out = out;
+  p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.NB = D / 16;
+  p.nblocks = (long long)(n / 16);
+  const long long want = (p.nblocks + 255) / 256;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  if (bits == 3) {
+    if (mean) kv_lowbit_dequant_kernel<3, true><<<grid, 256, 0, s>>>(p);
+    else kv_lowbit_dequant_kernel<3, false><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (mean) kv_lowbit_dequant_kernel<2, true><<<grid, 256, 0, s>>>(p);
+    else kv_lowbit_dequant_kernel<2, false><<<grid, 256, 0, s>>>(p);
+  }
+  return launch_status();
+}

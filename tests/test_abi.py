@@ -132,6 +132,33 @@ def test_noalloc_argument_errors_before_any_hip_call():
     assert call(H=0, k=None, v=None) == OK
 
 
+def test_lowbit_argument_errors():
+    V = ctypes.c_void_p
+    L = P.lib()
+
+    def q(bits=3, H=2, T=64, D=32, Lc=32, mode=0, **kw):
+        a = dict(k=FAKE, v=FAKE + (1 << 30), kc=FAKE + (2 << 30), vc=FAKE + (3 << 30), ks=FAKE + (4 << 30),
+                 vs=FAKE + (5 << 30), kt=FAKE + (6 << 30), vt=FAKE + (7 << 30), km=FAKE + (8 << 30), cc=None,
+                 ws=FAKE + (9 << 30), wsb=1 << 20)
+        a.update(kw)
+        return L.nvfp4_kv_smooth_quantize_lowbit(V(a["k"]), V(a["v"]), H, T, D, Lc, bits, mode, V(a["kc"]),
+                                                 V(a["vc"]), V(a["ks"]), V(a["vs"]), V(a["kt"]), V(a["vt"]),
+                                                 V(a["km"]), V(a["cc"]), V(a["ws"]), a["wsb"], None)
+    assert q(bits=4) == SHAPE and q(bits=1) == SHAPE
+    assert q(D=40) == SHAPE and q(mode=3) == MODE
+    assert q(k=None) == NULL
+    assert q(bits=3, kc=FAKE + (2 << 30) + 1) == ALIGN   # 3-bit codes: 2-byte aligned
+    assert q(bits=2, kc=FAKE + (2 << 30) + 2) == ALIGN   # 2-bit codes: 4-byte aligned
+    assert q(ws=None) == WORKSPACE and q(wsb=64) == WORKSPACE
+    # 3-bit codes of [2, 64, 32] are 1536 bytes: v_codes inside them is an alias
+    assert q(vc=FAKE + (2 << 30) + 1024) == ALIAS
+    assert q(H=0, k=None) == OK
+    d = L.nvfp4_dequantize_lowbit
+    assert d(V(FAKE), V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), None, 1, 32, 32, 32, 5, V(FAKE + (3 << 30)), None) == SHAPE
+    assert d(V(FAKE), V(FAKE + (1 << 30)), V(FAKE + (2 << 30)), None, 1, 32, 32, 32, 3, V(FAKE + 16), None) == ALIAS
+    assert d(None, V(FAKE), V(FAKE), None, 1, 32, 32, 32, 2, V(FAKE + (3 << 30)), None) == NULL
+
+
 def test_empty_calls_are_no_ops():
     assert _kvq(H=0, k=None, v=None) == OK
     assert _kvq(T=0, k=None) == OK
