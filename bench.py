@@ -94,8 +94,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
-    ap.add_argument("--op", choices=("kv", "attention", "stream", "gemm", "vt", "act", "weight"), default="kv",
-                    help="kv: the quantize / dequantize path (default); attention: attention over the NVFP4 cache; "
+    ap.add_argument("--bits", type=int, default=3, choices=(3, 2), help="element bits of --op lowbit")
+    ap.add_argument("--op", choices=("kv", "lowbit", "attention", "stream", "gemm", "vt", "act", "weight"),
+                    default="kv",
+                    help="kv: the quantize / dequantize path (default); lowbit: the same workload with 3-bit or 2-bit "
+                         "elements (--bits); attention: attention over the NVFP4 cache; "
                          "stream: the streaming cache (attention + append per layer); gemm: the W4A4 GEMM; "
                          "vt: V blocked along tokens; act: the activation quantizer (RHT + 1D blocks); "
                          "weight: the weight quantizer (2D tiles)")
@@ -104,12 +107,13 @@ def parse():
     return ap.parse_args()
 
 
-def kv_bytes(H, T, D, L, with_mean):
+def kv_bytes(H, T, D, L, with_mean, bits=4):
     """Algorithmic bytes of one tensor's quantize (or dequantize): bf16 in,
-    codes and scales out (or the reverse), plus tensor scales and means."""
+    codes (bits per element) and scales out (or the reverse), plus tensor
+    scales and means."""
     n = H * T * D
     nc = T // L
-    b = 2 * n + n // 2 + n // 16 + 4 * nc
+    b = 2 * n + n * bits // 8 + n // 16 + 4 * nc
     if with_mean:
         b += 4 * nc * H * D
     return b
@@ -137,7 +141,16 @@ def main():
     if a.op in ("act", "weight"):
         act_weight_bench(a)
         return
+    kv_bench(a, 4 if a.op == "kv" else a.bits)
 
+
+LOWBIT_METRIC = "{bits}-bit KV quantize GB/s (bytes in+out) and % of MI355X HBM peak"
+
+
+def kv_bench(a, bits):
+    """The full-cache workload: every layer smooth-quantized, then the whole
+    cache dequantized; NVFP4 4/6 (bits = 4, the headline) or the 3-bit / 2-bit
+    cache (the same readings with fewer element bits)."""
     import torch
 
     import precision_kv_cache_amd as P
@@ -163,8 +176,8 @@ def main():
     outs, deq = [], []
     for l in range(nlayers):
         outs.append({
-            "k_codes": torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
-            "v_codes": torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
+            "k_codes": torch.empty(H, T, D * bits // 8, dtype=torch.uint8, device=dev),
+            "v_codes": torch.empty(H, T, D * bits // 8, dtype=torch.uint8, device=dev),
             "k_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
             "v_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
             "k_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
@@ -181,8 +194,11 @@ def main():
         o = outs[l]
         if ev is not None:
             ev[0].record(stream)
-        P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream,
-                                   two_pass=a.two_pass)
+        if bits == 4:
+            P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream,
+                                       two_pass=a.two_pass)
+        else:
+            P.nvfp4_kv_smooth_quantize_lowbit(ks[l], vs[l], L, bits, a.mode, out=o, workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -190,10 +206,16 @@ def main():
         o = outs[l]
         if ev is not None:
             ev[0].record(stream)
-        P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, out=deq[l][0],
-                           stream=stream)
-        P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, out=deq[l][1],
-                           stream=stream)
+        if bits == 4:
+            P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, out=deq[l][0],
+                               stream=stream)
+            P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, out=deq[l][1],
+                               stream=stream)
+        else:
+            P.nvfp4_dequantize_lowbit(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, bits,
+                                      out=deq[l][0], stream=stream)
+            P.nvfp4_dequantize_lowbit(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, bits,
+                                      out=deq[l][1], stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -233,7 +255,7 @@ def main():
     q_ms = sum(e0.elapsed_time(e1) for e0, e1 in qev) / nlayers    # one layer's quantize call (K and V)
     d_ms = sum(e0.elapsed_time(e1) for e0, e1 in dev_ev) / nlayers  # one layer's dequantize calls (K and V)
 
-    qbytes_layer = kv_bytes(H, T, D, L, True) + kv_bytes(H, T, D, L, False)
+    qbytes_layer = kv_bytes(H, T, D, L, True, bits) + kv_bytes(H, T, D, L, False, bits)
     dbytes_layer = qbytes_layer
     step_bytes = nlayers * (qbytes_layer + dbytes_layer)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -241,7 +263,10 @@ def main():
     d_gbps = dbytes_layer / (d_ms * 1e-3) / 1e9
 
     # 4/6 choice histogram on one layer (outside the timed region)
-    o = P.nvfp4_kv_smooth_quantize(ks[0], vs[0], L, a.mode, choice_counts=True)
+    if bits == 4:
+        o = P.nvfp4_kv_smooth_quantize(ks[0], vs[0], L, a.mode, choice_counts=True)
+    else:
+        o = P.nvfp4_kv_smooth_quantize_lowbit(ks[0], vs[0], L, bits, a.mode, choice_counts=True)
     torch.cuda.synchronize()
     cc = o["choice_counts"].cpu().tolist()
 
@@ -258,11 +283,18 @@ def main():
     copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    kv_path = "two-pass" if a.two_pass or D != 128 else "overlap"
+    kv_path = "two-pass" if a.two_pass or D != 128 or bits != 4 else "overlap"
     dominant = "quantize" if q_ms >= d_ms else "dequantize"
     ach = q_gbps if dominant == "quantize" else d_gbps
+    if bits == 4:
+        choice = {"K": {"kept6": cc[0][0], "kept4": cc[0][1]}, "V": {"kept6": cc[1][0], "kept4": cc[1][1]}}
+        qname, dname, what = "nvfp4_kv_smooth_quantize", "nvfp4_dequantize", "4/6 smooth-quantize"
+    else:
+        choice = {"K": {"kept_ca": cc[0][0], "kept_cb": cc[0][1]}, "V": {"kept_ca": cc[1][0], "kept_cb": cc[1][1]}}
+        qname, dname = "nvfp4_kv_smooth_quantize_lowbit", "nvfp4_dequantize_lowbit"
+        what = f"{bits}-bit smooth-quantize (two-candidate block scale)"
     result = {
-        "metric": METRIC,
+        "metric": METRIC if bits == 4 else LOWBIT_METRIC.format(bits=bits),
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -276,8 +308,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "full 8-chunk KV cache: 30 layers x K,V bf16 [24 heads, 56320 tokens, 128], "
-                        "chunks of 7040 tokens; 4/6 smooth-quantize every layer, then dequantize the cache",
-            "layers": nlayers, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
+                        f"chunks of 7040 tokens; {what} every layer, then dequantize the cache",
+            "layers": nlayers, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L, "element_bits": bits,
             "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": step_bytes,
             "kv_path": kv_path,
         },
@@ -286,18 +318,16 @@ def main():
         "dequantize_GBps": round(d_gbps, 1),
         "quantize_call_ms": round(q_ms, 4),
         "dequantize_call_ms": round(d_ms, 4),
-        "choice_counts_layer0": {"K": {"kept6": cc[0][0], "kept4": cc[0][1]},
-                                 "V": {"kept6": cc[1][0], "kept4": cc[1][1]}},
+        "choice_counts_layer0": choice,
         "d2d_copy_GBps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "nvfp4_kv_smooth_quantize (one layer, K and V)" if dominant == "quantize"
-            else "nvfp4_dequantize (one layer, K and V)",
+            "kernel": f"{qname} (one layer, K and V)" if dominant == "quantize" else f"{dname} (one layer, K and V)",
             "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(kv_path) if dominant == "quantize" else None,
+            "traffic": measured_traffic(kv_path) if dominant == "quantize" and bits == 4 else None,
             "bytes_per_launch": qbytes_layer,
         },
         "input_generation_s": round(gen_s, 2),
@@ -306,7 +336,7 @@ def main():
     if not a.no_cpu_baseline:
         # the oracle's leg: its rate on the host, and the last timed step's
         # outputs of layer 0 chunk 0 compared with it bit for bit
-        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds, check=(outs[0], deq[0]))
+        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds, check=(outs[0], deq[0]), bits=bits)
         if not result["cpu_baseline"]["parity_check"]["bit_exact"]:
             print("bench.py: the sampled chunk differs from the oracle: " + json.dumps(result["cpu_baseline"]),
                   flush=True)
@@ -314,8 +344,9 @@ def main():
     outs.clear()
     deq.clear()
     torch.cuda.empty_cache()
-    result["act_weight"] = act_weight_timing(P, W, a.mode, stream)
-    result["heavy_tail_report"] = heavy_tail_report(P, W)
+    if bits == 4:
+        result["act_weight"] = act_weight_timing(P, W, a.mode, stream)
+        result["heavy_tail_report"] = heavy_tail_report(P, W)
     print(json.dumps(result), flush=True)
 
 
@@ -997,7 +1028,7 @@ def host_cores():
     return {"host_cores_usable": usable, "host_cores_total": os.cpu_count() or usable}
 
 
-def cpu_baseline(ks, vs, L, mode, target_s, check=None):
+def cpu_baseline(ks, vs, L, mode, target_s, check=None, bits=4):
     """The oracle as it stands, on the host cores: K and V smooth-quantize +
     dequantize of whole chunks, layer 0 chunk 0 onwards, until about
     target_s seconds of work on all oracle threads; then the same chunks again
@@ -1010,7 +1041,18 @@ def cpu_baseline(ks, vs, L, mode, target_s, check=None):
     import workloads as W
 
     H, T, D = ks[0].shape
-    chunk_bytes = 2 * (kv_bytes(H, L, D, L, True) + kv_bytes(H, L, D, L, False))
+    chunk_bytes = 2 * (kv_bytes(H, L, D, L, True, bits) + kv_bytes(H, L, D, L, False, bits))
+
+    def quant(kb, vb, nt, k_mean=None):
+        if bits == 4:
+            return O.smooth_quantize(kb, vb, L, mode, k_mean=k_mean, nthreads=nt)
+        return O.smooth_quantize_lowbit(kb, vb, L, bits, mode, k_mean=k_mean, nthreads=nt)
+
+    def deq(r, t, mean, nt):
+        if bits == 4:
+            return O.dequantize(r[t + "_codes"], r[t + "_scales"], r[t + "_tensor_scale"], mean, L, nthreads=nt)
+        return O.dequantize_lowbit(r[t + "_codes"], r[t + "_scales"], r[t + "_tensor_scale"], mean, L, bits,
+                                   nthreads=nt)
 
     def run(nt, budget_s):
         done, t_total, last = 0, 0.0, (0, 0)
@@ -1019,9 +1061,9 @@ def cpu_baseline(ks, vs, L, mode, target_s, check=None):
                 kb = W.bf16_bits(ks[l][:, c * L:(c + 1) * L])
                 vb = W.bf16_bits(vs[l][:, c * L:(c + 1) * L])
                 t0 = time.perf_counter()
-                r = O.smooth_quantize(kb, vb, L, mode, nthreads=nt)
-                O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], r["k_mean"], L, nthreads=nt)
-                O.dequantize(r["v_codes"], r["v_scales"], r["v_tensor_scale"], None, L, nthreads=nt)
+                r = quant(kb, vb, nt)
+                deq(r, "k", r["k_mean"], nt)
+                deq(r, "v", None, nt)
                 t_total += time.perf_counter() - t0
                 done += 1
                 last = (l, c)
@@ -1048,13 +1090,13 @@ def cpu_baseline(ks, vs, L, mode, target_s, check=None):
         m_ref = x.mean(1)[None]
         tol = 1e-6 * np.maximum(np.abs(m_ref), np.abs(x).mean(1)[None])
         mean_ok = bool((np.abs(gm.astype(np.float64) - m_ref) <= tol).all())
-        r = O.smooth_quantize(kb, vb, L, mode, k_mean=gm, nthreads=nt)
+        r = quant(kb, vb, nt, k_mean=gm)
         same = {key: bool(np.array_equal(o[key][:, rows].cpu().numpy(), r[key]))
                 for key in ("k_codes", "v_codes", "k_scales", "v_scales")}
         for key in ("k_tensor_scale", "v_tensor_scale"):
             same[key] = bool(np.array_equal(o[key][0:1].cpu().numpy().view(np.uint32), r[key].view(np.uint32)))
-        rk = O.dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], gm, L, nthreads=nt)
-        rv = O.dequantize(r["v_codes"], r["v_scales"], r["v_tensor_scale"], None, L, nthreads=nt)
+        rk = deq(r, "k", gm, nt)
+        rv = deq(r, "v", None, nt)
         same["dequant_k"] = bool(np.array_equal(W.bf16_bits(dk[:, rows]), rk))
         same["dequant_v"] = bool(np.array_equal(W.bf16_bits(dv[:, rows]), rv))
         out["parity_check"] = {"sample": "layer 0, chunk 0 of the last timed step", "mean_rule": mean_ok,
