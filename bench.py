@@ -95,7 +95,7 @@ def parse():
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--bits", type=int, default=3, choices=(3, 2), help="element bits of --op lowbit")
-    ap.add_argument("--op", choices=("kv", "lowbit", "attention", "stream", "gemm", "vt", "act", "weight"),
+    ap.add_argument("--op", choices=("kv", "lowbit", "chunk", "attention", "stream", "gemm", "vt", "act", "weight"),
                     default="kv",
                     help="kv: the quantize / dequantize path (default); lowbit: the same workload with 3-bit or 2-bit "
                          "elements (--bits); attention: attention over the NVFP4 cache; "
@@ -140,6 +140,9 @@ def main():
         return
     if a.op in ("act", "weight"):
         act_weight_bench(a)
+        return
+    if a.op == "chunk":
+        chunk_bench(a)
         return
     kv_bench(a, 4 if a.op == "kv" else a.bits)
 
@@ -345,6 +348,7 @@ def kv_bench(a, bits):
     deq.clear()
     torch.cuda.empty_cache()
     if bits == 4:
+        result["one_chunk_configs"] = one_chunk_timing(P, W, a.mode, stream, q_ms)
         result["act_weight"] = act_weight_timing(P, W, a.mode, stream)
         result["heavy_tail_report"] = heavy_tail_report(P, W)
     print(json.dumps(result), flush=True)
@@ -393,6 +397,99 @@ def act_weight_timing(P, W, mode, stream, reps=20):
                      "bytes": nbytes}
     res["shapes"] = {"activation": [rows, cols], "weight": list(w.shape)}
     return res
+
+
+def one_chunk_timing(P, W, mode, stream, layer_q_ms, sets=8, reps=6):
+    """The one-chunk calls, as the streaming cache makes them for every
+    generated chunk: K, V bf16 [24, 7040, 128], one chunk.  Two inputs: the
+    Gaussian chunk and the heavy-tailed chunk (Student-t(3) with per-channel
+    scales).  `sets` copies of inputs and outputs (8 x 86.5 MB of input) are
+    rotated, so no call finds its input in the 256 MB Infinity Cache.  Each
+    call is timed alone, back to back on one stream (launch gaps included),
+    as the average over reps x sets calls; quantize and dequantize apart."""
+    import torch
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    s = W.ONE_CHUNK
+    H, T, D, L = s.H, s.T, s.D, s.chunk_len
+    qbytes = kv_bytes(H, T, D, L, True) + kv_bytes(H, T, D, L, False)
+    ws = torch.zeros(P.nvfp4_kv_workspace_bytes(H, T, D, L), dtype=torch.uint8, device="cuda")
+    res = {"shape": [H, T, D], "chunk_len": L, "buffer_sets": sets, "calls_timed": reps * sets,
+           "bytes_per_call": qbytes}
+    for name, gen, seed in (("one_chunk", W.gaussian_kv, W.SEED_ONE_CHUNK),
+                            ("heavy_tail", W.heavy_tail_kv, W.SEED_HEAVY)):
+        k, v = gen(s, seed, device="cuda")
+        ins = [(k, v)] + [(k.clone(), v.clone()) for _ in range(sets - 1)]
+        outs = [P.nvfp4_kv_smooth_quantize(kk, vv, L, mode) for kk, vv in ins]
+        deq = [(torch.empty_like(k), torch.empty_like(v)) for _ in range(sets)]
+
+        def quant(i):
+            kk, vv = ins[i]
+            P.nvfp4_kv_smooth_quantize(kk, vv, L, mode, out=outs[i], workspace=ws, stream=stream)
+
+        def dequant(i):
+            o = outs[i]
+            P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, out=deq[i][0],
+                               stream=stream)
+            P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, out=deq[i][1],
+                               stream=stream)
+
+        entry = {}
+        for what, fn in (("quantize", quant), ("dequantize", dequant)):
+            for i in range(sets):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = E(), E()
+            e0.record(stream)
+            for _ in range(reps):
+                for i in range(sets):
+                    fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / (reps * sets)
+            gbps = qbytes / (ms * 1e-3) / 1e9
+            entry[what] = {"call_ms": round(ms, 4), "GBps": round(gbps, 1),
+                           "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+        both = entry["quantize"]["call_ms"] + entry["dequantize"]["call_ms"]
+        entry["GBps"] = round(2 * qbytes / (both * 1e-3) / 1e9, 1)
+        entry["pct_of_hbm_peak"] = round(100 * entry["GBps"] / HBM_PEAK_GBPS, 2)
+        # the same chunk's share of the full-layer quantize call (8 chunks per call)
+        entry["quantize_vs_layer_call_per_chunk"] = (
+            round(entry["quantize"]["call_ms"] / (layer_q_ms / 8), 3) if layer_q_ms else None)
+        res[name] = entry
+        del ins, outs, deq
+    err = P.kv_error_word(ws)
+    res["quantize_wait_timeouts"] = err
+    if err:
+        print(f"bench.py: a one-chunk quantize call's bounded wait timed out (error word {err})", flush=True)
+        sys.exit(3)
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunk_bench(a):
+    """The one-chunk configurations alone: the Gaussian chunk and the
+    heavy-tailed chunk, quantize and dequantize calls over rotating buffers."""
+    import torch
+
+    import precision_kv_cache_amd as P
+    import workloads as W
+
+    P.lib()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    r = one_chunk_timing(P, W, a.mode, stream, None, reps=max(1, a.steps))
+    g = r["one_chunk"]
+    result = {
+        "metric": METRIC, "value": g["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(g["quantize"]["call_ms"] + g["dequantize"]["call_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "one chunk: K,V bf16 [24 heads, 7040 tokens, 128], smooth-quantize then dequantize, "
+                               f"{r['buffer_sets']} rotating buffer sets", "mode": ["4over6", "fixed6", "fixed4"][a.mode]},
+        "pct_of_hbm_peak": g["pct_of_hbm_peak"],
+        "one_chunk_configs": r,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def heavy_tail_report(P, W):
