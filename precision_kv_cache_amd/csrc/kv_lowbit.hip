@@ -24,7 +24,8 @@
 // encode one 16-element block per row: there is no hardware conversion for
 // these grids, so a magnitude is rint(2|y|) capped at 3 (3 bits) or
 // |y| > 0.5 (2 bits), which is exactly round to nearest with ties to the
-// even code.  The dequantize decodes one block per lane.
+// even code.  The dequantize decodes half a block per lane, a fixed column
+// of rows, like the 4-bit one.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -160,6 +161,8 @@ __global__ __launch_bounds__(kMaxThreads) void kv_lowbit_quant_kernel(KVParams p
   const int r1 = active ? min(r0 + p.rows_q, p.L) : r0;  // idle lanes take no rows
   const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
   unsigned nb = 0, n = 0;
+  // one row per step: two rows' loads in flight need 110+ VGPRs (4 waves
+  // per SIMD instead of 8) and measured slower
   for (int r = r0 + roff; r < r1; r += p.RP) {
     const size_t blk = (row0 + r) * p.NB + col;
     const uint16_t* px = p.x[tau] + blk * 16;
@@ -197,51 +200,72 @@ struct LowBitDeq {
   const float* tscale;
   const float* mean;
   uint16_t* out;
-  int H, T, D, L, NB;
-  long long nblocks;
+  int H, T, D, L, NB, RP;
 };
 
-// One 16-element block per lane: x = bf16((v * S) * g_dec [+ m]).
+constexpr int kLbDeqRows = 4;  // rows per lane
+
+// One workgroup per (tile of RP * kLbDeqRows rows, head, chunk); lane (roff,
+// hc) decodes half-block hc (8 channels: block hc / 2, half hc % 2) of rows
+// roff, roff + RP, ... (RP = 256 / (2 NB) rows per pass).  So its chunk's
+// means are loaded once, and each wave-wide store writes one contiguous run
+// of whole rows, 16 bytes per lane.  The two lanes of a block both load its
+// code bytes and scale.  Workgroups of max(2 NB, 256) lanes (rounded up to
+// whole waves): a row of up to 512 halves (D <= 4096) is one pass.
 template <int BITS, bool MEAN>
-__global__ __launch_bounds__(256) void kv_lowbit_dequant_kernel(LowBitDeq p) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long b = blockIdx.x * (long long)blockDim.x + threadIdx.x; b < p.nblocks; b += stride) {
-    const long long row = b / p.NB;
-    const int col = (int)(b % p.NB);
-    const int t = (int)(row % p.T), h = (int)(row / p.T), c = t / p.L;
-    const uint8_t* pc = p.codes + b * LowBit<BITS>::bytes;
-    uint32_t lo, hi = 0u;
-    if (BITS == 3) {
-      const uint16_t* pw = reinterpret_cast<const uint16_t*>(pc);
-      lo = (uint32_t)pw[0] | ((uint32_t)pw[1] << 16);
-      hi = pw[2];
-    } else {
-      lo = *reinterpret_cast<const uint32_t*>(pc);
-    }
-    const float S = __builtin_amdgcn_cvt_f32_fp8((int)p.scales[b], 0);
-    const float g = p.tscale[c];
-    float m[16];
-    if (MEAN) {
-      const float4* mp = reinterpret_cast<const float4*>(p.mean + ((size_t)c * p.H + h) * p.D + (size_t)col * 16);
+__global__ __launch_bounds__(512) void kv_lowbit_dequant_kernel(LowBitDeq p) {
+  const int HB = 2 * p.NB;
+  const int tid = threadIdx.x, hc = tid % HB, roff = tid / HB;
+  if (roff >= p.RP) return;
+  const int h = blockIdx.y, c = blockIdx.z, half = hc & 1;
+  const float g = p.tscale[c];
+  float m[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 v = mp[j];
-        m[4 * j] = v.x; m[4 * j + 1] = v.y; m[4 * j + 2] = v.z; m[4 * j + 3] = v.w;
+  for (int i = 0; i < 8; ++i) m[i] = 0.0f;
+  if (MEAN) {
+    const float4* mp = reinterpret_cast<const float4*>(p.mean + ((size_t)c * p.H + h) * p.D + (size_t)hc * 8);
+    const float4 a = mp[0], b = mp[1];
+    m[0] = a.x; m[1] = a.y; m[2] = a.z; m[3] = a.w; m[4] = b.x; m[5] = b.y; m[6] = b.z; m[7] = b.w;
+  }
+  const int r0 = blockIdx.x * p.RP * kLbDeqRows + roff;
+  const int r1 = min((blockIdx.x + 1) * p.RP * kLbDeqRows, p.L);
+  const size_t row0 = (size_t)h * p.T + (size_t)c * p.L + r0;  // this lane's first row
+  const size_t b0 = row0 * p.NB + (hc >> 1);                   // its first block
+  const size_t step = (size_t)p.RP * p.NB;                     // blocks to the lane's next row
+  uint32_t lo[kLbDeqRows], hi[kLbDeqRows], sb[kLbDeqRows];
+#pragma unroll
+  for (int k = 0; k < kLbDeqRows; ++k) {  // every load of the lane before the first store
+    if (r0 + k * p.RP < r1) {
+      const size_t b = b0 + k * step;
+      const uint8_t* pc = p.codes + b * LowBit<BITS>::bytes;
+      if (BITS == 3) {
+        const uint16_t* pw = reinterpret_cast<const uint16_t*>(pc);
+        lo[k] = (uint32_t)pw[0] | ((uint32_t)pw[1] << 16);
+        hi[k] = pw[2];
+      } else {
+        lo[k] = *reinterpret_cast<const uint32_t*>(pc);
+        hi[k] = 0u;
       }
+      sb[k] = p.scales[b];
     }
-    uint32_t o[8];
+  }
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+  for (int k = 0; k < kLbDeqRows; ++k) {
+    if (r0 + k * p.RP >= r1) break;
+    const float S = __builtin_amdgcn_cvt_f32_fp8((int)sb[k], 0);
+    // this half's 8 codes, element 0 at bit 0: bits [8 BITS half, 8 BITS half + 8 BITS)
+    // of the block's field (48 bits at 3 bits per element, 32 at 2)
+    const uint64_t field = ((uint64_t)hi[k] << 32) | lo[k];
+    const uint32_t w = (uint32_t)(field >> (8 * BITS * half));
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
       float x2[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int pos = BITS * (i + u);
-        uint32_t code;
-        if (pos + BITS <= 32) code = (lo >> pos) & ((1u << BITS) - 1u);
-        else if (pos >= 32) code = (hi >> (pos - 32)) & ((1u << BITS) - 1u);
-        else code = ((lo >> pos) | (hi << (32 - pos))) & ((1u << BITS) - 1u);
-        const uint32_t k = code & ((1u << (BITS - 1)) - 1u);
-        const float v = BITS == 3 ? (float)k * 0.5f : (float)k;
+        const uint32_t code = (w >> (BITS * (i + u))) & ((1u << BITS) - 1u);
+        const uint32_t mag = code & ((1u << (BITS - 1)) - 1u);
+        const float v = BITS == 3 ? (float)mag * 0.5f : (float)mag;
         const float vs = __uint_as_float(__float_as_uint(v) | ((code >> (BITS - 1)) << 31));
         float xh = (vs * S) * g;  // two fp32 roundings (v * S is exact)
         if (MEAN) xh = xh + m[i + u];
@@ -249,9 +273,8 @@ __global__ __launch_bounds__(256) void kv_lowbit_dequant_kernel(LowBitDeq p) {
       }
       o[i / 2] = pack_bf16x2(x2[0], x2[1]);
     }
-    uint4* po = reinterpret_cast<uint4*>(p.out + b * 16);
-    po[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    uint16_t* po = p.out + ((row0 + (size_t)k * p.RP) * p.D + (size_t)hc * 8);
+    __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(po));
   }
 }
 
@@ -352,17 +375,18 @@ extern "C" NVFP4KV_API int nvfp4_dequantize_lowbit(const uint8_t* codes, const u
   LowBitDeq p;
   p.codes = codes; p.scales = scales; p.tscale = tensor_scale; p.mean = mean; p.out = out;
   p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.NB = D / 16;
-  p.nblocks = (long long)(n / 16);
-  const long long want = (p.nblocks + 255) / 256;
-  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  const int HB = 2 * p.NB;                // half-blocks per row, at most 512
+  p.RP = HB >= 256 ? 1 : 256 / HB;        // rows per pass
+  const unsigned threads = (unsigned)((HB * p.RP + 63) / 64 * 64);
+  const dim3 grid((unsigned)((chunk_len + p.RP * kLbDeqRows - 1) / (p.RP * kLbDeqRows)), (unsigned)H, (unsigned)nc);
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   if (bits == 3) {
-    if (mean) kv_lowbit_dequant_kernel<3, true><<<grid, 256, 0, s>>>(p);
-    else kv_lowbit_dequant_kernel<3, false><<<grid, 256, 0, s>>>(p);
+    if (mean) kv_lowbit_dequant_kernel<3, true><<<grid, threads, 0, s>>>(p);
+    else kv_lowbit_dequant_kernel<3, false><<<grid, threads, 0, s>>>(p);
   } else {
-    if (mean) kv_lowbit_dequant_kernel<2, true><<<grid, 256, 0, s>>>(p);
-    else kv_lowbit_dequant_kernel<2, false><<<grid, 256, 0, s>>>(p);
+    if (mean) kv_lowbit_dequant_kernel<2, true><<<grid, threads, 0, s>>>(p);
+    else kv_lowbit_dequant_kernel<2, false><<<grid, threads, 0, s>>>(p);
   }
   return launch_status();
 }
