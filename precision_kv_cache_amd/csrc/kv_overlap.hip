@@ -84,24 +84,21 @@ struct Tile {
 // s - depth (if 0 <= s - depth < U); tiles of a unit run head by head.
 // Putting a segment's statistics tiles first gets them dispatched, and the
 // unit ready, as early as possible.  The host keeps the grid (and so every
-// index here) below 2^24.
+// index here) below 2^24; the lookup is closed-form (segment_of), so its cost
+// does not grow with the number of units.
 __device__ __forceinline__ Tile decode(const OverlapParams& p, unsigned b) {
   const int U = 2 * p.nc;
   const unsigned NS = (unsigned)p.H * p.nst, NQ = (unsigned)p.H * p.nqt;
-  int s = 0;
-  unsigned ns = 0, nq = 0;
-  for (; s < U + p.depth; ++s) {
-    ns = s < U ? NS : 0u;
-    nq = (s >= p.depth && s - p.depth < U) ? NQ : 0u;
-    if (b < ns + nq) break;
-    b -= ns + nq;
-  }
+  int s;
+  unsigned off;
+  segment_of(b, U, p.depth, NS, NQ, s, off);
+  const unsigned ns = s < U ? NS : 0u;
   Tile t;
-  t.stats = b < ns;
+  t.stats = off < ns;
   if (t.stats) {
-    t.u = s; t.h = (int)(b / p.nst); t.t = (int)(b % p.nst); t.q = 0;
+    t.u = s; t.h = (int)(off / p.nst); t.t = (int)(off % p.nst); t.q = 0;
   } else {
-    const unsigned j = b - ns;
+    const unsigned j = off - ns;
     t.u = s - p.depth; t.h = (int)(j / p.nqt); t.t = (int)(j % p.nqt); t.q = (unsigned)t.u * NQ + j;
   }
   return t;

@@ -85,14 +85,9 @@ struct VtTile {
 // chunk s (if s < nc), then tpc * H * ncg quantize tiles of chunk s - depth.
 __device__ __forceinline__ VtTile vt_decode(const VtParams& p, unsigned b) {
   const unsigned NS = (unsigned)p.H * p.nst, NQ = (unsigned)p.tpc * p.H * p.ncg;
-  int s = 0;
-  unsigned ns = 0, nq = 0;
-  for (; s < p.nc + p.depth; ++s) {
-    ns = s < p.nc ? NS : 0u;
-    nq = (s >= p.depth && s - p.depth < p.nc) ? NQ : 0u;
-    if (b < ns + nq) break;
-    b -= ns + nq;
-  }
+  int s;
+  segment_of(b, p.nc, p.depth, NS, NQ, s, b);  // b: the offset in segment s from here on
+  const unsigned ns = s < p.nc ? NS : 0u;
   VtTile t;
   t.stats = b < ns;
   if (t.stats) {

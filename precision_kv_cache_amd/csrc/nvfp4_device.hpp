@@ -296,6 +296,37 @@ __device__ __forceinline__ double fetch(const double* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Grids of segments (the single-launch kernels): segment s = 0 .. n - 1 +
+// depth holds ns work items of unit s (when s < n), then nq items of unit
+// s - depth (when 0 <= s - depth < n).  For the flat index b, the segment s
+// and b's offset in it, in closed form: the segments are stats-only
+// (s < min(depth, n)), then either both (depth <= s < n) and quantize-only
+// (n <= s), or empty (n <= s < depth) and quantize-only.  ns, nq >= 1, and
+// the caller keeps the grid below 2^32.
+__device__ __forceinline__ void segment_of(unsigned b, int n, int depth, unsigned ns, unsigned nq, int& s,
+                                           unsigned& off) {
+  const unsigned a = (unsigned)(depth < n ? depth : n);
+  if (b < a * ns) {
+    s = (int)(b / ns);
+    off = b % ns;
+    return;
+  }
+  b -= a * ns;
+  if (depth < n) {
+    const unsigned both = ns + nq, m = (unsigned)(n - depth);
+    if (b < m * both) {
+      s = depth + (int)(b / both);
+      off = b % both;
+      return;
+    }
+    b -= m * both;
+    s = n + (int)(b / nq);
+  } else {
+    s = depth + (int)(b / nq);
+  }
+  off = b % nq;
+}
+
 // Wave-level reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
