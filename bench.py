@@ -74,35 +74,36 @@ def kernel_sources_sha256():
 
 
 def measured_traffic(path):
-    """HBM bytes per quantize call of a kernel path from the committed
-    rocprofv3 counter summary, or None once the kernel sources differ from the
-    measured ones."""
+    """HBM bytes per cache layer of a quantize call of a kernel path, from the
+    committed rocprofv3 counter summary, or None once the kernel sources
+    differ from the measured ones."""
     if path not in TRAFFIC_FILES:
         return None
     try:
         fields = dict(line.split(": ", 1) for line in open(TRAFFIC_FILES[path]).read().splitlines()
-                      if line.startswith(("traffic_bytes_per_call: ", "kernel_sources_sha256: ")))
+                      if line.startswith(("traffic_bytes_per_layer: ", "kernel_sources_sha256: ")))
     except OSError:
         return None
-    if fields.get("kernel_sources_sha256", "").strip() != kernel_sources_sha256():
+    if len(fields) < 2 or fields["kernel_sources_sha256"].strip() != kernel_sources_sha256():
         return None
-    return int(fields["traffic_bytes_per_call"])
+    return int(fields["traffic_bytes_per_layer"])
 
 
 def measured_valu(path):
-    """(wave-level VALU instructions per call, VALU busy %) of the overlapped
-    kernel from the committed rocprofv3 counter summary, or None once the
-    kernel sources differ from the measured ones (or for another path)."""
+    """(wave-level VALU instructions per cache layer, VALU busy %) of the
+    overlapped kernel from the committed rocprofv3 counter summary, or None
+    once the kernel sources differ from the measured ones (or for another
+    path)."""
     if path != "overlap":
         return None
-    keys = ("valu_instructions_per_call: ", "valu_busy_pct: ", "kernel_sources_sha256: ")
+    keys = ("valu_instructions_per_layer: ", "valu_busy_pct: ", "kernel_sources_sha256: ")
     try:
         fields = dict(line.split(": ", 1) for line in open(VALU_FILE).read().splitlines() if line.startswith(keys))
     except OSError:
         return None
     if len(fields) < 3 or fields["kernel_sources_sha256"].strip() != kernel_sources_sha256():
         return None
-    return int(fields["valu_instructions_per_call"]), float(fields["valu_busy_pct"])
+    return int(fields["valu_instructions_per_layer"]), float(fields["valu_busy_pct"])
 METRIC = "NVFP4 4/6 KV quantize GB/s (bytes in+out) and % of MI355X HBM peak"
 
 
@@ -115,6 +116,9 @@ def parse():
     ap.add_argument("--mode", type=int, default=0, help="0 = 4/6, 1 = fixed 6, 2 = fixed 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-pass", action="store_true", help="use the two-pass KV kernels (statistics, then quantize)")
+    ap.add_argument("--schedule", choices=("whole", "layer"), default="whole",
+                    help="whole: the cache head-major, one quantize call per step (the per-layer schedule is "
+                         "reported beside it); layer: one quantize call per layer")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle baseline")
     ap.add_argument("--bits", type=int, default=3, choices=(3, 2), help="element bits of --op lowbit")
     ap.add_argument("--op", choices=("kv", "lowbit", "chunk", "attention", "stream", "gemm", "vt", "act", "weight"),
@@ -172,17 +176,22 @@ def main():
 LOWBIT_METRIC = "{bits}-bit KV quantize GB/s (bytes in+out) and % of MI355X HBM peak"
 
 
-def kv_roofline(dominant, kv_path, bits, qname, dname, ach_gbps, q_ms, qbytes, nblocks):
-    """The dominant call's roofline.  The overlapped quantize kernel is
-    bound by its VALU issue (the 4/6 encode), so it is priced in wave-level
+def kv_roofline(dominant, kv_path, bits, qname, dname, ach_gbps, q_ms, qbytes, nblocks, layers):
+    """The dominant call's roofline; a call covers `layers` cache layers (K
+    and V), qbytes and nblocks are per call.  The overlapped quantize kernel
+    is bound by its VALU issue (the 4/6 encode), so it is priced in wave-level
     VALU instructions per second against the issue peak, the instruction count
-    per call coming from the committed counter summary; its HBM figures follow
-    under "hbm".  Every other dominant call is priced against HBM."""
+    per layer coming from the committed counter summary; its HBM figures
+    follow under "hbm".  Every other dominant call is priced against HBM."""
+    tr = measured_traffic(kv_path) if dominant == "quantize" and bits == 4 else None
     hbm = {"achieved": round(ach_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
            "frac": round(ach_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": qbytes,
-           "traffic": measured_traffic(kv_path) if dominant == "quantize" and bits == 4 else None}
-    kernel = f"{qname} (one layer, K and V)" if dominant == "quantize" else f"{dname} (one layer, K and V)"
+           "traffic": tr * layers if tr else None}
+    what = f"{layers} layers" if layers > 1 else "one layer"
+    kernel = f"{qname} ({what}, K and V)" if dominant == "quantize" else f"{dname} ({what}, K and V)"
     valu = measured_valu(kv_path) if dominant == "quantize" and bits == 4 else None
+    if valu:
+        valu = (valu[0] * layers, valu[1])
     if dominant != "quantize" or bits != 4 or kv_path != "overlap":
         return {"bound": "hbm", "kernel": kernel, "achieved": hbm["achieved"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": hbm["frac"], "traffic": hbm["traffic"], "bytes_per_launch": qbytes}
@@ -200,7 +209,16 @@ def kv_roofline(dominant, kv_path, bits, qname, dname, ach_gbps, q_ms, qbytes, n
 def kv_bench(a, bits):
     """The full-cache workload: every layer smooth-quantized, then the whole
     cache dequantized; NVFP4 4/6 (bits = 4, the headline) or the 3-bit / 2-bit
-    cache (the same readings with fewer element bits)."""
+    cache (the same readings with fewer element bits).
+
+    Two schedules of the same work.  "whole" (the default) holds the cache
+    head-major, K and V each one [H, layers * T, D] tensor in which layer l
+    is tokens l * T .. (l + 1) * T - 1, and makes one quantize call and two
+    dequantize calls per step: every (layer, chunk) is still its own chunk,
+    with its own mean and tensor scales, and the bytes equal those of the
+    per-layer calls.  "layer" makes one quantize call and two dequantize
+    calls per layer on layer-major tensors.  The default line times "whole"
+    and reports "layer" beside it."""
     import torch
 
     import precision_kv_cache_amd as P
@@ -212,6 +230,7 @@ def kv_bench(a, bits):
     s = W.CACHE_LAYER
     H, T, D, L = s.H, s.T, s.D, s.chunk_len
     nlayers = a.layers
+    nc = T // L
 
     t0 = time.time()
     ks, vs = [], []
@@ -222,88 +241,110 @@ def kv_bench(a, bits):
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
-    nc = T // L
-    outs, deq = [], []
-    for l in range(nlayers):
-        outs.append({
-            "k_codes": torch.empty(H, T, D * bits // 8, dtype=torch.uint8, device=dev),
-            "v_codes": torch.empty(H, T, D * bits // 8, dtype=torch.uint8, device=dev),
-            "k_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
-            "v_scales": torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
-            "k_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
-            "v_tensor_scale": torch.empty(nc, dtype=torch.float32, device=dev),
-            "k_mean": torch.empty(nc, H, D, dtype=torch.float32, device=dev),
-        })
-        deq.append((torch.empty(H, T, D, dtype=torch.bfloat16, device=dev),
-                    torch.empty(H, T, D, dtype=torch.bfloat16, device=dev)))
-    counts = torch.zeros(2, 2, dtype=torch.int64, device=dev)
-    ws = torch.zeros(P.nvfp4_kv_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)  # sticky error word 0
+    def outputs(tokens, chunks):
+        return {"k_codes": torch.empty(H, tokens, D * bits // 8, dtype=torch.uint8, device=dev),
+                "v_codes": torch.empty(H, tokens, D * bits // 8, dtype=torch.uint8, device=dev),
+                "k_scales": torch.empty(H, tokens, D // 16, dtype=torch.uint8, device=dev),
+                "v_scales": torch.empty(H, tokens, D // 16, dtype=torch.uint8, device=dev),
+                "k_tensor_scale": torch.empty(chunks, dtype=torch.float32, device=dev),
+                "v_tensor_scale": torch.empty(chunks, dtype=torch.float32, device=dev),
+                "k_mean": torch.empty(chunks, H, D, dtype=torch.float32, device=dev)}
+
+    # dequantized output, shared by the schedules (each overwrites all of it)
+    deq_buf = [torch.empty(nlayers * H * T * D, dtype=torch.bfloat16, device=dev) for _ in range(2)]
     stream = torch.cuda.current_stream()
 
-    def quant(l, ev=None):
-        o = outs[l]
-        if ev is not None:
-            ev[0].record(stream)
+    def quant_call(k, v, o, ws):
         if bits == 4:
-            P.nvfp4_kv_smooth_quantize(ks[l], vs[l], L, a.mode, out=o, workspace=ws, stream=stream,
-                                       two_pass=a.two_pass)
+            P.nvfp4_kv_smooth_quantize(k, v, L, a.mode, out=o, workspace=ws, stream=stream, two_pass=a.two_pass)
         else:
-            P.nvfp4_kv_smooth_quantize_lowbit(ks[l], vs[l], L, bits, a.mode, out=o, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+            P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, a.mode, out=o, workspace=ws, stream=stream)
 
-    def dequant(l, ev=None):
-        o = outs[l]
-        if ev is not None:
-            ev[0].record(stream)
+    def dequant_call(o, dk, dv):
         if bits == 4:
-            P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, out=deq[l][0],
+            P.nvfp4_dequantize(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, out=dk,
                                stream=stream)
-            P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, out=deq[l][1],
-                               stream=stream)
+            P.nvfp4_dequantize(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, out=dv, stream=stream)
         else:
             P.nvfp4_dequantize_lowbit(o["k_codes"], o["k_scales"], o["k_tensor_scale"], o["k_mean"], L, bits,
-                                      out=deq[l][0], stream=stream)
-            P.nvfp4_dequantize_lowbit(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, bits,
-                                      out=deq[l][1], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+                                      out=dk, stream=stream)
+            P.nvfp4_dequantize_lowbit(o["v_codes"], o["v_scales"], o["v_tensor_scale"], None, L, bits, out=dv,
+                                      stream=stream)
 
-    def step(qev=None, dev_ev=None):
-        for l in range(nlayers):
-            quant(l, None if qev is None else qev[l])
-        for l in range(nlayers):
-            dequant(l, None if dev_ev is None else dev_ev[l])
+    def schedule(kind):
+        """(quantize calls, dequantize calls, outputs for the parity sample,
+        dequantized (K, V) for it, workspace) of one step."""
+        if kind == "whole":
+            K = torch.empty(H, nlayers * T, D, dtype=torch.bfloat16, device=dev)
+            V = torch.empty_like(K)
+            for l in range(nlayers):
+                K[:, l * T:(l + 1) * T] = ks[l]
+                V[:, l * T:(l + 1) * T] = vs[l]
+            o = outputs(nlayers * T, nlayers * nc)
+            dk = deq_buf[0].view(H, nlayers * T, D)
+            dv = deq_buf[1].view(H, nlayers * T, D)
+            ws = torch.zeros(P.nvfp4_kv_workspace_bytes(H, nlayers * T, D, L), dtype=torch.uint8, device=dev)
+            return ([lambda: quant_call(K, V, o, ws)], [lambda: dequant_call(o, dk, dv)], o, (dk, dv), ws)
+        os_ = [outputs(T, nc) for _ in range(nlayers)]
+        dks = [deq_buf[0][l * H * T * D:(l + 1) * H * T * D].view(H, T, D) for l in range(nlayers)]
+        dvs = [deq_buf[1][l * H * T * D:(l + 1) * H * T * D].view(H, T, D) for l in range(nlayers)]
+        ws = torch.zeros(P.nvfp4_kv_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
+        return ([(lambda l=l: quant_call(ks[l], vs[l], os_[l], ws)) for l in range(nlayers)],
+                [(lambda l=l: dequant_call(os_[l], dks[l], dvs[l])) for l in range(nlayers)], os_[0],
+                (dks[0], dvs[0]), ws)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: one event pair around the whole run, plus an event pair
-    # around every library call of the last step (same stream) for the
-    # per-call durations the roofline uses
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    qev = [(E(), E()) for _ in range(nlayers)]
-    dev_ev = [(E(), E()) for _ in range(nlayers)]
-    start, stop = E(), E()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(a.steps):
-        last = i == a.steps - 1
-        step(qev if last else None, dev_ev if last else None)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / a.steps
-    # every quantize call of the warm-up and timed steps shares ws: its sticky
-    # error word is non-zero if any of them had a wait time out
-    wait_errors = P.kv_error_word(ws)
-    if wait_errors:
-        print(f"bench.py: a quantize call's bounded wait timed out (error word {wait_errors}); "
-              "its outputs are invalid, so no result is reported", flush=True)
-        sys.exit(3)
-    q_ms = sum(e0.elapsed_time(e1) for e0, e1 in qev) / nlayers    # one layer's quantize call (K and V)
-    d_ms = sum(e0.elapsed_time(e1) for e0, e1 in dev_ev) / nlayers  # one layer's dequantize calls (K and V)
+
+    def run(kind, warmup, steps):
+        """Times `steps` steps after `warmup` untimed ones: one event pair
+        around the whole run, plus an event pair around every library call of
+        the last step (same stream) for the per-call durations."""
+        qc, dc, o, dq, ws = schedule(kind)
+
+        def step(qev=None, dev_=None):
+            for i, f in enumerate(qc):
+                if qev is not None:
+                    qev[i][0].record(stream)
+                f()
+                if qev is not None:
+                    qev[i][1].record(stream)
+            for i, f in enumerate(dc):
+                if dev_ is not None:
+                    dev_[i][0].record(stream)
+                f()
+                if dev_ is not None:
+                    dev_[i][1].record(stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        qev = [(E(), E()) for _ in qc]
+        dev_ = [(E(), E()) for _ in dc]
+        start, stop = E(), E()
+        start.record(stream)
+        for i in range(steps):
+            last = i == steps - 1
+            step(qev if last else None, dev_ if last else None)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        # every quantize call of the run shares ws: its sticky error word is
+        # non-zero if any of them had a wait time out
+        err = P.kv_error_word(ws)
+        if err:
+            print(f"bench.py: a quantize call's bounded wait timed out (error word {err}); "
+                  "its outputs are invalid, so no result is reported", flush=True)
+            sys.exit(3)
+        return {"ms_step": start.elapsed_time(stop) / steps,
+                "q_call_ms": sum(e0.elapsed_time(e1) for e0, e1 in qev) / len(qev),
+                "d_call_ms": sum(e0.elapsed_time(e1) for e0, e1 in dev_) / len(dev_),
+                "calls_per_step": len(qc), "out": o, "deq": dq, "err": err}
+
+    main_kind = a.schedule
+    r = run(main_kind, a.warmup, a.steps)
+    ms_step, wait_errors = r["ms_step"], r["err"]
+    layers_per_call = nlayers if main_kind == "whole" else 1
+    q_ms = r["q_call_ms"] / layers_per_call   # one layer's share of a quantize call (K and V)
+    d_ms = r["d_call_ms"] / layers_per_call   # one layer's share of the dequantize calls (K and V)
 
     qbytes_layer = kv_bytes(H, T, D, L, True, bits) + kv_bytes(H, T, D, L, False, bits)
     dbytes_layer = qbytes_layer
@@ -311,6 +352,7 @@ def kv_bench(a, bits):
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     q_gbps = qbytes_layer / (q_ms * 1e-3) / 1e9
     d_gbps = dbytes_layer / (d_ms * 1e-3) / 1e9
+    check_out, check_deq = r["out"], r["deq"]
 
     # 4/6 choice histogram on one layer (outside the timed region)
     if bits == 4:
@@ -357,34 +399,52 @@ def kv_bench(a, bits):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "full 8-chunk KV cache: 30 layers x K,V bf16 [24 heads, 56320 tokens, 128], "
-                        f"chunks of 7040 tokens; {what} every layer, then dequantize the cache",
+            "workload": f"full 8-chunk KV cache: {nlayers} layers x K,V bf16 [24 heads, 56320 tokens, 128], "
+                        f"chunks of 7040 tokens; {what} every layer, then dequantize the cache"
+                        + ("; the cache held head-major, K and V each one [24, layers x 56320, 128] tensor, "
+                           "one quantize call and two dequantize calls per step" if main_kind == "whole" else
+                           "; one quantize call and two dequantize calls per layer"),
             "layers": nlayers, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L, "element_bits": bits,
             "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": step_bytes,
-            "kv_path": kv_path,
+            "kv_path": kv_path, "schedule": main_kind,
         },
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "quantize_GBps": round(q_gbps, 1),
         "dequantize_GBps": round(d_gbps, 1),
-        "quantize_call_ms": round(q_ms, 4),
-        "dequantize_call_ms": round(d_ms, 4),
+        "quantize_ms_per_layer": round(q_ms, 4),
+        "dequantize_ms_per_layer": round(d_ms, 4),
+        "quantize_call_ms": round(r["q_call_ms"], 4),
+        "dequantize_call_ms": round(r["d_call_ms"], 4),
         "choice_counts_layer0": choice,
         "d2d_copy_GBps": round(copy_gbps, 1),
-        "roofline": kv_roofline(dominant, kv_path, bits, qname, dname, ach, q_ms, qbytes_layer,
-                                2 * H * T * (D // 16)),
+        "roofline": kv_roofline(dominant, kv_path, bits, qname, dname, ach, r["q_call_ms"],
+                                layers_per_call * qbytes_layer, layers_per_call * 2 * H * T * (D // 16),
+                                layers_per_call),
         "input_generation_s": round(gen_s, 2),
         "quantize_wait_timeouts": wait_errors,
     }
     if not a.no_cpu_baseline:
         # the oracle's leg: its rate on the host, and the last timed step's
         # outputs of layer 0 chunk 0 compared with it bit for bit
-        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds, check=(outs[0], deq[0]), bits=bits)
+        result["cpu_baseline"] = cpu_baseline(ks, vs, L, a.mode, a.cpu_seconds, check=(check_out, check_deq),
+                                              bits=bits)
         if not result["cpu_baseline"]["parity_check"]["bit_exact"]:
             print("bench.py: the sampled chunk differs from the oracle: " + json.dumps(result["cpu_baseline"]),
                   flush=True)
             sys.exit(3)
-    outs.clear()
-    deq.clear()
+    del r, check_out, check_deq
+    torch.cuda.empty_cache()
+    if main_kind == "whole":
+        # the same work in per-layer calls, for comparison
+        rl = run("layer", 1, 3)
+        result["per_layer_schedule"] = {
+            "value": round(step_bytes / (rl["ms_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(rl["ms_step"], 4), "steps": 3, "warmup": 1,
+            "quantize_call_ms": round(rl["q_call_ms"], 4), "dequantize_call_ms": round(rl["d_call_ms"], 4),
+            "calls_per_step": 3 * nlayers}
+        del rl
+        torch.cuda.empty_cache()
+    del deq_buf
     torch.cuda.empty_cache()
     if bits == 4:
         result["one_chunk_configs"] = one_chunk_timing(P, W, a.mode, stream, q_ms)
