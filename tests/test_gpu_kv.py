@@ -217,3 +217,34 @@ def test_dequant_without_mean_and_empty():
     e = torch.empty(0, 64, 32, dtype=torch.bfloat16, device="cuda")
     r = P.nvfp4_kv_smooth_quantize(e, e.clone(), 64)
     assert r["k_codes"].numel() == 0
+
+
+def test_layers_in_one_call_equal_per_layer_calls():
+    """A cache held head-major, [H, layers * T, D] with layer l at tokens
+    l * T .., quantized (and dequantized) in one call gives, layer by layer,
+    the bytes of one call per layer: each (layer, chunk) is its own chunk with
+    its own mean and tensor scales.  Both kernel forms."""
+    s = W.KVShape(6, 2 * 2048, 128, 2048)  # per layer: 2 chunks of 2048 tokens
+    nl = 3
+    layers = [W.gaussian_kv(s, 500 + l, device="cuda") for l in range(nl)]
+    K = torch.cat([k for k, _ in layers], dim=1).contiguous()
+    V = torch.cat([v for _, v in layers], dim=1).contiguous()
+    nc = s.T // s.chunk_len
+    for path in PATHS:
+        say("layers in one call", s, nl, path)
+        whole = P.nvfp4_kv_smooth_quantize(K, V, s.chunk_len, choice_counts=True, **path)
+        dk = P.nvfp4_dequantize(whole["k_codes"], whole["k_scales"], whole["k_tensor_scale"], whole["k_mean"],
+                                s.chunk_len)
+        counts = torch.zeros_like(whole["choice_counts"])
+        for l, (k, v) in enumerate(layers):
+            r = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, choice_counts=True, **path)
+            rk = P.nvfp4_dequantize(r["k_codes"], r["k_scales"], r["k_tensor_scale"], r["k_mean"], s.chunk_len)
+            rows = slice(l * s.T, (l + 1) * s.T)
+            chunks = slice(l * nc, (l + 1) * nc)
+            for key in ("k_codes", "v_codes", "k_scales", "v_scales"):
+                assert torch.equal(whole[key][:, rows], r[key]), (path, l, key)
+            for key in ("k_tensor_scale", "v_tensor_scale", "k_mean"):
+                assert torch.equal(whole[key][chunks], r[key]), (path, l, key)
+            assert torch.equal(dk[:, rows], rk), (path, l)
+            counts += r["choice_counts"]
+        assert torch.equal(whole["choice_counts"], counts), path
