@@ -1073,6 +1073,11 @@ VT_METRIC = "V quantize with 16-token blocks per channel: GB/s (bytes in + out) 
 
 
 def vt_bench(a):
+    """V quantized with 16-token blocks per channel.  Schedule "whole" (the
+    default): V of every layer held head-major as one [24, layers * 56320,
+    128] tensor (layer l = tokens l * 56320 ..), one call per step; each
+    (layer, chunk) keeps its own tensor scale.  The one-layer call is timed
+    beside it.  Schedule "layer": one layer's V per call."""
     import torch
 
     import precision_kv_cache_amd as P
@@ -1083,51 +1088,79 @@ def vt_bench(a):
     torch.cuda.set_device(dev)
     s = W.CACHE_LAYER
     H, T, D, L = s.H, s.T, s.D, s.chunk_len
+    nl = a.layers if a.schedule == "whole" else 1
     t0 = time.time()
-    _, v = W.gaussian_kv(s, W.cache_layer_seed(0), device=dev)
+    vl = []
+    for l in range(nl):
+        _, v1 = W.gaussian_kv(s, W.cache_layer_seed(l), device=dev)
+        vl.append(v1)
+    v = vl[0] if nl == 1 else torch.cat(vl, dim=1).contiguous()
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    out = P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode)
-    ws = torch.zeros(P.lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, T, D, L), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    for _ in range(a.warmup):
-        P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode, out=out, workspace=ws, stream=stream)
-    torch.cuda.synchronize()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [(E(), E()) for _ in range(a.steps)]
-    start, stop = E(), E()
-    start.record(stream)
-    for i in range(a.steps):
-        ev[i][0].record(stream)
-        P.nvfp4_kv_quantize_v_tblocks(v, L, a.mode, out=out, workspace=ws, stream=stream)
-        ev[i][1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / a.steps
-    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / a.steps
-    nbytes = kv_bytes(H, T, D, L, False)
+
+    def timed(x, warmup, steps):
+        tt = x.shape[1]
+        out = P.nvfp4_kv_quantize_v_tblocks(x, L, a.mode)
+        ws = torch.zeros(P.lib().nvfp4_kv_quantize_v_tblocks_workspace_bytes(H, tt, D, L), dtype=torch.uint8,
+                         device=dev)
+        for _ in range(warmup):
+            P.nvfp4_kv_quantize_v_tblocks(x, L, a.mode, out=out, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        ev = [(E(), E()) for _ in range(steps)]
+        start, stop = E(), E()
+        start.record(stream)
+        for i in range(steps):
+            ev[i][0].record(stream)
+            P.nvfp4_kv_quantize_v_tblocks(x, L, a.mode, out=out, workspace=ws, stream=stream)
+            ev[i][1].record(stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        # the sticky error word after the warm-up and timed calls (0: no wait timed out)
+        err = P.kv_error_word(ws)
+        if err:
+            print(f"bench.py: a bounded wait timed out (error word {err}); no result is reported", flush=True)
+            sys.exit(3)
+        return start.elapsed_time(stop) / steps, sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps, out
+
+    ms_step, call_ms, out = timed(v, a.warmup, a.steps)
+    nbytes = nl * kv_bytes(H, T, D, L, False)
     gbps = nbytes / (ms_step * 1e-3) / 1e9
     call_gbps = nbytes / (call_ms * 1e-3) / 1e9
+    what = (f"V of {nl} 8-chunk cache layers held head-major, bf16 [24, {nl} x 56320, 128], one call" if nl > 1
+            else "V of one 8-chunk cache layer, bf16 [24, 56320, 128]")
     result = {
         "metric": VT_METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "V of one 8-chunk cache layer, bf16 [24, 56320, 128], chunks of 7040, quantized "
-                               "with 16-token blocks per (head, channel)",
-                   "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
-                   "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": nbytes},
+        "config": {"workload": what + ", chunks of 7040, quantized with 16-token blocks per (head, channel)",
+                   "layers": nl, "heads": H, "tokens": T, "head_dim": D, "chunk_len": L,
+                   "mode": ["4over6", "fixed6", "fixed4"][a.mode], "bytes_per_step": nbytes,
+                   "schedule": a.schedule},
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "kernel": "nvfp4_kv_quantize_v_tblocks (one layer's V)",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"nvfp4_kv_quantize_v_tblocks ({nl} layers' V)" if nl > 1
+                     else "nvfp4_kv_quantize_v_tblocks (one layer's V)",
                      "achieved": round(call_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes},
         "input_generation_s": round(gen_s, 2),
-        # the sticky error word after the warm-up and timed calls (0: no wait timed out)
-        "quantize_wait_timeouts": P.kv_error_word(ws),
+        "quantize_wait_timeouts": 0,
     }
-    if result["quantize_wait_timeouts"]:
-        print(f"bench.py: a bounded wait timed out (error word {result['quantize_wait_timeouts']}); "
-              "no result is reported", flush=True)
-        sys.exit(3)
+    if nl > 1:
+        # layer 0 of the whole-cache call against the one-layer call, bit for bit
+        ms1, call1, out1 = timed(vl[0], 2, 10)
+        nb1 = kv_bytes(H, T, D, L, False)
+        same = (torch.equal(out["codes"][:, :, :T // 2], out1["codes"]) and
+                torch.equal(out["scales"][:, :, :T // 16], out1["scales"]) and
+                torch.equal(out["tensor_scale"][:T // L], out1["tensor_scale"]))
+        result["per_layer_schedule"] = {"value": round(nb1 / (ms1 * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                        "ms_per_call": round(ms1, 4), "steps": 10, "warmup": 2,
+                                        "layer0_bytes_equal_whole_cache_call": bool(same)}
+        if not same:
+            print("bench.py: layer 0 of the whole-cache call differs from the one-layer call", flush=True)
+            sys.exit(3)
+    v = vl[0]
     if not a.no_cpu_baseline:
         import oracle as O
         nt = O.default_threads()
