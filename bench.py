@@ -258,7 +258,8 @@ def kv_bench(a, bits):
         if bits == 4:
             P.nvfp4_kv_smooth_quantize(k, v, L, a.mode, out=o, workspace=ws, stream=stream, two_pass=a.two_pass)
         else:
-            P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, a.mode, out=o, workspace=ws, stream=stream)
+            P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, a.mode, out=o, workspace=ws, stream=stream,
+                                              two_pass=a.two_pass)
 
     def dequant_call(o, dk, dv):
         if bits == 4:
@@ -375,7 +376,7 @@ def kv_bench(a, bits):
     copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    kv_path = "two-pass" if a.two_pass or D != 128 or bits != 4 else "overlap"
+    kv_path = "two-pass" if a.two_pass or D != 128 else "overlap"
     dominant = "quantize" if q_ms >= d_ms else "dequantize"
     ach = q_gbps if dominant == "quantize" else d_gbps
     if bits == 4:

@@ -410,8 +410,15 @@ NVFP4KV_API int nvfp4_kv_quantize_v_tblocks(const uint16_t* v, int H, int T, int
  *   k_codes, v_codes  out, [H, T, D * bits / 8], 2-byte (3 bits) or 4-byte
  *                 (2 bits) aligned.
  *   choice_counts out, nullable, uint64 [2][2]: {K, V} x {kept c_a, kept c_b}.
- *   workspace     >= nvfp4_kv_workspace_bytes(), 256-byte aligned; its
- *                 contents on entry are ignored (these kernels never wait).
+ *   mode          as above, optionally | NVFP4_KV_TWO_PASS: for D = 128 the
+ *                 call runs the overlapped kernel of nvfp4_kv_smooth_quantize
+ *                 (statistics and quantize tiles in one launch), otherwise, or
+ *                 with the bit, the two-pass kernels.  Both write the same
+ *                 bytes given the same mean.
+ *   workspace     >= nvfp4_kv_workspace_bytes(), 256-byte aligned; its first
+ *                 word is the sticky error word, as for
+ *                 nvfp4_kv_smooth_quantize (zero it before the first call),
+ *                 and the rest of its contents on entry are ignored.
  */
 NVFP4KV_API int nvfp4_kv_smooth_quantize_lowbit(const uint16_t* k, const uint16_t* v, int H, int T, int D,
                                                 int chunk_len, int bits, int mode, uint8_t* k_codes,

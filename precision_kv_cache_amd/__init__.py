@@ -209,23 +209,25 @@ def lowbit_outputs(H, T, D, chunk_len, bits, device, choice_counts=False):
 
 
 def nvfp4_kv_smooth_quantize_lowbit(k, v, chunk_len, bits, mode=MODE_4OVER6, choice_counts=False, out=None,
-                                    workspace=None, stream=None):
+                                    workspace=None, stream=None, two_pass=False):
     """K smoothing + 3-bit or 2-bit quantization of K, V bf16 [H, T, D]: the
     outputs of nvfp4_kv_smooth_quantize with codes [H, T, D * bits / 8] and
-    choice_counts {K, V} x {kept c_a, kept c_b}."""
+    choice_counts {K, V} x {kept c_a, kept c_b}.  two_pass forces the two-pass
+    kernels (the default is the overlapped kernel when D = 128)."""
     _bf16_dev(k, "k"); _bf16_dev(v, "v")
     if k.shape != v.shape or k.dim() != 3:
         raise ValueError("k and v must both be [H, T, D]")
     H, T, D = k.shape
     if out is None:
         out = lowbit_outputs(H, T, D, chunk_len, bits, k.device, choice_counts)
-    if workspace is None:
-        workspace = torch.empty(max(1, nvfp4_kv_workspace_bytes(H, T, D, chunk_len)), dtype=torch.uint8,
+    if workspace is None:  # zeroed: its first word is the sticky error word
+        workspace = torch.zeros(max(1, nvfp4_kv_workspace_bytes(H, T, D, chunk_len)), dtype=torch.uint8,
                                 device=k.device)
     rc = lib().nvfp4_kv_smooth_quantize_lowbit(
-        _ptr(k), _ptr(v), H, T, D, chunk_len, bits, mode, _ptr(out["k_codes"]), _ptr(out["v_codes"]),
-        _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]), _ptr(out["v_tensor_scale"]),
-        _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(workspace), workspace.numel(), _stream(stream))
+        _ptr(k), _ptr(v), H, T, D, chunk_len, bits, mode | (KV_TWO_PASS if two_pass else 0), _ptr(out["k_codes"]),
+        _ptr(out["v_codes"]), _ptr(out["k_scales"]), _ptr(out["v_scales"]), _ptr(out["k_tensor_scale"]),
+        _ptr(out["v_tensor_scale"]), _ptr(out["k_mean"]), _ptr(out.get("choice_counts")), _ptr(workspace),
+        workspace.numel(), _stream(stream))
     _check(rc, "nvfp4_kv_smooth_quantize_lowbit")
     return out
 

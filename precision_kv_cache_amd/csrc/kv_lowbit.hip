@@ -31,96 +31,13 @@
 
 #include "host_common.hpp"
 #include "kv_two_pass.hpp"
+#include "kv_overlap.hpp"
+#include "lowbit_device.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4kv.h"
 
 namespace nvfp4 {
 namespace {
-
-template <int BITS>
-struct LowBit {
-  static constexpr float ca = BITS == 3 ? 1.5f : 1.0f;  // maps the block maximum onto the top magnitude
-  static constexpr float cb = BITS == 3 ? 1.0f : 1.5f;  // the 3 : 2 companion
-  static constexpr int bytes = 2 * BITS;                // code bytes per block
-};
-
-template <int BITS>
-__host__ __device__ constexpr float lowbit_constant(int mode) {
-  return 448.0f * (mode == kModeFixed6 ? LowBit<BITS>::ca
-                                       : mode == kModeFixed4 ? LowBit<BITS>::cb
-                                                             : (LowBit<BITS>::ca < LowBit<BITS>::cb ? LowBit<BITS>::ca
-                                                                                                    : LowBit<BITS>::cb));
-}
-
-// One candidate on a block z (encode domain) with scale S and reciprocal R:
-// the packed codes (lo: bits 0..31, hi: bits 32..47) and the fp32 error.
-template <int BITS>
-__device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S, float R, uint32_t& lo,
-                                                  uint32_t& hi) {
-  float elo = 0.0f, ehi = 0.0f;
-  lo = 0u;
-  hi = 0u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float y = z[i] * R;
-    const float a = fabsf(y);
-    float k;  // magnitude index, as a float
-    if (BITS == 3)
-      k = fminf(__builtin_rintf(a * 2.0f), 3.0f);  // rint: nearest, ties to even
-    else
-      k = a > 0.5f ? 1.0f : 0.0f;                 // the tie 0.5 goes to the even code 0
-    const float v = BITS == 3 ? k * 0.5f : k;      // magnitude value, exact
-    const uint32_t neg = __float_as_uint(y) >> 31;
-    const float vs = __uint_as_float(__float_as_uint(v) | (neg << 31));  // signed value (-0 kept)
-    const float e = __builtin_fmaf(-vs, S, z[i]);  // v * S is exact: fl(z - v S)
-    if (i < 8)
-      elo = __builtin_fmaf(e, e, elo);
-    else
-      ehi = __builtin_fmaf(e, e, ehi);
-    const uint32_t code = (uint32_t)k | (neg << (BITS - 1));
-    const int pos = BITS * i;
-    if (pos < 32) lo |= code << pos;
-    if (pos + BITS > 32) hi |= code >> (32 - pos > 0 ? 32 - pos : 0) << (pos > 32 ? pos - 32 : 0);
-  }
-  return elo + ehi;
-}
-
-struct LowBitBlock {
-  uint32_t lo, hi, scale, useb;
-};
-
-template <int BITS, int MODE>
-__device__ __forceinline__ LowBitBlock lowbit_block16(const float (&z)[16], const float2* tab) {
-  const float t = block_absmax(z);
-  // both candidate scales in one conversion: byte 0 = E4M3(t / ca), byte 1 = E4M3(t / cb);
-  // the division by 1.5 is the IEEE quotient (correctly rounded division)
-  const float ra = LowBit<BITS>::ca == 1.0f ? t : t / LowBit<BITS>::ca;
-  const float rb = LowBit<BITS>::cb == 1.0f ? t : t / LowBit<BITS>::cb;
-  const uint32_t s = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, __float_as_int(t), false) & 0xffffu;
-  LowBitBlock out;
-  if (MODE == kModeFixed6) {
-    const float2 c = tab[s & 0xffu];
-    (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
-    out.scale = s & 0xffu;
-    out.useb = 0;
-  } else if (MODE == kModeFixed4) {
-    const float2 c = tab[s >> 8];
-    (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
-    out.scale = s >> 8;
-    out.useb = 1;
-  } else {
-    const float2 c0 = tab[s & 0xffu], c1 = tab[s >> 8];
-    uint32_t la, ha, lb, hb;
-    const float ea = lowbit_candidate<BITS>(z, c0.x, c0.y, la, ha);
-    const float eb = lowbit_candidate<BITS>(z, c1.x, c1.y, lb, hb);
-    const bool useb = eb < ea;
-    out.lo = useb ? lb : la;
-    out.hi = useb ? hb : ha;
-    out.scale = useb ? (s >> 8) : (s & 0xffu);
-    out.useb = useb ? 1u : 0u;
-  }
-  return out;
-}
 
 // One (chunk, tensor, head, row tile) of the quantize: lane (roff, col)
 // takes rows r0 + roff, + RP, ... of column block col.
@@ -193,6 +110,7 @@ __global__ __launch_bounds__(kMaxThreads) void kv_lowbit_quant_kernel(KVParams p
     store_wg_tally(p.tally + ((((size_t)c * 2 + tau) * p.H + h) * p.nqt + qt) * 4, t, sh_tally);
   }
 }
+
 
 struct LowBitDeq {
   const uint8_t* codes;
@@ -300,6 +218,8 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize_lowbit(const uint16_t* k, co
                                                            void* workspace, size_t workspace_bytes,
                                                            void* stream) noexcept {
   if (!kv_shape_ok(H, T, D, chunk_len) || (bits != 3 && bits != 2)) return NVFP4_ERR_SHAPE;
+  const bool two_pass = (mode & NVFP4_KV_TWO_PASS) != 0;
+  mode &= ~NVFP4_KV_TWO_PASS;
   if (mode < 0 || mode > 2) return NVFP4_ERR_MODE;
   if (H == 0 || T == 0) return NVFP4_OK;
   if (!k || !v || !k_codes || !v_codes || !k_scales || !v_scales || !k_tensor_scale || !v_tensor_scale || !k_mean)
@@ -311,7 +231,9 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize_lowbit(const uint16_t* k, co
     return NVFP4_ERR_ALIGN;
   const KVGeom g = kv_geom(H, T, D, chunk_len);
   const KVWorkspace wl = kv_workspace_layout(g);
-  if (!workspace || workspace_bytes < wl.total) return NVFP4_ERR_WORKSPACE;
+  // the kernels may use every byte nvfp4_kv_workspace_bytes covers
+  const size_t ws_need = nvfp4_kv_workspace_bytes(H, T, D, chunk_len);
+  if (!workspace || workspace_bytes < ws_need) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   const size_t n = (size_t)H * T * D;
   const Range in[2] = {range_of(k, n * 2), range_of(v, n * 2)};
@@ -319,12 +241,24 @@ extern "C" NVFP4KV_API int nvfp4_kv_smooth_quantize_lowbit(const uint16_t* k, co
                         range_of(k_scales, n / 16), range_of(v_scales, n / 16),
                         range_of(k_tensor_scale, (size_t)g.nc * 4), range_of(v_tensor_scale, (size_t)g.nc * 4),
                         range_of(k_mean, (size_t)g.nc * H * D * 4), range_of(choice_counts, 32),
-                        range_of(workspace, wl.total)};
+                        range_of(workspace, ws_need)};
   if (any_alias(in, 2, out, 9)) return NVFP4_ERR_ALIAS;
 
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
+  if (!two_pass && D == 128) {  // the single-launch overlapped kernel, as for NVFP4
+    OverlapParams q;
+    q.x[0] = k; q.x[1] = v;
+    q.codes[0] = k_codes; q.codes[1] = v_codes;
+    q.scales[0] = k_scales; q.scales[1] = v_scales;
+    q.tscale[0] = k_tensor_scale; q.tscale[1] = v_tensor_scale;
+    q.kmean = k_mean;
+    q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
+    const int rc = overlap_try_launch(q, mode, bits, workspace, workspace_bytes, choice_counts,
+                                      static_cast<unsigned*>(workspace), s);
+    if (rc <= 0) return rc;  // enqueued, or a launch error
+  }
   KVParams p;
   p.x[0] = k; p.x[1] = v;
   p.codes[0] = k_codes; p.codes[1] = v_codes;

@@ -35,6 +35,7 @@
 
 #include "host_common.hpp"
 #include "kv_overlap.hpp"
+#include "lowbit_device.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4kv.h"
 
@@ -190,7 +191,7 @@ __device__ __forceinline__ void v_stats_batch(const uint4 (&a)[kSBatch], int r, 
 // One (unit, head, tile) statistics task.  Lane t reads the 16-byte half
 // t % 16 (channels 8 (t % 16) ..) of rows r0 + t / 16, + 16, + 32, ...
 // K: fp64 channel sums and channel max / min; V: the largest magnitude.
-template <int MODE>
+template <int MODE, int BITS>
 __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double* shs, uint32_t* shx, float* shw,
                            unsigned* sh_flag) {
   const int c = u >> 1, tau = u & 1;
@@ -364,7 +365,11 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
     float Am = 0.0f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) Am = fmaxf(Am, shw[q]);
-    const float C = mode_constant(MODE);
+    float C;  // the tensor constant of the element format
+    if constexpr (BITS == 4)
+      C = mode_constant(MODE);
+    else
+      C = lowbit_constant<BITS>(MODE);
     const float g = Am > 0.0f ? C / Am : 0.0f;
     if (tid == 0) p.tscale[tau][c] = Am / C;  // output only: visible at kernel end
     (void)__hip_atomic_exchange(p.ready + ((size_t)tid * (2 * p.nc) + u) * kReplicaStride,
@@ -376,8 +381,9 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
 
 // One (unit, head, tile) quantize task: wait for the unit, then encode rows
 // r0 .. r0 + 255 of the head.  Lane (roff, col) takes rows r0 + roff,
-// + 32, ... of column block col.
-template <int MODE>
+// + 32, ... of column block col.  NVFP4 (BITS = 4) or the 3-bit / 2-bit
+// cache.
+template <int MODE, int BITS>
 __device__ void quant_tile(const OverlapParams& p, int u, int h, int qt, unsigned qidx, float* sh_mean,
                            float* shw, unsigned* sh_flag, const float2* tab, unsigned* sh_tally) {
   const int c = u >> 1, tau = u & 1;
@@ -422,11 +428,17 @@ __device__ void quant_tile(const OverlapParams& p, int u, int h, int qt, unsigne
   const int r0 = qt * kOvQuantRows;
   const int r1 = min(r0 + kOvQuantRows, p.L);
   const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
-  const uint2 n = tau == 0
-      ? quant_rows<MODE, true, true, kQBatch, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
-                                                   kQRowsPerPass, kNB, col, m, g, tab)
-      : quant_rows<MODE, false, true, kQBatch, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff, r1,
-                                                    kQRowsPerPass, kNB, col, m, g, tab);
+  uint2 n;
+  if constexpr (BITS == 4)
+    n = tau == 0 ? quant_rows<MODE, true, true, kQBatch, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
+                                                             kQRowsPerPass, kNB, col, m, g, tab)
+                 : quant_rows<MODE, false, true, kQBatch, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff,
+                                                              r1, kQRowsPerPass, kNB, col, m, g, tab);
+  else
+    n = tau == 0 ? lowbit_quant_rows<BITS, MODE, true, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
+                                                           kQRowsPerPass, kNB, col, m, g, tab)
+                 : lowbit_quant_rows<BITS, MODE, false, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff, r1,
+                                                            kQRowsPerPass, kNB, col, m, g, tab);
   if (p.choice) {
     const unsigned t[4] = {tau == 0 ? n.x : 0u, tau == 0 ? n.y : 0u, tau == 1 ? n.x : 0u, tau == 1 ? n.y : 0u};
     store_wg_tally(p.tally + (size_t)qidx * 4, t, sh_tally);
@@ -435,7 +447,7 @@ __device__ void quant_tile(const OverlapParams& p, int u, int h, int qt, unsigne
 
 }  // namespace
 
-template <int MODE>
+template <int MODE, int BITS>
 __global__ __launch_bounds__(kOvThreads) void kv_overlap_kernel(OverlapParams p) {
   __shared__ double shs[kWaves * kD];
   __shared__ uint32_t shx[kWaves * kD];
@@ -446,10 +458,10 @@ __global__ __launch_bounds__(kOvThreads) void kv_overlap_kernel(OverlapParams p)
   __shared__ unsigned sh_tally[4 * kWaves];
   const Tile t = decode(p, blockIdx.x);
   if (t.stats) {
-    stats_tile<MODE>(p, t.u, t.h, t.t, shs, shx, shw, &sh_flag);
+    stats_tile<MODE, BITS>(p, t.u, t.h, t.t, shs, shx, shw, &sh_flag);
   } else {
     fill_scale_table(sh_tab);
-    quant_tile<MODE>(p, t.u, t.h, t.t, t.q, sh_mean, shw, &sh_flag, sh_tab, sh_tally);
+    quant_tile<MODE, BITS>(p, t.u, t.h, t.t, t.q, sh_mean, shw, &sh_flag, sh_tab, sh_tally);
   }
 }
 
@@ -487,9 +499,18 @@ __global__ void overlap_zero_kernel(unsigned* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_bytes, unsigned long long* choice,
-                       unsigned* err_word, hipStream_t s) {
-  if (p.H <= 0 || p.nc <= 0 || p.L <= 0) return 1;
+template <int BITS>
+static void launch_overlap(const OverlapParams& p, int mode, unsigned grid, hipStream_t s) {
+  switch (mode) {
+    case kModeFixed6: kv_overlap_kernel<kModeFixed6, BITS><<<grid, kOvThreads, 0, s>>>(p); break;
+    case kModeFixed4: kv_overlap_kernel<kModeFixed4, BITS><<<grid, kOvThreads, 0, s>>>(p); break;
+    default: kv_overlap_kernel<kMode4over6, BITS><<<grid, kOvThreads, 0, s>>>(p); break;
+  }
+}
+
+int overlap_try_launch(OverlapParams p, int mode, int bits, void* workspace, size_t ws_bytes,
+                       unsigned long long* choice, unsigned* err_word, hipStream_t s) {
+  if (p.H <= 0 || p.nc <= 0 || p.L <= 0 || (bits != 4 && bits != 3 && bits != 2)) return 1;
   p.nst = (p.L + kOvStatsRows - 1) / kOvStatsRows;
   p.nqt = (p.L + kOvQuantRows - 1) / kOvQuantRows;
   const int U = 2 * p.nc;
@@ -516,11 +537,12 @@ int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_byt
   p.spin_limit = kOvSpinLimit;
   overlap_zero_kernel<<<(l.n_zero_words + 255) / 256, 256, 0, s>>>(reinterpret_cast<unsigned*>(ws + l.ready),
                                                                   l.n_zero_words);
-  switch (mode) {
-    case kModeFixed6: kv_overlap_kernel<kModeFixed6><<<(unsigned)grid, kOvThreads, 0, s>>>(p); break;
-    case kModeFixed4: kv_overlap_kernel<kModeFixed4><<<(unsigned)grid, kOvThreads, 0, s>>>(p); break;
-    default: kv_overlap_kernel<kMode4over6><<<(unsigned)grid, kOvThreads, 0, s>>>(p); break;
-  }
+  if (bits == 3)
+    launch_overlap<3>(p, mode, (unsigned)grid, s);
+  else if (bits == 2)
+    launch_overlap<2>(p, mode, (unsigned)grid, s);
+  else
+    launch_overlap<4>(p, mode, (unsigned)grid, s);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   if (choice) {
     launch_choice_reduce(p.tally, (size_t)U * p.H * p.nqt, choice, s);

@@ -53,7 +53,8 @@ constexpr size_t kKvWorkspaceHeader = 256;
 // NVFP4_ERR_HIP.
 // err_word: where a timed-out wait is recorded besides this call's own word
 // (never cleared here).
-int overlap_try_launch(OverlapParams p, int mode, void* workspace, size_t ws_bytes, unsigned long long* choice,
-                       unsigned* err_word, hipStream_t s);
+// bits: 4 (NVFP4), or 3 / 2 for the low-bit cache (lowbit_device.hpp).
+int overlap_try_launch(OverlapParams p, int mode, int bits, void* workspace, size_t ws_bytes,
+                       unsigned long long* choice, unsigned* err_word, hipStream_t s);
 
 }  // namespace nvfp4

@@ -490,7 +490,7 @@ int kv_quantize_launch(const uint16_t* k, const uint16_t* v, int H, int T, int D
     q.tscale[0] = k_tensor_scale; q.tscale[1] = v_tensor_scale;
     q.kmean = k_mean;
     q.H = H; q.T = T; q.L = chunk_len; q.nc = g.nc;
-    const int rc = overlap_try_launch(q, mode, workspace, workspace_bytes, choice_counts, err_word, s);
+    const int rc = overlap_try_launch(q, mode, 4, workspace, workspace_bytes, choice_counts, err_word, s);
     if (rc <= 0) return rc;  // enqueued, or a launch error
   }
   KVParams p;

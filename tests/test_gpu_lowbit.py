@@ -3,7 +3,8 @@
 scales, tensor scales, choice counts and dequantized values bit for bit (the
 oracle fed the GPU's K mean, which must meet the 1e-6 rule), on the seeded
 workloads, a full cache layer (sampled chunks), ragged shapes and degenerate
-values."""
+values, in both kernel forms (the overlapped kernel for D = 128, the
+two-pass kernels for every D)."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +17,7 @@ from gpu_helpers import mean_rule, say, to_np
 pytestmark = pytest.mark.gpu
 
 SENTINEL = 0x5A
+PATHS = [{}, {"two_pass": True}]  # keyword options of the binding
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,47 +55,53 @@ def _check(kb, vb, L, bits, mode, out, dk=None, dv=None):
     return ref
 
 
-def _run(kb, vb, L, bits, mode=O.MODE_4OVER6):
+def _run(kb, vb, L, bits, mode=O.MODE_4OVER6, path=None):
     H, T, D = kb.shape
     k, v = W.from_bits(kb, "cuda"), W.from_bits(vb, "cuda")
     ws = torch.full((P.nvfp4_kv_workspace_bytes(H, T, D, L),), 0xA5, dtype=torch.uint8, device="cuda")
-    out = P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, mode, out=_outputs(H, T, D, L, bits), workspace=ws)
+    ws[:4] = 0  # the sticky error word is the caller's to clear
+    out = P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, mode, out=_outputs(H, T, D, L, bits), workspace=ws,
+                                            **(path or {}))
     dk = torch.full((H, T, D), -777.0, dtype=torch.bfloat16, device="cuda")
     dv = torch.full((H, T, D), -777.0, dtype=torch.bfloat16, device="cuda")
     P.nvfp4_dequantize_lowbit(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], L, bits, out=dk)
     P.nvfp4_dequantize_lowbit(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, L, bits, out=dv)
     torch.cuda.synchronize()
+    assert P.kv_error_word(ws) == 0  # no bounded wait timed out
     return _check(kb, vb, L, bits, mode, out, dk, dv)
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["overlap", "two-pass"])
 @pytest.mark.parametrize("bits", [3, 2])
 @pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
-def test_tiny_workload(bits, mode):
-    say("lowbit tiny", bits, mode)
+def test_tiny_workload(bits, mode, path):
+    say("lowbit tiny", bits, mode, path)
     k, v = W.gaussian_kv(W.TINY, W.SEED_TINY)
-    _run(W.bf16_bits(k), W.bf16_bits(v), W.TINY.chunk_len, bits, mode)
+    _run(W.bf16_bits(k), W.bf16_bits(v), W.TINY.chunk_len, bits, mode, path)
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["overlap", "two-pass"])
 @pytest.mark.parametrize("bits", [3, 2])
-def test_one_chunk_and_heavy_tail(bits):
+def test_one_chunk_and_heavy_tail(bits, path):
     s = W.ONE_CHUNK
     for name, gen, seed in (("one chunk", W.gaussian_kv, W.SEED_ONE_CHUNK), ("heavy tail", W.heavy_tail_kv, W.SEED_HEAVY)):
-        say("lowbit", name, s, "bits", bits)
+        say("lowbit", name, s, "bits", bits, path)
         k, v = gen(s, seed)
-        ref = _run(W.bf16_bits(k), W.bf16_bits(v), s.chunk_len, bits)
+        ref = _run(W.bf16_bits(k), W.bf16_bits(v), s.chunk_len, bits, O.MODE_4OVER6, path)
         n = k.numel() // 16
         assert 0 < ref["k_useb"] < n and 0 < ref["v_useb"] < n  # both candidates are chosen somewhere
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["overlap", "two-pass"])
 @pytest.mark.parametrize("bits", [3, 2])
-def test_full_cache_layer_sampled(bits):
+def test_full_cache_layer_sampled(bits, path):
     """One layer of the 8-chunk cache ([24, 56320, 128]): chunks 0, 3 and 7
     against the oracle bit for bit, the whole layer by its choice counts."""
     s = W.CACHE_LAYER
     L = s.chunk_len
-    say("lowbit full layer", s, "bits", bits)
+    say("lowbit full layer", s, "bits", bits, path)
     k, v = W.gaussian_kv(s, W.cache_layer_seed(2), device="cuda")
-    out = P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, out=_outputs(s.H, s.T, s.D, L, bits))
+    out = P.nvfp4_kv_smooth_quantize_lowbit(k, v, L, bits, out=_outputs(s.H, s.T, s.D, L, bits), **path)
     dk = P.nvfp4_dequantize_lowbit(out["k_codes"], out["k_scales"], out["k_tensor_scale"], out["k_mean"], L, bits)
     dv = P.nvfp4_dequantize_lowbit(out["v_codes"], out["v_scales"], out["v_tensor_scale"], None, L, bits)
     torch.cuda.synchronize()
@@ -108,6 +116,7 @@ def test_full_cache_layer_sampled(bits):
     assert cc.sum(1).tolist() == [k.numel() // 16] * 2
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["overlap", "two-pass"])
 @pytest.mark.parametrize("bits", [3, 2])
 @pytest.mark.parametrize("H,T,D,L", [
     (3, 77, 128, 7),        # 11 chunks of 7 rows
@@ -116,14 +125,15 @@ def test_full_cache_layer_sampled(bits):
     (2, 7, 32, 1),          # one token per chunk: K' = 0
     (24, 1000, 128, 100),   # ragged tiles
 ])
-def test_ragged_shapes(bits, H, T, D, L):
-    say("lowbit shape", (H, T, D, L), "bits", bits)
+def test_ragged_shapes(bits, H, T, D, L, path):
+    say("lowbit shape", (H, T, D, L), "bits", bits, path)
     k, v = W.gaussian_kv(W.KVShape(H, T, D, L), 777 + H * T + D)
-    _run(W.bf16_bits(k), W.bf16_bits(v), L, bits)
+    _run(W.bf16_bits(k), W.bf16_bits(v), L, bits, O.MODE_4OVER6, path)
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["overlap", "two-pass"])
 @pytest.mark.parametrize("bits", [3, 2])
-def test_degenerate_values(bits):
+def test_degenerate_values(bits, path):
     rng = np.random.default_rng(88)
     H, T, D, L = 2, 64, 128, 32
     cases = {
@@ -135,7 +145,7 @@ def test_degenerate_values(bits):
         "tiny": (rng.standard_normal((H, T, D)) * 1e-20, rng.standard_normal((H, T, D)) * 1e-30),
     }
     for name, (k, v) in cases.items():
-        say("lowbit degenerate", name, "bits", bits)
+        say("lowbit degenerate", name, "bits", bits, path)
         kb = W.bf16_bits(torch.as_tensor(np.asarray(k, np.float32)).to(torch.bfloat16))
         vb = W.bf16_bits(torch.as_tensor(np.asarray(v, np.float32)).to(torch.bfloat16))
-        _run(kb, vb, L, bits)
+        _run(kb, vb, L, bits, O.MODE_4OVER6, path)
