@@ -60,7 +60,8 @@ VALU_FILE = os.path.join(ROOT, "profiles", "kv_valu_full_cache.md")
 # the sources the KV quantize call's kernels are built from
 KV_KERNEL_SOURCES = ("precision_kv_cache_amd/csrc/kv_quant.hip", "precision_kv_cache_amd/csrc/kv_overlap.hip",
                      "precision_kv_cache_amd/csrc/kv_overlap.hpp", "precision_kv_cache_amd/csrc/nvfp4_device.hpp",
-                     "precision_kv_cache_amd/csrc/host_common.hpp", "include/nvfp4kv.h")
+                     "precision_kv_cache_amd/csrc/lowbit_device.hpp", "precision_kv_cache_amd/csrc/host_common.hpp",
+                     "include/nvfp4kv.h")
 
 
 def kernel_sources_sha256():
