@@ -6,8 +6,8 @@
 // unit's tensor scale needs its largest |K - mean| (or |V|) before any of its
 // blocks can be encoded, so each unit is read twice: once for its
 // statistics and once to encode it.  This kernel makes the second read come
-// from the Infinity Cache and hides the memory-bound statistics behind the
-// VALU-bound encoding:
+// mostly from the Infinity Cache and runs the statistics of later units
+// beside the encoding of earlier ones:
 //
 //   * one launch of ordinary (non-persistent) workgroups; the grid is a
 //     sequence of segments, segment s holding the statistics tiles of unit s

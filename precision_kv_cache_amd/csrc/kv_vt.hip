@@ -12,9 +12,9 @@
 // of one head, staged through LDS so that each lane reads one channel's
 // tokens, then the shared 4/6 block routine).  The grid is a sequence of
 // segments, segment s holding the statistics tiles of chunk s and then the
-// quantize tiles of chunk s - depth, so the second read comes from the
-// Infinity Cache and the memory-bound statistics run beside the VALU-bound
-// encoding.  A quantize tile waits only for statistics tiles of an earlier
+// quantize tiles of chunk s - depth, so the second read comes mostly from
+// the Infinity Cache and the statistics of later chunks run beside the
+// encoding of earlier ones.  A quantize tile waits only for statistics tiles of an earlier
 // segment (lower workgroup index), and statistics tiles never wait; with
 // in-order dispatch those are resident or finished whenever the quantize
 // tile runs, so the waits cannot cycle.  They are bounded all the same: on
