@@ -135,7 +135,7 @@ __global__ __launch_bounds__(512) void kv_lowbit_dequant_kernel(LowBitDeq p) {
   const int HB = 2 * p.NB;
   const int tid = threadIdx.x, hc = tid % HB, roff = tid / HB;
   if (roff >= p.RP) return;
-  const int h = blockIdx.y, c = blockIdx.z, half = hc & 1;
+  const int c = blockIdx.y, h = blockIdx.z, half = hc & 1;
   const float g = p.tscale[c];
   float m[8];
 #pragma unroll
@@ -312,7 +312,8 @@ extern "C" NVFP4KV_API int nvfp4_dequantize_lowbit(const uint8_t* codes, const u
   const int HB = 2 * p.NB;                // half-blocks per row, at most 512
   p.RP = HB >= 256 ? 1 : 256 / HB;        // rows per pass
   const unsigned threads = (unsigned)((HB * p.RP + 63) / 64 * 64);
-  const dim3 grid((unsigned)((chunk_len + p.RP * kLbDeqRows - 1) / (p.RP * kLbDeqRows)), (unsigned)H, (unsigned)nc);
+  // chunks before heads in the dispatch order (one contiguous front per head)
+  const dim3 grid((unsigned)((chunk_len + p.RP * kLbDeqRows - 1) / (p.RP * kLbDeqRows)), (unsigned)nc, (unsigned)H);
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   if (bits == 3) {

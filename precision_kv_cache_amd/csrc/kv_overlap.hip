@@ -2,12 +2,13 @@
 // smoothing + NVFP4 4/6 quantization (LongLive-2.0 summary page: inference
 // pipeline, step 7; full-stack NVFP4), for head dimension 128.
 //
-// A unit is one (chunk, tensor): u = 2 * chunk + tensor, K before V.  A
-// unit's tensor scale needs its largest |K - mean| (or |V|) before any of its
-// blocks can be encoded, so each unit is read twice: once for its
-// statistics and once to encode it.  This kernel makes the second read come
-// mostly from the Infinity Cache and runs the statistics of later units
-// beside the encoding of earlier ones:
+// A unit is one (chunk, tensor): u = tensor * n_chunks + chunk, every K
+// chunk before the first V chunk (the resident workgroups then cover fewer
+// separate regions of memory at a time).  A unit's tensor scale needs its
+// largest |K - mean| (or |V|) before any of its blocks can be encoded, so
+// each unit is read twice: once for its statistics and once to encode it.
+// This kernel makes the second read come mostly from the Infinity Cache and
+// runs the statistics of later units beside the encoding of earlier ones:
 //
 //   * one launch of ordinary (non-persistent) workgroups; the grid is a
 //     sequence of segments, segment s holding the statistics tiles of unit s
@@ -194,7 +195,7 @@ __device__ __forceinline__ void v_stats_batch(const uint4 (&a)[kSBatch], int r, 
 template <int MODE, int BITS>
 __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double* shs, uint32_t* shx, float* shw,
                            unsigned* sh_flag) {
-  const int c = u >> 1, tau = u & 1;
+  const int c = u % p.nc, tau = u / p.nc;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int hc = tid % kHalves, roff = tid / kHalves;
   const int r0 = ts * kOvStatsRows;
@@ -386,7 +387,7 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
 template <int MODE, int BITS>
 __device__ void quant_tile(const OverlapParams& p, int u, int h, int qt, unsigned qidx, float* sh_mean,
                            float* shw, unsigned* sh_flag, const float2* tab, unsigned* sh_tally) {
-  const int c = u >> 1, tau = u & 1;
+  const int c = u % p.nc, tau = u / p.nc;
   const int tid = threadIdx.x;
   if (tid == 0) {
     const unsigned long long* rw =

@@ -372,7 +372,7 @@ template <bool MEAN, int HBC>
 __global__ __launch_bounds__(512) void dequant_kernel(DeqParams p) {
   const int HB = HBC > 0 ? HBC : p.HB;
   const int RP = HBC > 0 ? kMaxThreads / HBC : p.RP;
-  const int qt = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
+  const int qt = blockIdx.x, c = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, hc = tid % HB, roff = tid / HB;
   if (roff >= RP) return;
   float m[8];
@@ -586,7 +586,10 @@ extern "C" NVFP4KV_API int nvfp4_dequantize(const uint8_t* codes, const uint8_t*
   p.H = H; p.T = T; p.D = D; p.L = chunk_len; p.HB = dg.HB; p.RP = dg.RP; p.rows_q = dg.rows_q;
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  const dim3 grid(dg.nqt, H, g.nc);
+  // chunks before heads in the dispatch order: the resident workgroups then
+  // sweep one head's rows (all its chunks, contiguous) as a single front
+  // instead of touching one region per (chunk, head) at once
+  const dim3 grid(dg.nqt, g.nc, H);
   if (D == 128) {
     if (mean) dequant_kernel<true, 16><<<grid, dg.threads, 0, s>>>(p);
     else dequant_kernel<false, 16><<<grid, dg.threads, 0, s>>>(p);
