@@ -123,7 +123,7 @@ struct LowBitDeq {
 
 constexpr int kLbDeqRows = 4;  // rows per lane
 
-// One workgroup per (tile of RP * kLbDeqRows rows, head, chunk); lane (roff,
+// One workgroup per (tile of RP * kLbDeqRows rows, chunk, head); lane (roff,
 // hc) decodes half-block hc (8 channels: block hc / 2, half hc % 2) of rows
 // roff, roff + RP, ... (RP = 256 / (2 NB) rows per pass).  So its chunk's
 // means are loaded once, and each wave-wide store writes one contiguous run

@@ -342,7 +342,7 @@ void launch_kv_stats(const KVParams& p, unsigned n_workgroups, int threads, hipS
 // RP rows apart; it issues all of their code and scale loads before the
 // first store, so each lane keeps kDeqRows loads in flight.  The bf16 output
 // is streamed out with non-temporal stores: nothing here reads it again.
-constexpr int kDeqRows = 4;
+constexpr int kDeqRows = 2;
 
 struct DeqParams {
   const uint8_t* codes;
