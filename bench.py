@@ -111,8 +111,10 @@ METRIC = "NVFP4 4/6 KV quantize GB/s (bytes in+out) and % of MI355X HBM peak"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 calls for --op act / weight, which take ~0.05 ms each)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 3; 100 calls for --op act / weight, so the clocks settle)")
     ap.add_argument("--layers", type=int, default=30, help="cache layers (the workload has 30)")
     ap.add_argument("--mode", type=int, default=0, help="0 = 4/6, 1 = fixed 6, 2 = fixed 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -148,6 +150,11 @@ def kv_bytes(H, T, D, L, with_mean, bits=4):
 
 def main():
     a = parse()
+    short = a.op in ("act", "weight")  # calls of a few tens of microseconds
+    if a.steps is None:
+        a.steps = 200 if short else 20
+    if a.warmup is None:
+        a.warmup = 100 if short else 3
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this path runs on a single MI355X "
@@ -450,7 +457,7 @@ def kv_bench(a, bits):
     print(json.dumps(result), flush=True)
 
 
-def act_weight_timing(P, W, mode, stream, reps=20):
+def act_weight_timing(P, W, mode, stream, reps=200, warm=100):
     """The GEMM-operand quantizers on their workload: activation [16384, 3072]
     with the 16-point RHT and 1D blocks, weight [3072, 3072] with 16x16
     tiles.  Several input copies are rotated (at least 400 MB in all) so no
@@ -478,7 +485,7 @@ def act_weight_timing(P, W, mode, stream, reps=20):
             ("weight_quantize_2d", lambda i: P.nvfp4_quantize_2d(wsz[i % len(wsz)], mode, out=wo, workspace=wws,
                                                                  stream=stream),
              2 * w.numel() + w.numel() // 2 + w.numel() // 256 + 4)):
-        for i in range(3):
+        for i in range(warm):  # calls of tens of microseconds: let the clocks settle first
             fn(i)
         e0, e1 = E(), E()
         torch.cuda.synchronize()

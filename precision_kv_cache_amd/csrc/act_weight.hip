@@ -132,16 +132,17 @@ __global__ __launch_bounds__(kAWThreads) void quant1d_kernel(const uint16_t* x, 
   sign_factors(sign_mask, sgn);
   for (long long f = blockIdx.x * (long long)blockDim.x + threadIdx.x; f < nblk;
        f += (long long)gridDim.x * blockDim.x) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + f * 16);
-    const uint4 a = src[0], b = src[1];
+    // the block's last read (the amax pass left it in the Infinity Cache)
+    // and its codes are streamed: non-temporal loads and stores
+    const uint4 a = load_nt(x + f * 16), b = load_nt(x + f * 16 + 8);
     float z[16];
     unpack16(a, b, z);
     if (RHT) rht16_unscaled(z, sgn);
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = z[i] * gz;
     const Block46 q = quant_block16<MODE>(z, sh_tab);
-    *reinterpret_cast<uint2*>(codes + f * 8) = make_uint2(q.lo, q.hi);
-    scales[f] = (uint8_t)q.scale;
+    store_nt(codes + f * 8, q.lo, q.hi);
+    store_nt(scales + f, (uint8_t)q.scale);
   }
 }
 
@@ -304,7 +305,7 @@ extern "C" NVFP4KV_API int nvfp4_quantize_1d(const uint16_t* x, int rows, int co
   const long long nblk = (long long)(n / 16);
   (void)hipGetLastError();
   const int np = launch_amax(x, nblk, hadamard != 0, sign_mask, workspace, s);
-  const unsigned gq = grid_for(nblk, 2);
+  const unsigned gq = grid_for(nblk, 8);  // eight blocks per lane: fewer workgroups re-reducing the partials
 #define NVFP4_Q1D(MODE)                                                                                      \
   (hadamard ? quant1d_kernel<MODE, true><<<gq, kAWThreads, 0, s>>>(x, nblk, sign_mask, partial, np, codes,   \
                                                                    scales, tensor_scale)                     \
