@@ -239,8 +239,9 @@ NVFP4KV_API int nvfp4_quantize_2d(const uint16_t* w, int rows, int cols, int mod
 
 /*
  * Dequantize a weight quantized with 2D tiles (the inverse of
- * nvfp4_quantize_2d; training pipeline, step 4: weights carry one block
- * scale per 16x16 tile).  Every element of tile (r / 16, c / 16) decodes as
+ * nvfp4_quantize_2d; LongLive-2.0 summary page, training pipeline, step 4,
+ * and its full-stack NVFP4 section: weights carry one block scale per 16x16
+ * tile).  Every element of tile (r / 16, c / 16) decodes as
  * bf16((v * S_tile) * g_dec), each step one fp32 rounding.
  *
  *   codes         uint8 [rows, cols/2] (8-byte aligned), low nibble = even column.
