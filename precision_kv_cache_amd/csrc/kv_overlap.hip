@@ -430,12 +430,19 @@ __device__ void quant_tile(const OverlapParams& p, int u, int h, int qt, unsigne
   const int r1 = min(r0 + kOvQuantRows, p.L);
   const size_t row0 = (size_t)h * p.T + (size_t)c * p.L;
   uint2 n;
-  if constexpr (BITS == 4)
-    n = tau == 0 ? quant_rows<MODE, true, true, kQBatch, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
-                                                             kQRowsPerPass, kNB, col, m, g, tab)
-                 : quant_rows<MODE, false, true, kQBatch, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff,
-                                                              r1, kQRowsPerPass, kNB, col, m, g, tab);
-  else
+  constexpr int kRows = kOvQuantRows / kQRowsPerPass;  // rows per lane in a full tile
+  if constexpr (BITS == 4) {
+    if (p.ahead && r1 - r0 == kOvQuantRows)
+      n = tau == 0 ? quant_rows_ahead<MODE, true, kRows, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff,
+                                                              kQRowsPerPass, col, m, g, tab)
+                   : quant_rows_ahead<MODE, false, kRows, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff,
+                                                               kQRowsPerPass, col, m, g, tab);
+    else
+      n = tau == 0 ? quant_rows<MODE, true, true, kQBatch, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff,
+                                                               r1, kQRowsPerPass, kNB, col, m, g, tab)
+                   : quant_rows<MODE, false, true, kQBatch, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff,
+                                                                r1, kQRowsPerPass, kNB, col, m, g, tab);
+  } else
     n = tau == 0 ? lowbit_quant_rows<BITS, MODE, true, kNB>(p.x[0], p.codes[0], p.scales[0], row0, r0 + roff, r1,
                                                            kQRowsPerPass, kNB, col, m, g, tab)
                  : lowbit_quant_rows<BITS, MODE, false, kNB>(p.x[1], p.codes[1], p.scales[1], row0, r0 + roff, r1,
@@ -535,6 +542,7 @@ int overlap_try_launch(OverlapParams p, int mode, int bits, void* workspace, siz
   p.err_sticky = err_word;
   p.choice = choice != nullptr;
   p.depth = kOvDepth;
+  p.ahead = U <= kOvAheadUnits ? 1 : 0;
   p.spin_limit = kOvSpinLimit;
   overlap_zero_kernel<<<(l.n_zero_words + 255) / 256, 256, 0, s>>>(reinterpret_cast<unsigned*>(ws + l.ready),
                                                                   l.n_zero_words);

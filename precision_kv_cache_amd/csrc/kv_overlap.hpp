@@ -12,6 +12,11 @@ constexpr int kOvThreads = 256;
 constexpr int kOvStatsRows = 512;    // rows per statistics tile
 constexpr int kOvQuantRows = 256;    // rows per quantize tile
 constexpr int kOvDepth = 3;          // segments between a unit's statistics and its quantization
+// Calls of at most this many (chunk, tensor) units quantize with each row's
+// loads issued one row ahead: they have about one round of quantize tiles,
+// so no other workgroup hides a tile's load latency.  Larger calls keep
+// fewer live registers instead.
+constexpr int kOvAheadUnits = 4;
 constexpr int kOvReplicas = 32;      // copies of each unit's ready word
 constexpr unsigned kOvSpinLimit = 1u << 22;  // polls before a wait gives up
 
@@ -34,6 +39,7 @@ struct OverlapParams {
                              // caller's word for the call that has no workspace)
   uint32_t* tally;           // [U * nq][4] per-quantize-tile 4/6 choice counts (when choice)
   int choice;
+  int ahead;  // quantize tiles load each row one row ahead (calls of few units, see kOvAheadUnits)
   int H, T, L, nc, nst, nqt, depth;
   unsigned spin_limit;
 };

@@ -260,6 +260,47 @@ __device__ __forceinline__ uint2 quant_rows(const uint16_t* xb, uint8_t* codes, 
   return make_uint2(n4, nblk);
 }
 
+// Full-tile form of quant_rows with the loads one row ahead: exactly ROWS
+// rows per lane (r, r + step, ..., r + (ROWS - 1) step), and row q + 1's
+// loads are issued before row q is encoded, so they are in flight during
+// that encode.  Same arguments (NB fixed, no bound: every row exists) and
+// result as quant_rows.
+template <int MODE, bool SMOOTH, int ROWS, int NB>
+__device__ __forceinline__ uint2 quant_rows_ahead(const uint16_t* xb, uint8_t* codes, uint8_t* scales, size_t row0,
+                                                  int r, int step, int col, const float (&m)[16], float g,
+                                                  const float2* tab) {
+  const size_t blk = (row0 + r) * NB + col;
+  const uint16_t* px = xb + blk * 16;
+  uint8_t* pc = codes + blk * 8;
+  uint8_t* ps = scales + blk;
+  const size_t dq = (size_t)step * NB;  // blocks from one of the lane's rows to the next
+  uint4 a[ROWS], b[ROWS];
+  a[0] = load_nt(px);
+  b[0] = load_nt(px + 8);
+  unsigned n4 = 0;
+#pragma unroll
+  for (int q = 0; q < ROWS; ++q) {
+    if (q + 1 < ROWS) {
+      a[q + 1] = load_nt(px + (q + 1) * dq * 16);
+      b[q + 1] = load_nt(px + (q + 1) * dq * 16 + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the next row's loads go out before this row's arithmetic
+    float z[16];
+    unpack16(a[q], b[q], z);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float xs = SMOOTH ? z[i] - m[i] : z[i];  // k' = fl(K - m)
+      z[i] = xs * g;                                  // z = fl(k' * g_enc)
+    }
+    const Block46 qb = quant_block16<MODE>(z, tab);
+    store_nt(pc + q * dq * 8, qb.lo, qb.hi);
+    store_nt(ps + q * dq, (uint8_t)qb.scale);
+    n4 += qb.use4;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return make_uint2(n4, (unsigned)ROWS);
+}
+
 // Hand-off of small results between workgroups of one kernel.
 //
 // On this multi-XCD part every XCD has its own L2, and an agent-scope
