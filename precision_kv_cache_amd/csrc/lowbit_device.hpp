@@ -30,36 +30,63 @@ __host__ __device__ constexpr float lowbit_constant(int mode) {
 }
 
 // One candidate on a block z (encode domain) with scale S and reciprocal R:
-// the packed codes (lo: bits 0..31, hi: bits 32..47) and the fp32 error.
+// the packed magnitude fields of the codes (lo: bits 0..31, hi: bits
+// 32..47; the sign bits are the block's, see lowbit_signs) and the fp32
+// error.
+//
+// The magnitude index k (nearest grid point to |y|, y = fl(z R), ties to
+// the even index, saturated at the top) comes from one fp32 rounding:
+// 2|y| + 2^23 (3 bits) or |y| + 2^23 (2 bits) rounds to nearest even at a
+// spacing of 1, i.e. to 2^23 + rint(2|y|) (or 2^23 + rint(|y|)), so after
+// the clamp to 2^23 + top, k sits in the low bits of the sum and the
+// magnitude value (k / 2, or k) is the sum minus 2^23, exactly.  The error
+// needs no sign: y has z's sign (R >= 0) and v S is exact, so
+// |fl(z - sign(z) v S)| = fl(|z| - v S) and the squares agree.
 template <int BITS>
 __device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S, float R, uint32_t& lo,
                                                   uint32_t& hi) {
+  constexpr float kMagic = 8388608.0f;  // 2^23
+  constexpr float kTop = BITS == 3 ? 3.0f : 1.0f;
+  constexpr uint32_t kMask = BITS == 3 ? 3u : 1u;
   float elo = 0.0f, ehi = 0.0f;
   lo = 0u;
   hi = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float y = z[i] * R;
-    const float a = fabsf(y);
-    float k;  // magnitude index, as a float
-    if (BITS == 3)
-      k = fminf(__builtin_rintf(a * 2.0f), 3.0f);  // rint: nearest, ties to even
-    else
-      k = a > 0.5f ? 1.0f : 0.0f;                 // the tie 0.5 goes to the even code 0
-    const float v = BITS == 3 ? k * 0.5f : k;      // magnitude value, exact
-    const uint32_t neg = __float_as_uint(y) >> 31;
-    const float vs = __uint_as_float(__float_as_uint(v) | (neg << 31));  // signed value (-0 kept)
-    const float e = __builtin_fmaf(-vs, S, z[i]);  // v * S is exact: fl(z - v S)
+    const float t = fminf(BITS == 3 ? __builtin_fmaf(fabsf(y), 2.0f, kMagic) : fabsf(y) + kMagic, kMagic + kTop);
+    const float v = BITS == 3 ? __builtin_fmaf(t, 0.5f, -0.5f * kMagic) : t - kMagic;  // k / 2 or k, exact
+    const float e = __builtin_fmaf(-v, S, fabsf(z[i]));
     if (i < 8)
       elo = __builtin_fmaf(e, e, elo);
     else
       ehi = __builtin_fmaf(e, e, ehi);
-    const uint32_t code = (uint32_t)k | (neg << (BITS - 1));
-    const int pos = BITS * i;
-    if (pos < 32) lo |= code << pos;
-    if (pos + BITS > 32) hi |= code >> (32 - pos > 0 ? 32 - pos : 0) << (pos > 32 ? pos - 32 : 0);
+    const uint32_t k = __float_as_uint(t) & kMask;
+    const int pos = BITS * i;  // the magnitude field: bits pos .. pos + BITS - 2 (never across bit 32)
+    if (pos < 32)
+      lo |= k << pos;
+    else
+      hi |= k << (pos - 32);
   }
   return elo + ehi;
+}
+
+// The sign bits of a block's codes (bit BITS i + BITS - 1 = sign bit of
+// z_i, which is y_i's for every candidate; -0 keeps its sign), split like
+// the codes into lo (bits 0..31) and hi (bits 32..47).
+template <int BITS>
+__device__ __forceinline__ void lowbit_signs(const float (&z)[16], uint32_t& lo, uint32_t& hi) {
+  lo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t sb = __float_as_uint(z[i]) >> 31;
+    const int pos = BITS * i + BITS - 1;
+    if (pos < 32)
+      lo |= sb << pos;
+    else
+      hi |= sb << (pos - 32);
+  }
 }
 
 struct LowBitBlock {
@@ -75,6 +102,8 @@ __device__ __forceinline__ LowBitBlock lowbit_block16(const float (&z)[16], cons
   const float rb = LowBit<BITS>::cb == 1.0f ? t : t / LowBit<BITS>::cb;
   const uint32_t s = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rb, __float_as_int(t), false) & 0xffffu;
   LowBitBlock out;
+  uint32_t slo, shi;
+  lowbit_signs<BITS>(z, slo, shi);
   if (MODE == kModeFixed6) {
     const float2 c = tab[s & 0xffu];
     (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
@@ -96,6 +125,8 @@ __device__ __forceinline__ LowBitBlock lowbit_block16(const float (&z)[16], cons
     out.scale = useb ? (s >> 8) : (s & 0xffu);
     out.useb = useb ? 1u : 0u;
   }
+  out.lo |= slo;
+  out.hi |= shi;
   return out;
 }
 
