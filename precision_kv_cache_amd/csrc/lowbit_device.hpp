@@ -29,6 +29,19 @@ __host__ __device__ constexpr float lowbit_constant(int mode) {
                                                                                                     : LowBit<BITS>::cb));
 }
 
+// The sum, modulo 2^32, of 0x4B000000 << pos over the elements whose
+// magnitude field lies in the low (hi = false) or high code word.
+template <int BITS>
+__host__ __device__ constexpr uint32_t lowbit_pack_bias(bool hi) {
+  uint32_t b = 0u;
+  for (int i = 0; i < 16; ++i) {
+    const int pos = BITS * i;
+    if (!hi && pos < 32) b += 0x4B000000u << pos;
+    if (hi && pos >= 32) b += 0x4B000000u << (pos - 32);
+  }
+  return b;
+}
+
 // One candidate on a block z (encode domain) with scale S and reciprocal R:
 // the packed magnitude fields of the codes (lo: bits 0..31, hi: bits
 // 32..47; the sign bits are the block's, see lowbit_signs) and the fp32
@@ -47,7 +60,6 @@ __device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S,
                                                   uint32_t& hi) {
   constexpr float kMagic = 8388608.0f;  // 2^23
   constexpr float kTop = BITS == 3 ? 3.0f : 1.0f;
-  constexpr uint32_t kMask = BITS == 3 ? 3u : 1u;
   float elo = 0.0f, ehi = 0.0f;
   lo = 0u;
   hi = 0u;
@@ -61,13 +73,17 @@ __device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S,
       elo = __builtin_fmaf(e, e, elo);
     else
       ehi = __builtin_fmaf(e, e, ehi);
-    const uint32_t k = __float_as_uint(t) & kMask;
+    // t's bits are 0x4B000000 + k (no carry: k <= top): the fields are added
+    // with t's bits shifted in whole, and the shifted constant parts are
+    // taken out once below
     const int pos = BITS * i;  // the magnitude field: bits pos .. pos + BITS - 2 (never across bit 32)
     if (pos < 32)
-      lo |= k << pos;
+      lo += __float_as_uint(t) << pos;
     else
-      hi |= k << (pos - 32);
+      hi += __float_as_uint(t) << (pos - 32);
   }
+  lo -= lowbit_pack_bias<BITS>(false);
+  hi -= lowbit_pack_bias<BITS>(true);
   return elo + ehi;
 }
 
