@@ -133,6 +133,10 @@ def parse():
                          "weight: the weight quantizer (2D tiles)")
     ap.add_argument("--layout", choices=("all", "sink"), default="all",
                     help="attention key set: every cache key, or the sink layout (global sink, shot sink, window)")
+    ap.add_argument("--attention-form", choices=("staged", "on-load"), default=None,
+                    help="attention and stream: decode each key tile once per call into the workspace (staged, "
+                         "the default; with key splits), or in every query block (on-load; --op stream then runs "
+                         "its attention unsplit, without a workspace)")
     return ap.parse_args()
 
 
@@ -676,8 +680,12 @@ def attention_bench(a):
     nk = sum(n for _, n in ranges)
     out = torch.empty_like(q)
     # workspace that lets the call split each query block's keys over several
-    # workgroups (and merge them) where that fills the CUs better
-    aws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(H, Tq, D), dtype=torch.uint8, device=dev)
+    # workgroups (and merge them) where that fills the CUs better and, for the
+    # staged form, holds every key tile decoded once per call
+    staged = a.attention_form in (None, "staged")
+    nws = (P.nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, H, T, L, ranges) if staged
+           else P.nvfp4_kv_attention_workspace_bytes(H, Tq, D))
+    aws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for _ in range(a.warmup):
         P.nvfp4_kv_attention(q, cache, L, ranges, out=out, workspace=aws, stream=stream)
@@ -714,14 +722,15 @@ def attention_bench(a):
         "config": {
             "workload": f"attention of one chunk of queries [24 heads, 7040, 128] over one layer's NVFP4 cache "
                         f"({'all 56320 keys' if a.layout == 'all' else 'sink layout'}, chunks of 7040), "
-                        f"dequantized on load",
+                        + ("each key tile decoded once per call" if staged else "dequantized on load"),
+            "form": "staged" if staged else "on-load", "workspace_bytes": nws,
             "heads": H, "queries": Tq, "keys": nk, "head_dim": D, "chunk_len": L, "key_ranges": ranges,
         },
         "pct_of_mfma_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
         "cache_bytes_read": cache_bytes,
         "roofline": {
             "bound": "mfma",
-            "kernel": "nvfp4_kv_attention (one call)",
+            "kernel": "nvfp4_kv_attention (one call" + (": staging and attention kernels)" if staged else ")"),
             "achieved": round(call_tflops, 1),
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -777,6 +786,11 @@ def stream_bench(a):
     ranges = cache.key_ranges()
     nk = sum(n for _, n in ranges)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    att_staged = a.attention_form in (None, "staged")
+    aws = False
+    if att_staged:
+        aws = torch.empty(P.nvfp4_kv_attention_staged_workspace_bytes(H, L, D, H, cap * L, L, ranges),
+                          dtype=torch.uint8, device=dev)
 
     def step(att_ev=None, app_ev=None):
         cache.begin_chunk()
@@ -784,10 +798,10 @@ def stream_bench(a):
         for l in range(nl):
             if att_ev is not None:
                 att_ev[l][0].record(main)
-            # unsplit (no workspace): the appends on the side stream fill the CUs
-            # that attention's last round of workgroups leaves idle, which key
-            # splits would take from them (measured slower here)
-            cache.attention(l, q, out=out, workspace=False, stream=main)
+            # staged, with key splits (the workspace); the on-load form runs
+            # unsplit, since there the splits took from the appends on the side
+            # stream the CUs that attention's last round leaves idle
+            cache.attention(l, q, out=out, workspace=aws, stream=main)
             if att_ev is not None:
                 att_ev[l][1].record(main)
             done[l].record(main)  # the layer's K and V would come out of this layer's forward
@@ -854,6 +868,7 @@ def stream_bench(a):
                         f"chunks ({nk} keys), append of the chunk into an 8-slot cache",
             "layers": nl, "heads": H, "chunk_len": L, "frame_tokens": F, "keys": nk, "key_ranges": ranges,
             "slots": cap,
+            "attention_form": "staged, key splits" if att_staged else "on-load, unsplit",
         },
         "attention_call_ms": round(att_ms, 4),
         "append_call_ms_alone": round(app_alone_ms, 4),

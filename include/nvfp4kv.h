@@ -289,7 +289,13 @@ NVFP4KV_API int nvfp4_dequantize_2d(const uint8_t* codes, const uint8_t* scales,
  *                 small kernel then merges the partial results per query
  *                 row).  nvfp4_kv_attention_workspace_bytes() is enough for
  *                 every split; NULL or less than two splits' worth runs
- *                 unsplit.  Contents on entry ignored.
+ *                 unsplit.  A workspace of at least
+ *                 nvfp4_kv_attention_staged_workspace_bytes() for the same
+ *                 key list also holds the decoded image of every 64-key tile
+ *                 (35 KB per tile and cache head): the call then decodes each
+ *                 tile once, in a staging kernel, instead of once per query
+ *                 block, with bit-identical results.  Contents on entry
+ *                 ignored.
  *
  * Arithmetic: K is decoded to v * S, exact in bf16, so the logits are exact
  * up to fp32 accumulation (g_K, the softmax scale and the mean term
@@ -300,6 +306,16 @@ NVFP4KV_API int nvfp4_dequantize_2d(const uint8_t* codes, const uint8_t* scales,
  * and rounds out to bf16 once.
  */
 NVFP4KV_API size_t nvfp4_kv_attention_workspace_bytes(int H, int Tq, int D) NVFP4KV_NOEXCEPT;
+/*
+ * Workspace bytes for every key split plus the decoded tile images of the
+ * key list (key_ranges, n_ranges over a cache of H_kv heads, T tokens and
+ * chunk_len-token chunks; the same arguments nvfp4_kv_attention and
+ * nvfp4_kv_attention_chunked take).  0 for arguments those calls reject; for
+ * a key list of more than 65536 chunk pieces, which runs unstaged, just the
+ * split bytes.
+ */
+NVFP4KV_API size_t nvfp4_kv_attention_staged_workspace_bytes(int H, int Tq, int D, int H_kv, int T, int chunk_len,
+                                                             const int* key_ranges, int n_ranges) NVFP4KV_NOEXCEPT;
 NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,
                                    const uint8_t* k_scales, const float* k_tensor_scale, const float* k_mean,
                                    const uint8_t* v_codes, const uint8_t* v_scales, const float* v_tensor_scale,

@@ -17,7 +17,7 @@ __all__ = [
     "nvfp4_kv_workspace_bytes", "nvfp4_kv_error_word_offset", "nvfp4_kv_smooth_quantize", "nvfp4_kv_smooth_quantize_noalloc", "nvfp4_kv_smooth_quantize_lowbit",
     "nvfp4_dequantize_lowbit", "nvfp4_dequantize", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize_2d", "nvfp4_kv_attention", "nvfp4_kv_attention_chunked",
-    "nvfp4_kv_attention_workspace_bytes",
+    "nvfp4_kv_attention_workspace_bytes", "nvfp4_kv_attention_staged_workspace_bytes",
     "ATTN_MAX_RANGES", "KVCacheState", "KVCache", "nvfp4_gemm_w4a4", "nvfp4_kv_quantize_v_tblocks", "nvfp4_diag_e2m1_encode", "nvfp4_diag_candidates",
     "nvfp4_diag_reciprocal", "nvfp4_diag_bf16_round", "LIB_PATH",
 ]
@@ -58,6 +58,7 @@ def lib():
             "nvfp4_quantize_2d": (i, [P, i, i, i, P, P, P, P, sz, P]),
             "nvfp4_dequantize_2d": (i, [P, P, P, i, i, P, P]),
             "nvfp4_kv_attention_workspace_bytes": (sz, [i, i, i]),
+            "nvfp4_kv_attention_staged_workspace_bytes": (sz, [i, i, i, i, i, i, P, i]),
             "nvfp4_kv_attention": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P, P, sz,
                                        P]),
             "nvfp4_kv_attention_chunked": (i, [P, i, i, i, P, P, P, P, P, P, P, i, i, i, P, i, ctypes.c_float, P, P,
@@ -266,13 +267,30 @@ def nvfp4_kv_attention_workspace_bytes(H, Tq, D):
     return int(lib().nvfp4_kv_attention_workspace_bytes(H, Tq, D))
 
 
-def _attn_workspace(workspace, H, Tq, D, device):
+def _ranges_arr(key_ranges):
+    rg = [(int(a), int(n)) for a, n in key_ranges]
+    return rg, (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
+
+
+def nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, H_kv, T, chunk_len, key_ranges):
+    """Workspace bytes for every key split plus the decoded image of every
+    key tile of this key list (cache of H_kv heads, T tokens): with such a
+    workspace an attention call decodes each tile once (0 for invalid
+    arguments)."""
+    rg, arr = _ranges_arr(key_ranges)
+    return int(lib().nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, H_kv, T, chunk_len, arr, len(rg)))
+
+
+def _attn_workspace(workspace, H, Tq, D, device, keys=None):
     """workspace argument -> (tensor or None, bytes): None allocates one big
-    enough for every key split, False runs unsplit, a uint8 tensor is used."""
+    enough for every key split and, given keys = (H_kv, T, chunk_len,
+    key_ranges), for the staged form too; False runs unsplit and unstaged; a
+    uint8 tensor is used as it is."""
     if workspace is False:
         return None, 0
     if workspace is None:
-        n = nvfp4_kv_attention_workspace_bytes(H, Tq, D)
+        n = (nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, *keys) if keys is not None
+             else nvfp4_kv_attention_workspace_bytes(H, Tq, D))
         if n == 0:
             return None, 0
         workspace = torch.empty(n, dtype=torch.uint8, device=device)
@@ -297,9 +315,11 @@ def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=
     for H_kv heads with H % H_kv == 0.  softmax_scale defaults to 1/sqrt(D).
     Returns out (bf16 [H, Tq, D]), or (out, lse fp32 [H, Tq]) when lse is
     True or a preallocated fp32 [H, Tq] tensor (written in place).
-    workspace: None allocates one that allows key splits, False runs
-    unsplit, or a uint8 device tensor (at least
-    nvfp4_kv_attention_workspace_bytes for every split)."""
+    workspace: None allocates one that allows key splits and the staged
+    form (each key tile decoded once per call), False runs unsplit and
+    unstaged, or a uint8 device tensor (nvfp4_kv_attention_workspace_bytes
+    allows every split, nvfp4_kv_attention_staged_workspace_bytes the staged
+    form as well)."""
     _bf16_dev(q, "q")
     if q.dim() != 3:
         raise ValueError("q must be [H, Tq, D]")
@@ -308,12 +328,11 @@ def nvfp4_kv_attention(q, cache, chunk_len, key_ranges, softmax_scale=None, out=
     H_kv, T = kc.shape[0], kc.shape[1]
     if softmax_scale is None:
         softmax_scale = D ** -0.5
-    rg = [(int(a), int(n)) for a, n in key_ranges]
-    arr = (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
+    rg, arr = _ranges_arr(key_ranges)
     if out is None:
         out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
     lse_t = _lse_out(lse, H, Tq, q.device)
-    ws, ws_bytes = _attn_workspace(workspace, H, Tq, D, q.device)
+    ws, ws_bytes = _attn_workspace(workspace, H, Tq, D, q.device, (H_kv, T, chunk_len, rg))
     rc = lib().nvfp4_kv_attention(
         _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
         _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, T, chunk_len, arr,
@@ -335,12 +354,11 @@ def nvfp4_kv_attention_chunked(q, cache, chunk_len, key_ranges, softmax_scale=No
         raise ValueError("k_codes chunk length differs from chunk_len")
     if softmax_scale is None:
         softmax_scale = D ** -0.5
-    rg = [(int(a), int(n)) for a, n in key_ranges]
-    arr = (ctypes.c_int * max(1, 2 * len(rg)))(*[x for r in rg for x in r])
+    rg, arr = _ranges_arr(key_ranges)
     if out is None:
         out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device=q.device)
     lse_t = _lse_out(lse, H, Tq, q.device)
-    ws, ws_bytes = _attn_workspace(workspace, H, Tq, D, q.device)
+    ws, ws_bytes = _attn_workspace(workspace, H, Tq, D, q.device, (H_kv, nch * L, chunk_len, rg))
     rc = lib().nvfp4_kv_attention_chunked(
         _ptr(q), H, Tq, D, _ptr(kc), _ptr(cache["k_scales"]), _ptr(cache["k_tensor_scale"]), _ptr(cache.get("k_mean")),
         _ptr(cache["v_codes"]), _ptr(cache["v_scales"]), _ptr(cache["v_tensor_scale"]), H_kv, nch * L, chunk_len, arr,
@@ -453,7 +471,9 @@ class KVCache:
         if out is None:
             out = torch.empty(Hq, Tq, D, dtype=torch.bfloat16, device=q.device)
         lse_t = _lse_out(lse, Hq, Tq, q.device)
-        ws, ws_bytes = _attn_workspace(workspace, Hq, Tq, D, q.device)
+        st = self.state
+        keys = (st.heads, st.capacity * st.chunk_len, st.chunk_len, self.key_ranges())
+        ws, ws_bytes = _attn_workspace(workspace, Hq, Tq, D, q.device, keys)
         rc = lib().nvfp4_kv_cache_attention(ctypes.byref(self.state), _ptr(self.storage), self.storage_bytes, layer,
                                             _ptr(q), Hq, Tq, float(softmax_scale), _ptr(out), _ptr(lse_t),
                                             _ptr(ws), ws_bytes, _stream(stream))

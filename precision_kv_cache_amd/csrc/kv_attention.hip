@@ -29,6 +29,14 @@
 // fills the CUs in fewer rounds; each part stores its unnormalized O, its
 // reference maximum and its weight sum, and a small kernel merges the parts
 // per query row in a fixed order.
+//
+// Staged form: when the workspace also holds the decoded image of every key
+// tile (the LDS bytes the decode would write, 35 KB per tile and cache head),
+// a staging kernel decodes each tile once per call, and the attention
+// workgroups copy the images into LDS with direct-to-LDS loads instead of
+// decoding every tile in each of the head's query blocks.  The images hold
+// the same bytes, so the results are bit-identical to the decode-on-load
+// form.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <algorithm>
@@ -82,6 +90,12 @@ struct AttnParams {
   int split_r[kMaxSplit], split_pos[kMaxSplit], split_tiles[kMaxSplit];
   float* part_o;   // [ksplit][H][Tq][D]
   float* part_ml;  // [ksplit][H][Tq][2]
+  // Staged form: img holds the decoded LDS image of tile t of cache head kvh
+  // at (kvh * ntiles + t) * kBuf; split j starts at tile split_t0[j].
+  const uint8_t* img;
+  uint8_t* img_out;  // the same buffer, written by the staging kernel
+  long long ntiles;
+  int split_t0[kMaxSplit];
 };
 
 // Next tile of the key list: [start, start + n), n <= 64, inside one range
@@ -205,6 +219,61 @@ __device__ __forceinline__ float max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Cursor (range, position) at which tile `at` of the key list starts: the
+// walk of next_tile, counted in closed form per chunk piece.
+__device__ bool tile_cursor(const AttnParams& p, long long at, int& cr, int& cpos) {
+  long long t = 0;
+  for (int r = 0; r < p.nr; ++r) {
+    long long pos = p.rstart[r];
+    const long long end = pos + p.rlen[r];
+    while (pos < end) {
+      const long long cend = min(end, (pos / p.L + 1) * (long long)p.L);  // this chunk piece's end
+      const long long nt = (cend - pos + kKT - 1) / kKT;
+      if (at < t + nt) {
+        cr = r;
+        cpos = (int)(pos + (at - t) * kKT);
+        return true;
+      }
+      t += nt;
+      pos = cend;
+    }
+  }
+  return false;
+}
+
+constexpr int kStageTiles = 4;  // tiles per staging workgroup
+
+// Staging kernel: decodes tiles blockIdx.x * kStageTiles .. + kStageTiles - 1
+// of cache head blockIdx.y's key list into their images (load_tile and
+// store_tile, the decode-on-load path, with a global destination).
+__global__ __launch_bounds__(kThreads) void attention_stage_kernel(AttnParams p) {
+  const int kvh = blockIdx.y;
+  const long long t0 = (long long)blockIdx.x * kStageTiles;
+  int r = 0, pos = 0;
+  if (!tile_cursor(p, t0, r, pos)) return;
+  for (int i = 0; i < kStageTiles && t0 + i < p.ntiles; ++i) {
+    int start = 0, n = 0;
+    if (!next_tile(p, r, pos, start, n)) return;
+    TileRegs regs;
+    load_tile(p, kvh, start, n, regs);
+    store_tile(p.img_out + ((size_t)kvh * p.ntiles + t0 + i) * kBuf, regs, p.vg[start / p.L]);
+  }
+}
+
+// Copies the image of tile ti of cache head kvh into LDS buffer `buf` by
+// direct-to-LDS loads: kBuf / 1024 rounds of 64 lanes x 16 bytes, spread
+// over the waves.  The caller waits for them (vmcnt) before its barrier.
+__device__ __forceinline__ void copy_image(const AttnParams& p, int kvh, long long ti, uint8_t* buf) {
+  static_assert(kBuf % 1024 == 0, "the image is whole rounds of 64 x 16 bytes (and 256-byte aligned)");
+  constexpr int kRounds = kBuf / 1024;
+  const uint8_t* src = p.img + ((size_t)kvh * p.ntiles + ti) * kBuf + (threadIdx.x & 63) * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int wi = wave; wi < kRounds; wi += kWaves)
+    __builtin_amdgcn_global_load_lds(src + (size_t)wi * 1024, (__attribute__((address_space(3))) void*)(buf + wi * 1024),
+                                     16, 0, 0);
+}
+
+template <bool STAGED>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
 
@@ -244,10 +313,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   int r = p.split_r[js], pos = p.split_pos[js], left = p.split_tiles[js];
   int t_start = 0, t_n = 0;
   bool have = take_tile(p, r, pos, t_start, t_n, left);
+  long long ti = p.split_t0[js];  // tile index of the current tile (staged form)
   TileRegs regs;
   if (have) {
-    load_tile(p, kvh, t_start, t_n, regs);
-    store_tile(lds, regs, p.vg[t_start / p.L]);
+    if constexpr (STAGED) {
+      copy_image(p, kvh, ti, lds);
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      load_tile(p, kvh, t_start, t_n, regs);
+      store_tile(lds, regs, p.vg[t_start / p.L]);
+    }
   }
   __syncthreads();
   int cur = 0;
@@ -255,7 +330,14 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   while (have) {
     int n_start = 0, n_n = 0;
     const bool nhave = take_tile(p, r, pos, n_start, n_n, left);
-    if (nhave) load_tile(p, kvh, n_start, n_n, regs);
+    if (nhave) {
+      // the next tile's bytes, into the other buffer (last read before the
+      // previous barrier) or into registers for the decode below
+      if constexpr (STAGED)
+        copy_image(p, kvh, ti + 1, lds + (cur ^ 1) * kBuf);
+      else
+        load_tile(p, kvh, n_start, n_n, regs);
+    }
 
     // this tile's chunk: logit factor g_K * sigma and bias sigma * (q . m_c)
     const int c = t_start / p.L;
@@ -378,11 +460,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
       }
     }
 
-    if (nhave) {
+    if constexpr (STAGED)
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next image is in LDS
+    else if (nhave)
       store_tile(lds + (cur ^ 1) * kBuf, regs, p.vg[n_start / p.L]);
-    }
     __syncthreads();
     cur ^= 1;
+    ++ti;
     t_start = n_start;
     t_n = n_n;
     have = nhave;
@@ -480,6 +564,20 @@ static size_t split_bytes(int k, size_t rows) {
   return align_up((size_t)k * rows * kD * 4, 256) + align_up((size_t)k * rows * 8, 256);
 }
 
+// Bytes of the decoded tile images of a key list of ntiles tiles.
+static size_t image_bytes(int H_kv, long long ntiles) { return (size_t)H_kv * (size_t)ntiles * kBuf; }
+
+constexpr long long kMaxPieces = 1 << 16;        // chunk pieces of a key list that splits and staging walk
+constexpr long long kMaxImageTiles = 1LL << 30;  // tiles of a staged key list
+
+// Chunk pieces of the key list (each range cut at chunk edges).
+static long long count_pieces(const AttnParams& p) {
+  long long pieces = 0;
+  for (int r = 0; r < p.nr; ++r)
+    pieces += ((long long)p.rstart[r] + p.rlen[r] - 1) / p.L - p.rstart[r] / p.L + 1;
+  return pieces;
+}
+
 // Key splits per query block: the count (at most kMaxSplit) that minimizes
 // the rounds of the grid over the CUs, per unit of work, when the workspace
 // holds it and every split gets at least 4 tiles.
@@ -562,33 +660,51 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   p.split_r[0] = 0;
   p.split_pos[0] = p.nr > 0 ? p.rstart[0] : 0;
   p.split_tiles[0] = 0x7fffffff;
+  p.split_t0[0] = 0;
   const size_t rows = (size_t)H * Tq;
-  if (workspace && workspace_bytes >= split_bytes(2, rows)) {
-    long long pieces = 0;  // chunk pieces of the key list: bounds the host walk
-    for (int r = 0; r < p.nr; ++r)
-      pieces += ((long long)p.rstart[r] + p.rlen[r] - 1) / chunk_len - p.rstart[r] / chunk_len + 1;
-    if (pieces <= (1 << 16)) {
-      int cr = 0, cpos = 0;
-      const long long ntiles = host_tiles(p, -1, &cr, &cpos);
-      const int k = choose_ksplit(p.hq, ntiles, rows, workspace_bytes);
-      if (k > 1) {
-        p.ksplit = k;
-        for (int j = 0; j < k; ++j) {
-          const long long t0 = ntiles * j / k, t1 = ntiles * (j + 1) / k;
-          host_tiles(p, t0, &p.split_r[j], &p.split_pos[j]);
-          p.split_tiles[j] = (int)(t1 - t0);
-        }
-        p.part_o = static_cast<float*>(workspace);
-        p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align_up((size_t)k * rows * kD * 4, 256));
+  // Key splits and staging need the tile walk on the host (and the staging
+  // kernel repeats it per workgroup), so both are skipped for key lists of
+  // very many chunk pieces.
+  const bool walkable = count_pieces(p) <= kMaxPieces;
+  int cr = 0, cpos = 0;
+  const long long ntiles = walkable ? host_tiles(p, -1, &cr, &cpos) : 0;
+  if (workspace && walkable && workspace_bytes >= split_bytes(2, rows)) {
+    const int k = choose_ksplit(p.hq, ntiles, rows, workspace_bytes);
+    if (k > 1) {
+      p.ksplit = k;
+      for (int j = 0; j < k; ++j) {
+        const long long t0 = ntiles * j / k, t1 = ntiles * (j + 1) / k;
+        host_tiles(p, t0, &p.split_r[j], &p.split_pos[j]);
+        p.split_tiles[j] = (int)(t1 - t0);
+        p.split_t0[j] = (int)t0;
       }
+      p.part_o = static_cast<float*>(workspace);
+      p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)k * rows * kD * 4, 256));
     }
+  }
+  // Staged form when the workspace holds, after the room of every key split,
+  // every tile image (the size nvfp4_kv_attention_staged_workspace_bytes
+  // gives): a smaller workspace keeps the decode on load.
+  bool staged = false;
+  const size_t img_off = split_bytes(kMaxSplit, rows);
+  if (workspace && ntiles > 0 && ntiles <= kMaxImageTiles && H_kv <= 65535 &&
+      img_off + image_bytes(H_kv, ntiles) <= workspace_bytes) {
+    staged = true;
+    p.ntiles = ntiles;
+    p.img_out = static_cast<uint8_t*>(workspace) + img_off;
+    p.img = p.img_out;
   }
   p.total = p.hq * p.ksplit;
   p.per_xcd = (p.total + kXcds - 1) / kXcds;
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
-  attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
+  if (staged) {
+    const unsigned gx = (unsigned)((p.ntiles + kStageTiles - 1) / kStageTiles);
+    attention_stage_kernel<<<dim3(gx, (unsigned)H_kv), dim3(kThreads), 0, s>>>(p);
+    attention_kernel<true><<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
+  } else {
+    attention_kernel<false><<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
+  }
   if (p.ksplit > 1) {
     const long long nb = ((long long)rows + 7) / 8;
     attention_combine_kernel<<<dim3((unsigned)nb), dim3(256), 0, s>>>(p.part_o, p.part_ml, p.ksplit, (long long)rows,
@@ -604,6 +720,30 @@ using namespace nvfp4;
 extern "C" NVFP4KV_API size_t nvfp4_kv_attention_workspace_bytes(int H, int Tq, int D) noexcept {
   if (H < 1 || Tq < 1 || D != kD) return 0;
   return split_bytes(kMaxSplit, (size_t)H * Tq);
+}
+
+extern "C" NVFP4KV_API size_t nvfp4_kv_attention_staged_workspace_bytes(int H, int Tq, int D, int H_kv, int T,
+                                                                       int chunk_len, const int* key_ranges,
+                                                                       int n_ranges) noexcept {
+  if (H < 1 || Tq < 1 || D != kD || H_kv < 1 || T < 0 || chunk_len < 1 || H % H_kv != 0 || T % chunk_len != 0)
+    return 0;
+  if (n_ranges < 0 || n_ranges > NVFP4_ATTN_MAX_RANGES || (n_ranges > 0 && !key_ranges)) return 0;
+  AttnParams p{};
+  p.L = chunk_len;
+  for (int i = 0; i < n_ranges; ++i) {
+    const long long a = key_ranges[2 * i], n = key_ranges[2 * i + 1];
+    if (a < 0 || n < 0 || a + n > T) return 0;
+    if (n == 0) continue;
+    p.rstart[p.nr] = (int)a;
+    p.rlen[p.nr] = (int)n;
+    ++p.nr;
+  }
+  const size_t splits = split_bytes(kMaxSplit, (size_t)H * Tq);
+  if (count_pieces(p) > kMaxPieces) return splits;  // such a key list runs unstaged
+  int cr = 0, cpos = 0;
+  const long long ntiles = host_tiles(p, -1, &cr, &cpos);
+  if (ntiles > kMaxImageTiles || H_kv > 65535) return splits;
+  return splits + image_bytes(H_kv, ntiles);
 }
 
 extern "C" NVFP4KV_API int nvfp4_kv_attention(const uint16_t* q, int H, int Tq, int D, const uint8_t* k_codes,

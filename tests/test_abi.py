@@ -10,6 +10,7 @@ import subprocess
 import pytest
 
 import precision_kv_cache_amd as P
+import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("nvfp4kv.h", "nvfp4kv_diag.h")]
@@ -231,6 +232,44 @@ def test_attention_argument_errors():
     wb = P.nvfp4_kv_attention_workspace_bytes(24, 7040, 128)
     assert wb >= 4 * 24 * 7040 * (128 + 2) * 4
     assert P.nvfp4_kv_attention_workspace_bytes(24, 7040, 64) == 0
+
+
+def _tiles(ranges, L):
+    """Tiles of the attention's key walk: each range cut at chunk edges, each
+    piece in tiles of at most 64 keys."""
+    t = 0
+    for a, n in ranges:
+        pos, end = a, a + n
+        while pos < end:
+            cend = min(end, (pos // L + 1) * L)
+            t += -(-(cend - pos) // 64)
+            pos = cend
+    return t
+
+
+def test_attention_staged_workspace_bytes():
+    """Every split plus one decoded image per (cache head, tile): 64 K rows
+    of 272 bytes and 128 V^T rows of 144 bytes, 35,840 bytes."""
+    img = 64 * 272 + 128 * 144
+    for H, Tq, Hkv, T, L, ranges in [
+        (24, 7040, 24, 56320, 7040, [(0, 56320)]),
+        (24, 7040, 24, 56320, 7040, W.sink_ranges(8)),
+        (4, 300, 2, 640, 128, [(0, 70), (200, 77), (383, 257)]),
+        (3, 17, 1, 512, 64, [(448, 64), (0, 64), (100, 1)]),
+        (2, 5, 2, 256, 128, []),
+        (2, 5, 2, 256, 128, [(5, 0), (7, 3)]),
+    ]:
+        got = P.nvfp4_kv_attention_staged_workspace_bytes(H, Tq, 128, Hkv, T, L, ranges)
+        assert got == P.nvfp4_kv_attention_workspace_bytes(H, Tq, 128) + Hkv * _tiles(ranges, L) * img, ranges
+    assert _tiles([(0, 56320)], 7040) == 880
+    bad = [dict(D=64), dict(Hkv=3), dict(T=650), dict(ranges=[(600, 50)]), dict(ranges=[(-1, 2)]),
+           dict(ranges=[(0, 1)] * 9), dict(L=0), dict(H=0)]
+    for b in bad:
+        a = dict(H=4, Tq=10, D=128, Hkv=2, T=640, L=128, ranges=[(0, 640)])
+        a.update(b)
+        assert P.nvfp4_kv_attention_staged_workspace_bytes(a["H"], a["Tq"], a["D"], a["Hkv"], a["T"], a["L"],
+                                                           a["ranges"]) == 0, b
+    assert P.lib().nvfp4_kv_attention_staged_workspace_bytes(4, 10, 128, 2, 640, 128, None, 1) == 0
 
 
 def _gemm(ac=FAKE, as_=FAKE + (1 << 30), ag=FAKE + (2 << 30), M=64, K=128, wc=FAKE + (3 << 30),

@@ -41,26 +41,31 @@ def _to_gpu(c):
     return {k: (None if c.get(k) is None else torch.from_numpy(np.ascontiguousarray(c[k])).cuda()) for k in keys}
 
 
-def _run_gpu(q_bits, cache, L, ranges, scale=None, split=True):
-    """split: with a workspace (the call may split each query block's keys
-    over several workgroups and merge them), else without one (unsplit)."""
+def _run_gpu(q_bits, cache, L, ranges, scale=None, mode="staged"):
+    """mode: "staged" -- a workspace for every key split and the decoded
+    image of every key tile (each tile decoded once per call); "split" -- a
+    workspace for the splits only (each query block decodes its tiles);
+    "unsplit" -- no workspace."""
     q = W.from_bits(q_bits, "cuda")
     H, Tq, D = q.shape
     out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device="cuda")
     out.view(torch.uint8).fill_(0xFF)          # NaN: an unwritten output cannot pass
-    ws = None
-    if split:
-        ws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(H, Tq, D), dtype=torch.uint8, device="cuda")
+    ws = False
+    if mode != "unsplit":
+        Hkv, T = cache["k_codes"].shape[:2]
+        n = (P.nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, Hkv, T, L, ranges) if mode == "staged"
+             else P.nvfp4_kv_attention_workspace_bytes(H, Tq, D))
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
         ws.fill_(0xFF)                         # garbage on entry
     o, lse = P.nvfp4_kv_attention(q, _to_gpu(cache), L, ranges, softmax_scale=scale, out=out, lse=True,
-                                  workspace=ws if split else False)
+                                  workspace=ws)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _full(q_bits, cache, L, ranges, scale=None, split=True, **kw):
+def _full(q_bits, cache, L, ranges, scale=None, mode="staged", **kw):
     H, Tq, D = q_bits.shape
-    got, got_lse = _run_gpu(q_bits, cache, L, ranges, scale, split)
+    got, got_lse = _run_gpu(q_bits, cache, L, ranges, scale, mode)
     rows = np.arange(H * Tq)
     _check(q_bits, cache, L, ranges, got.reshape(-1, D), got_lse.reshape(-1), rows, scale, **kw)
 
@@ -86,19 +91,37 @@ def test_zero_query_weights_every_listed_key_equally():
     np.testing.assert_allclose(got_lse, np.log(len(keys)), rtol=1e-6)
 
 
-@pytest.mark.parametrize("split", [True, False], ids=["split", "unsplit"])
-@pytest.mark.parametrize("H,Hkv,T,L,Tq,ranges", [
+RANDOM_CASES = [
     (2, 2, 640, 128, 300, [(0, 640)]),                         # 5 chunks, ragged query block
     (4, 2, 640, 128, 256, [(0, 70), (200, 77), (383, 257)]),   # grouped heads, segment edges inside tiles
     (3, 1, 512, 64, 17, [(448, 64), (0, 64), (100, 1)]),       # one cache head, single-key range
     (1, 1, 96, 96, 513, [(0, 96)]),                            # one chunk shorter than two tiles
-])
-def test_random_cache(H, Hkv, T, L, Tq, ranges, split):
-    say("random cache", H, Hkv, T, L, Tq, ranges, "split" if split else "unsplit")
+]
+
+
+def _random_case(H, Hkv, T, L, Tq):
     k, v = W.gaussian_kv(W.KVShape(Hkv, T, 128, L), 22 + T + Tq)
-    cache = _cache(W.bf16_bits(k), W.bf16_bits(v), L)
-    q = W.bf16_bits(W.queries(H, Tq, 128, 31 + Tq))
-    _full(q, cache, L, ranges, split=split)
+    return _cache(W.bf16_bits(k), W.bf16_bits(v), L), W.bf16_bits(W.queries(H, Tq, 128, 31 + Tq))
+
+
+@pytest.mark.parametrize("mode", ["staged", "split", "unsplit"])
+@pytest.mark.parametrize("H,Hkv,T,L,Tq,ranges", RANDOM_CASES)
+def test_random_cache(H, Hkv, T, L, Tq, ranges, mode):
+    say("random cache", H, Hkv, T, L, Tq, ranges, mode)
+    cache, q = _random_case(H, Hkv, T, L, Tq)
+    _full(q, cache, L, ranges, mode=mode)
+
+
+@pytest.mark.parametrize("H,Hkv,T,L,Tq,ranges", RANDOM_CASES)
+def test_staged_equals_decode_on_load(H, Hkv, T, L, Tq, ranges):
+    """The staged form copies into LDS the bytes the per-block decode would
+    write there and splits the keys the same way, so out and lse equal the
+    decode-on-load form's bit for bit."""
+    say("staged vs decode on load", H, Hkv, T, L, Tq, ranges)
+    cache, q = _random_case(H, Hkv, T, L, Tq)
+    a = _run_gpu(q, cache, L, ranges, mode="split")
+    b = _run_gpu(q, cache, L, ranges, mode="staged")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 def test_heavy_tail_cache_and_sharp_softmax():
@@ -122,7 +145,7 @@ def test_no_mean_single_key_and_empty():
     nomean = dict(cache)
     nomean["k_mean"] = None
     _full(q, nomean, L, [(0, T)])
-    _full(q, nomean, L, [(0, T)], split=False)
+    _full(q, nomean, L, [(0, T)], mode="unsplit")
     _full(q, cache, L, [(77, 1)])
     got, got_lse = _run_gpu(q, cache, L, [])
     assert np.all(got == 0) and np.all(np.isneginf(got_lse))
@@ -153,7 +176,10 @@ def test_full_cache_layer_sampled(layout):
     del k, v
     q = W.bf16_bits(W.queries(shape.H, W.ATTN_QUERIES, shape.D, W.SEED_ATTN))
     ranges = [(0, shape.T)] if layout == "all" else W.sink_ranges(shape.n_chunks)
-    got, got_lse = _run_gpu(q, cache, shape.chunk_len, ranges)
+    got, got_lse = _run_gpu(q, cache, shape.chunk_len, ranges)       # staged, as the benchmark runs it
+    ref = _run_gpu(q, cache, shape.chunk_len, ranges, mode="split")   # decode on load
+    assert np.array_equal(got, ref[0]) and np.array_equal(got_lse, ref[1])
+    del ref
     Tq = W.ATTN_QUERIES
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([rng.integers(0, shape.H * Tq, 56), [0, Tq - 1, shape.H * Tq - 1],

@@ -33,7 +33,9 @@ def test_quantize_dequantize_attention_replays():
     # eager reference
     ref = P.nvfp4_kv_smooth_quantize(k, v, s.chunk_len, workspace=ws)
     ref_dk = P.nvfp4_dequantize(ref["k_codes"], ref["k_scales"], ref["k_tensor_scale"], ref["k_mean"], s.chunk_len)
-    aws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(s.H, 300, s.D), dtype=torch.uint8, device="cuda")
+    # room for the staged attention: a staging kernel, then the attention kernels
+    aws = torch.empty(P.nvfp4_kv_attention_staged_workspace_bytes(s.H, 300, s.D, s.H, s.T, s.chunk_len, ranges),
+                      dtype=torch.uint8, device="cuda")
     ref_att, ref_lse = P.nvfp4_kv_attention(q, ref, s.chunk_len, ranges, lse=True, workspace=aws)
     torch.cuda.synchronize()
 

@@ -93,8 +93,8 @@ def test_streamed_chunks(geom):
 
 def test_chunked_attention_matches_head_major():
     """nvfp4_kv_attention_chunked over a chunk-major copy of a cache gives the
-    same bits as nvfp4_kv_attention over the head-major original, split and
-    unsplit."""
+    same bits as nvfp4_kv_attention over the head-major original: staged
+    (the default workspace), split only, and unsplit."""
     H, T, L, D, Tq = 2, 512, 128, 128, 100
     k, v = W.gaussian_kv(W.KVShape(H, T, D, L), 42)
     ref = O.smooth_quantize(W.bf16_bits(k), W.bf16_bits(v), L)
@@ -107,8 +107,9 @@ def test_chunked_attention_matches_head_major():
         cm[key] = torch.from_numpy(np.ascontiguousarray(a.reshape(H, nc, L, -1).transpose(1, 0, 2, 3))).cuda()
     q = W.queries(H, Tq, D, 43, device="cuda")
     ranges = [(300, 200), (0, 37), (129, 1)]
-    for ws in (None, False):  # with key splits where they help, and unsplit
+    split_ws = torch.empty(P.nvfp4_kv_attention_workspace_bytes(H, Tq, D), dtype=torch.uint8, device="cuda")
+    for ws in (None, split_ws, False):  # staged, key splits only, unsplit
         a, la = P.nvfp4_kv_attention(q, hm, L, ranges, lse=True, workspace=ws)
         b, lb = P.nvfp4_kv_attention_chunked(q, cm, L, ranges, lse=True, workspace=ws)
         torch.cuda.synchronize()
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb), ws
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb), type(ws)
