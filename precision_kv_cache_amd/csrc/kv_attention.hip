@@ -241,23 +241,20 @@ __device__ bool tile_cursor(const AttnParams& p, long long at, int& cr, int& cpo
   return false;
 }
 
-constexpr int kStageTiles = 4;  // tiles per staging workgroup
-
-// Staging kernel: decodes tiles blockIdx.x * kStageTiles .. + kStageTiles - 1
-// of cache head blockIdx.y's key list into their images (load_tile and
-// store_tile, the decode-on-load path, with a global destination).
+// Staging kernel: decodes tile blockIdx.x of cache head blockIdx.y's key
+// list into its image (load_tile and store_tile, the decode-on-load path,
+// with a global destination).  One tile per workgroup: 275 us for the
+// 21,120 tiles of a full-cache layer, against 305 us with four per
+// workgroup, 287-322 us with two to eight whose loads are all issued before
+// the first decode, and 305-331 us when the rows' pad bytes are written too.
 __global__ __launch_bounds__(kThreads) void attention_stage_kernel(AttnParams p) {
   const int kvh = blockIdx.y;
-  const long long t0 = (long long)blockIdx.x * kStageTiles;
-  int r = 0, pos = 0;
-  if (!tile_cursor(p, t0, r, pos)) return;
-  for (int i = 0; i < kStageTiles && t0 + i < p.ntiles; ++i) {
-    int start = 0, n = 0;
-    if (!next_tile(p, r, pos, start, n)) return;
-    TileRegs regs;
-    load_tile(p, kvh, start, n, regs);
-    store_tile(p.img_out + ((size_t)kvh * p.ntiles + t0 + i) * kBuf, regs, p.vg[start / p.L]);
-  }
+  const long long ti = blockIdx.x;
+  int r = 0, pos = 0, start = 0, n = 0;
+  if (!tile_cursor(p, ti, r, pos) || !next_tile(p, r, pos, start, n)) return;
+  TileRegs regs;
+  load_tile(p, kvh, start, n, regs);
+  store_tile(p.img_out + ((size_t)kvh * p.ntiles + ti) * kBuf, regs, p.vg[start / p.L]);
 }
 
 // Copies the image of tile ti of cache head kvh into LDS buffer `buf` by
@@ -568,7 +565,11 @@ static size_t split_bytes(int k, size_t rows) {
 static size_t image_bytes(int H_kv, long long ntiles) { return (size_t)H_kv * (size_t)ntiles * kBuf; }
 
 constexpr long long kMaxPieces = 1 << 16;        // chunk pieces of a key list that splits and staging walk
-constexpr long long kMaxImageTiles = 1LL << 30;  // tiles of a staged key list
+// Tiles of a staged key list: the staging grid's work-items (tiles x 512)
+// stay below 2^32, as a launch counts them in 32 bits.
+constexpr long long kMaxImageTiles = (1LL << 32) / kThreads - 1;
+// Workgroups of an attention launch, every split included, for the same reason.
+constexpr long long kMaxAttnGroups = (1LL << 32) / kThreads - kXcds;
 
 // Chunk pieces of the key list (each range cut at chunk edges).
 static long long count_pieces(const AttnParams& p) {
@@ -589,7 +590,7 @@ static int choose_ksplit(int hq, long long ntiles, size_t rows, size_t ws_bytes)
   int best = 1;
   double best_t = 1e30;
   for (int k = 1; k <= kMaxSplit; ++k) {
-    if (k > 1 && (ntiles < 4LL * k || split_bytes(k, rows) > ws_bytes)) break;
+    if (k > 1 && (ntiles < 4LL * k || split_bytes(k, rows) > ws_bytes || (long long)hq * k > kMaxAttnGroups)) break;
     const double rounds = (double)(((long long)hq * k + ncu - 1) / ncu) / k;
     if (rounds < best_t - 1e-9) {
       best_t = rounds;
@@ -653,7 +654,7 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   p.sigma = softmax_scale * 1.4426950408889634f;
   p.nqb = (Tq + kQB - 1) / kQB;
   const long long hq = (long long)H * p.nqb;
-  if (hq > (1LL << 26)) return NVFP4_ERR_SHAPE;
+  if (hq > kMaxAttnGroups) return NVFP4_ERR_SHAPE;
   p.hq = (int)hq;
   // one split: the whole key list from its start, no tile budget
   p.ksplit = 1;
@@ -699,8 +700,7 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   if (staged) {
-    const unsigned gx = (unsigned)((p.ntiles + kStageTiles - 1) / kStageTiles);
-    attention_stage_kernel<<<dim3(gx, (unsigned)H_kv), dim3(kThreads), 0, s>>>(p);
+    attention_stage_kernel<<<dim3((unsigned)p.ntiles, (unsigned)H_kv), dim3(kThreads), 0, s>>>(p);
     attention_kernel<true><<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
   } else {
     attention_kernel<false><<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);

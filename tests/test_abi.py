@@ -270,6 +270,13 @@ def test_attention_staged_workspace_bytes():
         assert P.nvfp4_kv_attention_staged_workspace_bytes(a["H"], a["Tq"], a["D"], a["Hkv"], a["T"], a["L"],
                                                            a["ranges"]) == 0, b
     assert P.lib().nvfp4_kv_attention_staged_workspace_bytes(4, 10, 128, 2, 640, 128, None, 1) == 0
+    # the staging grid (512 work-items per tile) stays below 2^32 work-items: at most 2^23 - 1 tiles,
+    # a longer key list runs unstaged and needs only the split room
+    splits = P.nvfp4_kv_attention_workspace_bytes(1, 1, 128)
+    T = (1 << 29) - 64
+    assert P.nvfp4_kv_attention_staged_workspace_bytes(1, 1, 128, 1, T, T, [(0, T)]) == splits + ((1 << 23) - 1) * img
+    T = 1 << 29
+    assert P.nvfp4_kv_attention_staged_workspace_bytes(1, 1, 128, 1, T, T, [(0, T)]) == splits
 
 
 def _gemm(ac=FAKE, as_=FAKE + (1 << 30), ag=FAKE + (2 << 30), M=64, K=128, wc=FAKE + (3 << 30),
