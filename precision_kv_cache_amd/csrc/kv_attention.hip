@@ -1,5 +1,6 @@
 // kv_attention.hip -- softmax attention of bf16 queries over key ranges of
-// one layer's NVFP4 KV cache, dequantizing the cache on load.  This is the
+// one layer's NVFP4 KV cache, decoding the cache tile by tile into LDS (in
+// each workgroup, or once per call in the staged form below).  This is the
 // consumer of the cache that the LongLive-2.0 summary page builds in its
 // inference pipeline (step 7: smoothed K and V in NVFP4 per chunk) and reads
 // through a global sink, a shot sink and the recent window (step 9).
@@ -30,8 +31,9 @@
 // reference maximum and its weight sum, and a small kernel merges the parts
 // per query row in a fixed order.
 //
-// Staged form: when the workspace also holds the decoded image of every key
-// tile (the LDS bytes the decode would write, 35 KB per tile and cache head),
+// Staged form: when the workspace also holds, after the room of every split,
+// the decoded image of every key tile (the LDS bytes the decode would write,
+// 35 KB per tile and cache head),
 // a staging kernel decodes each tile once per call, and the attention
 // workgroups copy the images into LDS with direct-to-LDS loads instead of
 // decoding every tile in each of the head's query blocks.  The images hold
