@@ -262,9 +262,19 @@ __global__ __launch_bounds__(kThreads) void attention_stage_kernel(AttnParams p)
 // Copies the image of tile ti of cache head kvh into LDS buffer `buf` by
 // direct-to-LDS loads: kBuf / 1024 rounds of 64 lanes x 16 bytes, spread
 // over the waves.  The caller waits for them (vmcnt) before its barrier.
+constexpr int kImageRounds = kBuf / 1024;  // rounds of 64 lanes x 16 bytes per image
+static_assert(kBuf % 1024 == 0, "the image is whole rounds of 64 x 16 bytes (and 256-byte aligned)");
+// Rounds a wave issues per image: kImageRounds / kWaves, one more for the
+// first kImageRounds % kWaves waves.
+constexpr int kRoundsLo = kImageRounds / kWaves;
+static_assert(kRoundsLo + 1 < 16, "the waits below encode these counts in 4 bits");
+
+// s_waitcnt immediate: wait until at most n of this wave's vector-memory
+// operations are outstanding (export and LDS/scalar counters not waited for).
+constexpr int vmcnt_at_most(int n) { return 0x0F70 | n; }
+
 __device__ __forceinline__ void copy_image(const AttnParams& p, int kvh, long long ti, uint8_t* buf) {
-  static_assert(kBuf % 1024 == 0, "the image is whole rounds of 64 x 16 bytes (and 256-byte aligned)");
-  constexpr int kRounds = kBuf / 1024;
+  constexpr int kRounds = kImageRounds;
   const uint8_t* src = p.img + ((size_t)kvh * p.ntiles + ti) * kBuf + (threadIdx.x & 63) * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int wi = wave; wi < kRounds; wi += kWaves)
@@ -274,7 +284,10 @@ __device__ __forceinline__ void copy_image(const AttnParams& p, int kvh, long lo
 
 template <bool STAGED>
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+  // Staged: three image buffers, the copies running two tiles ahead; else two
+  // buffers for the decode of the next tile.
+  constexpr int kBufs = STAGED ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBufs * kBuf];
 
   // Workgroups are dispatched round-robin over the XCDs; give the slots of
   // one XCD consecutive query blocks of the same head so that they share
@@ -314,9 +327,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   bool have = take_tile(p, r, pos, t_start, t_n, left);
   long long ti = p.split_t0[js];  // tile index of the current tile (staged form)
   TileRegs regs;
+  int b_start = 0, b_n = 0;
+  bool hb = false;
   if (have) {
     if constexpr (STAGED) {
       copy_image(p, kvh, ti, lds);
+      hb = take_tile(p, r, pos, b_start, b_n, left);
+      if (hb) copy_image(p, kvh, ti + 1, lds + kBuf);
       __builtin_amdgcn_s_waitcnt(0);
     } else {
       load_tile(p, kvh, t_start, t_n, regs);
@@ -326,16 +343,24 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   __syncthreads();
   int cur = 0;
 
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index
   while (have) {
     int n_start = 0, n_n = 0;
-    const bool nhave = take_tile(p, r, pos, n_start, n_n, left);
-    if (nhave) {
-      // the next tile's bytes, into the other buffer (last read before the
-      // previous barrier) or into registers for the decode below
-      if constexpr (STAGED)
-        copy_image(p, kvh, ti + 1, lds + (cur ^ 1) * kBuf);
-      else
-        load_tile(p, kvh, n_start, n_n, regs);
+    bool nhave = false, issued = false;
+    if constexpr (STAGED) {
+      // tile t + 1 is (or is being) copied; issue the copy of tile t + 2 into
+      // the buffer of tile t - 1, last read before the previous barrier
+      nhave = hb; n_start = b_start; n_n = b_n;
+      int c_start = 0, c_n = 0;
+      const bool hc = hb && take_tile(p, r, pos, c_start, c_n, left);
+      if (hc) {
+        copy_image(p, kvh, ti + 2, lds + (cur == 0 ? 2 : cur - 1) * kBuf);
+        issued = true;
+      }
+      hb = hc; b_start = c_start; b_n = c_n;
+    } else {
+      nhave = take_tile(p, r, pos, n_start, n_n, left);
+      if (nhave) load_tile(p, kvh, n_start, n_n, regs);
     }
 
     // this tile's chunk: logit factor g_K * sigma and bias sigma * (q . m_c)
@@ -459,12 +484,22 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
       }
     }
 
-    if constexpr (STAGED)
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the next image is in LDS
-    else if (nhave)
-      store_tile(lds + (cur ^ 1) * kBuf, regs, p.vg[n_start / p.L]);
-    __syncthreads();
-    cur ^= 1;
+    if constexpr (STAGED) {
+      // this wave's share of tile t + 1 (issued one iteration ago) is in LDS;
+      // this iteration's copies may stay in flight
+      if (!issued)
+        __builtin_amdgcn_s_waitcnt(0);
+      else if (wv < kImageRounds % kWaves)
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kRoundsLo + 1));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kRoundsLo));
+      __builtin_amdgcn_s_barrier();
+      cur = cur == 2 ? 0 : cur + 1;
+    } else {
+      if (nhave) store_tile(lds + (cur ^ 1) * kBuf, regs, p.vg[n_start / p.L]);
+      __syncthreads();
+      cur ^= 1;
+    }
     ++ti;
     t_start = n_start;
     t_n = n_n;
