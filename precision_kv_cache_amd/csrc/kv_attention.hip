@@ -244,24 +244,25 @@ __device__ bool tile_cursor(const AttnParams& p, long long at, int& cr, int& cpo
 }
 
 // Staging kernel: decodes tile blockIdx.x of cache head blockIdx.y's key
-// list into its image (load_tile and store_tile, the decode-on-load path,
-// with a global destination).  One tile per workgroup: 275 us for the
-// 21,120 tiles of a full-cache layer, against 305 us with four per
-// workgroup, 287-322 us with two to eight whose loads are all issued before
-// the first decode, and 305-331 us when the rows' pad bytes are written too.
+// list into LDS exactly as the decode-on-load path does (load_tile,
+// store_tile), then copies the 35 KB image out in whole 16-byte rows per
+// lane, so the workspace receives full cache lines (the pad bytes carry
+// whatever LDS held; nothing reads them).
 __global__ __launch_bounds__(kThreads) void attention_stage_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t img[kBuf];
   const int kvh = blockIdx.y;
   const long long ti = blockIdx.x;
   int r = 0, pos = 0, start = 0, n = 0;
   if (!tile_cursor(p, ti, r, pos) || !next_tile(p, r, pos, start, n)) return;
   TileRegs regs;
   load_tile(p, kvh, start, n, regs);
-  store_tile(p.img_out + ((size_t)kvh * p.ntiles + ti) * kBuf, regs, p.vg[start / p.L]);
+  store_tile(img, regs, p.vg[start / p.L]);
+  __syncthreads();
+  u32x4* dst = reinterpret_cast<u32x4*>(p.img_out + ((size_t)kvh * p.ntiles + ti) * kBuf);
+  const u32x4* src = reinterpret_cast<const u32x4*>(img);
+  for (int i = threadIdx.x; i < kBuf / 16; i += kThreads) dst[i] = src[i];
 }
 
-// Copies the image of tile ti of cache head kvh into LDS buffer `buf` by
-// direct-to-LDS loads: kBuf / 1024 rounds of 64 lanes x 16 bytes, spread
-// over the waves.  The caller waits for them (vmcnt) before its barrier.
 constexpr int kImageRounds = kBuf / 1024;  // rounds of 64 lanes x 16 bytes per image
 static_assert(kBuf % 1024 == 0, "the image is whole rounds of 64 x 16 bytes (and 256-byte aligned)");
 // Rounds a wave issues per image: kImageRounds / kWaves, one more for the

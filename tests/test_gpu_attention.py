@@ -43,9 +43,9 @@ def _to_gpu(c):
 
 def _run_gpu(q_bits, cache, L, ranges, scale=None, mode="staged"):
     """mode: "staged" -- a workspace for every key split and the decoded
-    image of every key tile (each tile decoded once per call); "split" -- a
-    workspace for the splits only (each query block decodes its tiles);
-    "unsplit" -- no workspace."""
+    image of every key tile (each tile decoded once per call); "staged-1" --
+    one byte less (the decode on load); "split" -- a workspace for the splits
+    only (each query block decodes its tiles); "unsplit" -- no workspace."""
     q = W.from_bits(q_bits, "cuda")
     H, Tq, D = q.shape
     out = torch.empty(H, Tq, D, dtype=torch.bfloat16, device="cuda")
@@ -53,8 +53,10 @@ def _run_gpu(q_bits, cache, L, ranges, scale=None, mode="staged"):
     ws = False
     if mode != "unsplit":
         Hkv, T = cache["k_codes"].shape[:2]
-        n = (P.nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, Hkv, T, L, ranges) if mode == "staged"
+        n = (P.nvfp4_kv_attention_staged_workspace_bytes(H, Tq, D, Hkv, T, L, ranges) if mode.startswith("staged")
              else P.nvfp4_kv_attention_workspace_bytes(H, Tq, D))
+        if mode == "staged-1":
+            n -= 1
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
         ws.fill_(0xFF)                         # garbage on entry
     o, lse = P.nvfp4_kv_attention(q, _to_gpu(cache), L, ranges, softmax_scale=scale, out=out, lse=True,
@@ -122,6 +124,9 @@ def test_staged_equals_decode_on_load(H, Hkv, T, L, Tq, ranges):
     a = _run_gpu(q, cache, L, ranges, mode="split")
     b = _run_gpu(q, cache, L, ranges, mode="staged")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # one byte short of the staged size: the decode on load, with the same splits
+    c = _run_gpu(q, cache, L, ranges, mode="staged-1")
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
 
 
 def test_heavy_tail_cache_and_sharp_softmax():
