@@ -265,45 +265,22 @@ __global__ __launch_bounds__(kThreads) void attention_stage_kernel(AttnParams p)
 
 constexpr int kImageRounds = kBuf / 1024;  // rounds of 64 lanes x 16 bytes per image
 static_assert(kBuf % 1024 == 0, "the image is whole rounds of 64 x 16 bytes (and 256-byte aligned)");
-// Rounds a wave issues per image: kImageRounds / kWaves, one more for the
-// first kImageRounds % kWaves waves.
-constexpr int kRoundsLo = kImageRounds / kWaves;
-static_assert(kRoundsLo + 1 < 16, "the waits below encode these counts in 4 bits");
 
-// s_waitcnt immediate: wait until at most n of this wave's vector-memory
-// operations are outstanding (export and LDS/scalar counters not waited for).
-constexpr int vmcnt_at_most(int n) { return 0x0F70 | n; }
-
+// Copies the image of tile ti of cache head kvh into LDS buffer `buf` by
+// direct-to-LDS loads, the rounds spread over the waves.  The caller waits
+// for them (vmcnt) before its barrier.
 __device__ __forceinline__ void copy_image(const AttnParams& p, int kvh, long long ti, uint8_t* buf) {
-  constexpr int kRounds = kImageRounds;
   const uint8_t* src = p.img + ((size_t)kvh * p.ntiles + ti) * kBuf + (threadIdx.x & 63) * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  for (int wi = wave; wi < kRounds; wi += kWaves)
+  for (int wi = wave; wi < kImageRounds; wi += kWaves)
     __builtin_amdgcn_global_load_lds(src + (size_t)wi * 1024, (__attribute__((address_space(3))) void*)(buf + wi * 1024),
                                      16, 0, 0);
 }
 
-template <bool STAGED>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
-  // Staged: three image buffers, the copies running two tiles ahead; else two
-  // buffers for the decode of the next tile.
-  constexpr int kBufs = STAGED ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBufs * kBuf];
+// ---- the per-tile steps of a wave (32 queries), shared by both kernels ----
 
-  // Workgroups are dispatched round-robin over the XCDs; give the slots of
-  // one XCD consecutive query blocks of the same head so that they share
-  // that XCD's L2 for the head's cache.
-  const int w = (int)(blockIdx.x % kXcds) * p.per_xcd + (int)(blockIdx.x / kXcds);
-  if (w >= p.total) return;
-  const int js = w / p.hq, hqi = w % p.hq;  // key split, (head, query block)
-  const int h = hqi / p.nqb, qb = hqi % p.nqb;
-  const int kvh = h / p.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int qw0 = qb * kQB + wave * kQW;
-
-  // Q^T fragments: lane holds query qw0 + 16 nt + l16, dims 32 ks + 8 g .. +7.
-  bf16x8 bq[2][4];
+// Q^T fragments: lane holds query qw0 + 16 nt + l16, dims 32 ks + 8 g .. +7.
+__device__ __forceinline__ void load_queries(const AttnParams& p, int h, int qw0, int l16, int g, bf16x8 (&bq)[2][4]) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int qi = qw0 + 16 * nt + l16;
@@ -315,200 +292,140 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
         bq[nt][ks] = bf16x8{};
     }
   }
+}
 
-  f32x4 o[8][2];
+// A tile of chunk c: logit factor kf = g_K * sigma and, per query, the bias
+// beta = sigma * (q . m_c).
+__device__ __forceinline__ void chunk_factors(const AttnParams& p, int kvh, int c, const bf16x8 (&bq)[2][4], int g,
+                                              float& kf, float (&beta)[2]) {
+  kf = p.kg[c] * p.sigma;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) o[m][0] = o[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float M[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, beta[2] = {0.f, 0.f};
-  float kf = 0.f;
-  int cur_chunk = -1;
+  for (int nt = 0; nt < 2; ++nt) {
+    float part = 0.f;
+    if (p.km) {
+      const float* mc = p.km + ((size_t)c * p.Hkv + kvh) * kD + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float4 m0 = *reinterpret_cast<const float4*>(mc + 32 * ks);
+        const float4 m1 = *reinterpret_cast<const float4*>(mc + 32 * ks + 4);
+        const bf16x8& qv = bq[nt][ks];
+        part = __builtin_fmaf(bf(qv, 0), m0.x, part);
+        part = __builtin_fmaf(bf(qv, 1), m0.y, part);
+        part = __builtin_fmaf(bf(qv, 2), m0.z, part);
+        part = __builtin_fmaf(bf(qv, 3), m0.w, part);
+        part = __builtin_fmaf(bf(qv, 4), m1.x, part);
+        part = __builtin_fmaf(bf(qv, 5), m1.y, part);
+        part = __builtin_fmaf(bf(qv, 6), m1.z, part);
+        part = __builtin_fmaf(bf(qv, 7), m1.w, part);
+      }
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    beta[nt] = part * p.sigma;
+  }
+}
 
-  int r = p.split_r[js], pos = p.split_pos[js], left = p.split_tiles[js];
-  int t_start = 0, t_n = 0;
-  bool have = take_tile(p, r, pos, t_start, t_n, left);
-  long long ti = p.split_t0[js];  // tile index of the current tile (staged form)
-  TileRegs regs;
-  int b_start = 0, b_n = 0;
-  bool hb = false;
-  if (have) {
-    if constexpr (STAGED) {
-      copy_image(p, kvh, ti, lds);
-      hb = take_tile(p, r, pos, b_start, b_n, left);
-      if (hb) copy_image(p, kvh, ti + 1, lds + kBuf);
-      __builtin_amdgcn_s_waitcnt(0);
-    } else {
-      load_tile(p, kvh, t_start, t_n, regs);
-      store_tile(lds, regs, p.vg[t_start / p.L]);
+// S^T = K~ Q^T: s[mt][nt][i] = q . (v S) of key 16 mt + 4 g + i, query 16 nt + l16.
+__device__ __forceinline__ void tile_scores(const uint8_t* kb, const bf16x8 (&bq)[2][4], int l16, int g,
+                                            f32x4 (&s)[4][2]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const bf16x8 a = lds_frag(kb + (16 * mt + l16) * kKRow + 64 * ks + 16 * g);
+      s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[0][ks], s[mt][0], 0, 0, 0);
+      s[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[1][ks], s[mt][1], 0, 0, 0);
     }
   }
-  __syncthreads();
-  int cur = 0;
+}
 
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index
-  while (have) {
-    int n_start = 0, n_n = 0;
-    bool nhave = false, issued = false;
-    if constexpr (STAGED) {
-      // tile t + 1 is (or is being) copied; issue the copy of tile t + 2 into
-      // the buffer of tile t - 1, last read before the previous barrier
-      nhave = hb; n_start = b_start; n_n = b_n;
-      int c_start = 0, c_n = 0;
-      const bool hc = hb && take_tile(p, r, pos, c_start, c_n, left);
-      if (hc) {
-        copy_image(p, kvh, ti + 2, lds + (cur == 0 ? 2 : cur - 1) * kBuf);
-        issued = true;
-      }
-      hb = hc; b_start = c_start; b_n = c_n;
-    } else {
-      nhave = take_tile(p, r, pos, n_start, n_n, left);
-      if (nhave) load_tile(p, kvh, n_start, n_n, regs);
-    }
-
-    // this tile's chunk: logit factor g_K * sigma and bias sigma * (q . m_c)
-    const int c = t_start / p.L;
-    if (c != cur_chunk) {
-      cur_chunk = c;
-      kf = p.kg[c] * p.sigma;
+// Online softmax of a tile of t_n keys, base 2: logit = s * kf + beta (kf >=
+// 0, so the largest s gives the largest logit).  The reference M moves only
+// when a logit exceeds it by more than 8, so the weights stay below 2^8 and
+// the O rescale is rare.  Leaves the weights, rounded to bf16, in pb: the P^T
+// fragments, keys 32 k2 + 8 g + j (j < 4: block 2 k2, j >= 4: block 2 k2 + 1).
+__device__ __forceinline__ void tile_softmax(f32x4 (&s)[4][2], int t_n, float kf, const float (&beta)[2],
+                                             float (&M)[2], float (&lsum)[2], f32x4 (&o)[8][2], bf16x8 (&pb)[2][2],
+                                             int g) {
+  if (t_n < kKT) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float part = 0.f;
-        if (p.km) {
-          const float* mc = p.km + ((size_t)c * p.Hkv + kvh) * kD + 8 * g;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const float4 m0 = *reinterpret_cast<const float4*>(mc + 32 * ks);
-            const float4 m1 = *reinterpret_cast<const float4*>(mc + 32 * ks + 4);
-            const bf16x8& qv = bq[nt][ks];
-            part = __builtin_fmaf(bf(qv, 0), m0.x, part);
-            part = __builtin_fmaf(bf(qv, 1), m0.y, part);
-            part = __builtin_fmaf(bf(qv, 2), m0.z, part);
-            part = __builtin_fmaf(bf(qv, 3), m0.w, part);
-            part = __builtin_fmaf(bf(qv, 4), m1.x, part);
-            part = __builtin_fmaf(bf(qv, 5), m1.y, part);
-            part = __builtin_fmaf(bf(qv, 6), m1.z, part);
-            part = __builtin_fmaf(bf(qv, 7), m1.w, part);
-          }
-        }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        beta[nt] = part * p.sigma;
-      }
-    }
-
-    const uint8_t* kb = lds + cur * kBuf;
-    const uint8_t* vb = kb + kKBytes;
-
-    // S^T = K~ Q^T: s[mt][nt][i] = q . (v S) of key 16 mt + 4 g + i, query 16 nt + l16
-    f32x4 s[4][2];
+      for (int i = 0; i < 4; ++i)
+        if (16 * mt + 4 * g + i >= t_n) s[mt][0][i] = s[mt][1][i] = -INFINITY;
+  }
+  float alpha[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) s[mt][0] = s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 2; ++nt) {
+    float mx = s[0][nt][0];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = lds_frag(kb + (16 * mt + l16) * kKRow + 64 * ks + 16 * g);
-        s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[0][ks], s[mt][0], 0, 0, 0);
-        s[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[1][ks], s[mt][1], 0, 0, 0);
-      }
-    }
-    if (t_n < kKT) {
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
+    mx = max4(mx);
+    const float cand = __builtin_fmaf(mx, kf, beta[nt]);
+    const float mnew = cand > M[nt] + 8.0f ? cand : M[nt];
+    alpha[nt] = __builtin_amdgcn_exp2f(M[nt] - mnew);
+    const float c0 = beta[nt] - mnew;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[mt][nt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][i], kf, c0));
+    if (t_n < kKT) {  // keys past the tile's end weigh 0 (also when kf == 0)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (16 * mt + 4 * g + i >= t_n) s[mt][0][i] = s[mt][1][i] = -INFINITY;
+          if (16 * mt + 4 * g + i >= t_n) s[mt][nt][i] = 0.f;
     }
-
-    // online softmax, base 2: logit = s * kf + beta (kf >= 0, so the largest s
-    // gives the largest logit).  The reference M moves only when a logit
-    // exceeds it by more than 8, so the weights stay below 2^8 and the O
-    // rescale is rare.
-    float alpha[2];
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs += s[mt][nt][i];
+    lsum[nt] = __builtin_fmaf(lsum[nt], alpha[nt], rs);
+    M[nt] = mnew;
+  }
+  if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) o[m][nt] *= alpha[nt];
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float mx = s[0][nt][0];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-      mx = max4(mx);
-      const float cand = __builtin_fmaf(mx, kf, beta[nt]);
-      const float mnew = cand > M[nt] + 8.0f ? cand : M[nt];
-      alpha[nt] = __builtin_amdgcn_exp2f(M[nt] - mnew);
-      const float c0 = beta[nt] - mnew;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[mt][nt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][i], kf, c0));
-      if (t_n < kKT) {  // keys past the tile's end weigh 0 (also when kf == 0)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * mt + 4 * g + i >= t_n) s[mt][nt][i] = 0.f;
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rs += s[mt][nt][i];
-      lsum[nt] = __builtin_fmaf(lsum[nt], alpha[nt], rs);
-      M[nt] = mnew;
+      const f32x4 a = s[2 * k2][nt], b = s[2 * k2 + 1][nt];
+      const u32x4 u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                    pack_bf16x2(b[2], b[3])};
+      pb[k2][nt] = __builtin_bit_cast(bf16x8, u);
     }
-    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[m][nt] *= alpha[nt];
-    }
+}
 
-    // P^T fragments: keys 32 kb + 8 g + j (j < 4: block 2 kb, j >= 4: block 2 kb + 1)
-    bf16x8 pb[2][2];
+// O^T += V~^T P^T
+__device__ __forceinline__ void tile_pv(const uint8_t* vb, const bf16x8 (&pb)[2][2], int l16, int g,
+                                        f32x4 (&o)[8][2]) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+  for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f32x4 a = s[2 * k2][nt], b = s[2 * k2 + 1][nt];
-        const u32x4 u{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                      pack_bf16x2(b[2], b[3])};
-        pb[k2][nt] = __builtin_bit_cast(bf16x8, u);
-      }
-
-    // O^T += V~^T P^T
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const bf16x8 a = lds_frag(vb + (16 * m + l16) * kVRow + 64 * k2 + 16 * g);
-        o[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k2][0], o[m][0], 0, 0, 0);
-        o[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k2][1], o[m][1], 0, 0, 0);
-      }
+    for (int m = 0; m < 8; ++m) {
+      const bf16x8 a = lds_frag(vb + (16 * m + l16) * kVRow + 64 * k2 + 16 * g);
+      o[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k2][0], o[m][0], 0, 0, 0);
+      o[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[k2][1], o[m][1], 0, 0, 0);
     }
-
-    if constexpr (STAGED) {
-      // this wave's share of tile t + 1 (issued one iteration ago) is in LDS;
-      // this iteration's copies may stay in flight
-      if (!issued)
-        __builtin_amdgcn_s_waitcnt(0);
-      else if (wv < kImageRounds % kWaves)
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kRoundsLo + 1));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kRoundsLo));
-      __builtin_amdgcn_s_barrier();
-      cur = cur == 2 ? 0 : cur + 1;
-    } else {
-      if (nhave) store_tile(lds + (cur ^ 1) * kBuf, regs, p.vg[n_start / p.L]);
-      __syncthreads();
-      cur ^= 1;
-    }
-    ++ti;
-    t_start = n_start;
-    t_n = n_n;
-    have = nhave;
   }
+}
 
-  // O = O^T / l, rows of 4 dims per lane; lse = ln 2 * (M + log2 l).  A key
-  // split stores its O, M and l for the combine kernel instead.
+// O = O^T / l, rows of 4 dims per lane; lse = ln 2 * (M + log2 l).  A key
+// split stores its O, M and l for the combine kernel instead.  The lane's
+// indices are recomputed here rather than kept live across the tile loop.
+__device__ __forceinline__ void store_rows(const AttnParams& p, int js, int h, int qb, const f32x4 (&o)[8][2],
+                                           const float (&M)[2], const float (&lsum)[2]) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int qw0 = qb * kQB + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kQW;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     float l = lsum[nt];
@@ -534,6 +451,143 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
     }
     if (p.lse && g == 0) p.lse[(size_t)h * p.Tq + qi] = (M[nt] + __log2f(l)) * 0.69314718055994531f;
   }
+}
+
+// The workgroup's (key split, head, query block).  Workgroups are dispatched
+// round-robin over the XCDs; the slots of one XCD take consecutive query
+// blocks of the same head so that they share that XCD's L2 for the head's
+// cache.
+struct Work {
+  int js, h, kvh, qb;
+};
+__device__ __forceinline__ bool work_of(const AttnParams& p, Work& wk) {
+  const int w = (int)(blockIdx.x % kXcds) * p.per_xcd + (int)(blockIdx.x / kXcds);
+  if (w >= p.total) return false;
+  wk.js = w / p.hq;
+  const int hqi = w % p.hq;
+  wk.h = hqi / p.nqb;
+  wk.qb = hqi % p.nqb;
+  wk.kvh = wk.h / p.group;
+  return true;
+}
+
+// Decode on load: the workgroup decodes each tile into one of two LDS
+// buffers (the next tile's bytes load while the current tile is computed),
+// one barrier per tile.
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+  Work wk;
+  if (!work_of(p, wk)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int qw0 = wk.qb * kQB + wave * kQW;
+  bf16x8 bq[2][4];
+  load_queries(p, wk.h, qw0, l16, g, bq);
+  f32x4 o[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m][0] = o[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, beta[2] = {0.f, 0.f};
+  float kf = 0.f;
+  int cur_chunk = -1;
+
+  int r = p.split_r[wk.js], pos = p.split_pos[wk.js], left = p.split_tiles[wk.js];
+  int t_start = 0, t_n = 0;
+  bool have = take_tile(p, r, pos, t_start, t_n, left);
+  TileRegs regs;
+  if (have) {
+    load_tile(p, wk.kvh, t_start, t_n, regs);
+    store_tile(lds, regs, p.vg[t_start / p.L]);
+  }
+  __syncthreads();
+  int cur = 0;
+  while (have) {
+    int n_start = 0, n_n = 0;
+    const bool nhave = take_tile(p, r, pos, n_start, n_n, left);
+    if (nhave) load_tile(p, wk.kvh, n_start, n_n, regs);
+    const int c = t_start / p.L;
+    if (c != cur_chunk) {
+      cur_chunk = c;
+      chunk_factors(p, wk.kvh, c, bq, g, kf, beta);
+    }
+    const uint8_t* kb = lds + cur * kBuf;
+    f32x4 s[4][2];
+    bf16x8 pb[2][2];
+    tile_scores(kb, bq, l16, g, s);
+    tile_softmax(s, t_n, kf, beta, M, lsum, o, pb, g);
+    tile_pv(kb + kKBytes, pb, l16, g, o);
+    // the next tile into the other buffer, last read before the previous barrier
+    if (nhave) store_tile(lds + (cur ^ 1) * kBuf, regs, p.vg[n_start / p.L]);
+    __syncthreads();
+    cur ^= 1;
+    t_start = n_start;
+    t_n = n_n;
+    have = nhave;
+  }
+  store_rows(p, wk.js, wk.h, wk.qb, o, M, lsum);
+}
+
+// Staged form: four image buffers and one barrier per pair of tiles.  At the
+// barrier before tiles t, t + 1 (t even from the split's first tile) both
+// are in LDS; right after it every wave issues its share of the copies of
+// tiles t + 2, t + 3 into the buffers of tiles t - 2, t - 1 (read before
+// this barrier), then computes t and t + 1 with no barrier between them, so
+// the waves may drift apart within a pair.
+__global__ __launch_bounds__(kThreads) void attention_staged_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kBuf];
+  Work wk;
+  if (!work_of(p, wk)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int qw0 = wk.qb * kQB + wave * kQW;
+  bf16x8 bq[2][4];
+  load_queries(p, wk.h, qw0, l16, g, bq);
+  f32x4 o[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m][0] = o[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, beta[2] = {0.f, 0.f};
+  float kf = 0.f;
+  int cur_chunk = -1;
+
+  int r = p.split_r[wk.js], pos = p.split_pos[wk.js], left = p.split_tiles[wk.js];
+  long long ti = p.split_t0[wk.js];  // tile index of the pair's first tile
+  int c0s = 0, c0n = 0, c1s = 0, c1n = 0;  // the pair's tiles: start, count
+  bool h0 = take_tile(p, r, pos, c0s, c0n, left);
+  bool h1 = h0 && take_tile(p, r, pos, c1s, c1n, left);
+  if (h0) copy_image(p, wk.kvh, ti, lds);
+  if (h1) copy_image(p, wk.kvh, ti + 1, lds + kBuf);
+  int b = 0;  // buffer of the pair's first tile: 0 or 2
+  f32x4 s[4][2];
+  bf16x8 pb[2][2];
+  while (h0) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the pair are in LDS
+    __builtin_amdgcn_s_barrier();
+    int n0s = 0, n0n = 0, n1s = 0, n1n = 0;
+    const bool g0 = h1 && take_tile(p, r, pos, n0s, n0n, left);
+    const bool g1 = g0 && take_tile(p, r, pos, n1s, n1n, left);
+    uint8_t* nb = lds + (b ^ 2) * kBuf;
+    if (g0) copy_image(p, wk.kvh, ti + 2, nb);
+    if (g1) copy_image(p, wk.kvh, ti + 3, nb + kBuf);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && !h1) break;
+      const int ts = k == 0 ? c0s : c1s, tn = k == 0 ? c0n : c1n;
+      const uint8_t* kb = lds + (b + k) * kBuf;
+      const int c = ts / p.L;
+      if (c != cur_chunk) {
+        cur_chunk = c;
+        chunk_factors(p, wk.kvh, c, bq, g, kf, beta);
+      }
+      tile_scores(kb, bq, l16, g, s);
+      tile_softmax(s, tn, kf, beta, M, lsum, o, pb, g);
+      tile_pv(kb + kKBytes, pb, l16, g, o);
+    }
+    c0s = n0s; c0n = n0n; c1s = n1s; c1n = n1n;
+    h0 = g0;
+    h1 = g1;
+    b ^= 2;
+    ti += 2;
+  }
+  store_rows(p, wk.js, wk.h, wk.qb, o, M, lsum);
 }
 
 // Merges the key splits of each query row: M* = max_j M_j, w_j = 2^(M_j - M*)
@@ -739,9 +793,9 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   (void)hipGetLastError();
   if (staged) {
     attention_stage_kernel<<<dim3((unsigned)p.ntiles, (unsigned)H_kv), dim3(kThreads), 0, s>>>(p);
-    attention_kernel<true><<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
+    attention_staged_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
   } else {
-    attention_kernel<false><<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
+    attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
   }
   if (p.ksplit > 1) {
     const long long nb = ((long long)rows + 7) / 8;
