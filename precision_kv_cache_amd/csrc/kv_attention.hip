@@ -33,12 +33,12 @@
 //
 // Staged form: when the workspace also holds, after the room of every split,
 // the decoded image of every key tile (the LDS bytes the decode would write,
-// 35 KB per tile and cache head),
-// a staging kernel decodes each tile once per call, and the attention
-// workgroups copy the images into LDS with direct-to-LDS loads instead of
-// decoding every tile in each of the head's query blocks.  The images hold
-// the same bytes, so the results are bit-identical to the decode-on-load
-// form.
+// 35 KB per tile and cache head), a staging kernel decodes each tile once per
+// call, and the attention workgroups copy the images into LDS with
+// direct-to-LDS loads instead of decoding every tile in each of the head's
+// query blocks: four image buffers, the copies a pair of tiles ahead, one
+// barrier per pair.  The images hold the same bytes and the per-tile steps
+// are shared, so the results are bit-identical to the decode-on-load form.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <algorithm>
