@@ -244,18 +244,61 @@ __device__ bool tile_cursor(const AttnParams& p, long long at, int& cr, int& cpo
 }
 
 // Staging kernel: decodes tile blockIdx.x of cache head blockIdx.y's key
-// list into LDS exactly as the decode-on-load path does (load_tile,
-// store_tile), then copies the 35 KB image out in whole 16-byte rows per
-// lane, so the workspace receives full cache lines (the pad bytes carry
-// whatever LDS held; nothing reads them).
+// list into LDS exactly as the decode-on-load path does (store_tile), then
+// copies the 35 KB image out in whole 16-byte rows per lane, so the workspace
+// receives full cache lines (the pad bytes carry whatever LDS held; nothing
+// reads them).  WIDE: the tile's code rows (64 contiguous bytes per key) and
+// scale rows (8 bytes) are first copied into LDS with 16- and 8-byte loads,
+// and the decode reads its bytes from there; else the decode-on-load path's
+// own narrow loads (load_tile), for caches whose codes are not 16-byte or
+// whose scales are not 8-byte aligned.
+template <bool WIDE>
 __global__ __launch_bounds__(kThreads) void attention_stage_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t img[kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t raw[2][kKT * (kD / 2 + kD / 16)];  // K, V: codes then scales
   const int kvh = blockIdx.y;
   const long long ti = blockIdx.x;
   int r = 0, pos = 0, start = 0, n = 0;
   if (!tile_cursor(p, ti, r, pos) || !next_tile(p, r, pos, start, n)) return;
   TileRegs regs;
-  load_tile(p, kvh, start, n, regs);
+  if constexpr (WIDE) {
+    const int tid = threadIdx.x;
+    const size_t row0 = (size_t)kvh * p.hstride + (size_t)(start / p.L) * p.cstride + start % p.L;
+    constexpr int kCodeRow = kD / 2, kScaleRow = kD / 16, kScales = kKT * kCodeRow;
+    {  // codes: 4 x 16 bytes per key, threads 0-255 for K, 256-511 for V
+      const int op = tid >> 8, ch = tid & 255, kk = ch >> 2;
+      if (kk < n) {
+        const uint8_t* src = (op == 0 ? p.kc : p.vc) + (row0 + kk) * kCodeRow + 16 * (ch & 3);
+        *reinterpret_cast<u32x4*>(raw[op] + 16 * ch) = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+    if (tid < 2 * kKT) {  // scales: 8 bytes per key
+      const int op = tid / kKT, kk = tid % kKT;
+      if (kk < n) {
+        const uint8_t* src = (op == 0 ? p.ks : p.vs) + (row0 + kk) * kScaleRow;
+        *reinterpret_cast<u32x2*>(raw[op] + kScales + 8 * kk) = *reinterpret_cast<const u32x2*>(src);
+      }
+    }
+    __syncthreads();
+    {  // the fields load_tile would read, from LDS (keys past the end: the last key)
+      const int kk = min(tid >> 3, n - 1), b = tid & 7;
+      const uint2 c = *reinterpret_cast<const uint2*>(raw[0] + kk * kCodeRow + 8 * b);
+      regs.k0 = c.x;
+      regs.k1 = c.y;
+      regs.kscale = raw[0][kScales + kk * kScaleRow + b];
+    }
+    {
+      const int a = tid & 15, c = tid >> 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = min(4 * a + i, n - 1);
+        regs.v[i] = *reinterpret_cast<const uint16_t*>(raw[1] + kk * kCodeRow + 2 * c);
+        regs.vscale[i] = raw[1][kScales + kk * kScaleRow + (c >> 2)];
+      }
+    }
+  } else {
+    load_tile(p, kvh, start, n, regs);
+  }
   store_tile(img, regs, p.vg[start / p.L]);
   __syncthreads();
   u32x4* dst = reinterpret_cast<u32x4*>(p.img_out + ((size_t)kvh * p.ntiles + ti) * kBuf);
@@ -792,7 +835,11 @@ static int attention_launch(const uint16_t* q, int H, int Tq, int D, const uint8
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   if (staged) {
-    attention_stage_kernel<<<dim3((unsigned)p.ntiles, (unsigned)H_kv), dim3(kThreads), 0, s>>>(p);
+    const dim3 sg((unsigned)p.ntiles, (unsigned)H_kv);
+    if (aligned(k_codes, 16) && aligned(v_codes, 16) && aligned(k_scales, 8) && aligned(v_scales, 8))
+      attention_stage_kernel<true><<<sg, dim3(kThreads), 0, s>>>(p);
+    else
+      attention_stage_kernel<false><<<sg, dim3(kThreads), 0, s>>>(p);
     attention_staged_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);
   } else {
     attention_kernel<<<dim3(kXcds * p.per_xcd), dim3(kThreads), 0, s>>>(p);

@@ -129,6 +129,39 @@ def test_staged_equals_decode_on_load(H, Hkv, T, L, Tq, ranges):
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
 
 
+def test_staged_narrow_and_wide_loads_agree():
+    """The staging kernel copies a tile's code and scale rows with wide loads
+    when the codes are 16-byte and the scales 8-byte aligned, else it gathers
+    them as the decode on load does: a cache whose V codes sit 2 bytes and K
+    scales 1 byte off such a boundary gives the same bits, and both match the
+    oracle."""
+    H, Hkv, T, L, Tq, ranges = 4, 2, 640, 128, 256, [(0, 70), (200, 77), (383, 257)]
+    say("staged, unaligned cache", H, Hkv, T, L, Tq, ranges)
+    cache, q_bits = _random_case(H, Hkv, T, L, Tq)
+    gc = _to_gpu(cache)
+
+    def shifted(t, off):
+        flat = t.reshape(-1)
+        buf = torch.empty(flat.numel() + off, dtype=torch.uint8, device="cuda")
+        out = buf[off:]
+        out.copy_(flat)
+        return out.view(t.shape)
+
+    mis = dict(gc)
+    mis["v_codes"] = shifted(gc["v_codes"], 2)
+    mis["k_scales"] = shifted(gc["k_scales"], 1)
+    assert mis["v_codes"].data_ptr() % 16 == 2 and mis["k_scales"].data_ptr() % 8 == 1
+    q = W.from_bits(q_bits, "cuda")
+    ws = torch.empty(P.nvfp4_kv_attention_staged_workspace_bytes(H, Tq, 128, Hkv, T, L, ranges),
+                     dtype=torch.uint8, device="cuda")
+    a, la = P.nvfp4_kv_attention(q, gc, L, ranges, lse=True, workspace=ws)
+    b, lb = P.nvfp4_kv_attention(q, mis, L, ranges, lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+    got = a.float().cpu().numpy().astype(np.float64).reshape(-1, 128)
+    _check(q_bits, cache, L, ranges, got, la.cpu().numpy().astype(np.float64).reshape(-1), np.arange(H * Tq))
+
+
 def test_heavy_tail_cache_and_sharp_softmax():
     """Student-t K and V with per-channel scales, and softmax_scale 1 (logits
     ~11x larger than 1/sqrt(D)): weights concentrate on few keys."""
