@@ -98,6 +98,8 @@ RANDOM_CASES = [
     (4, 2, 640, 128, 256, [(0, 70), (200, 77), (383, 257)]),   # grouped heads, segment edges inside tiles
     (3, 1, 512, 64, 17, [(448, 64), (0, 64), (100, 1)]),       # one cache head, single-key range
     (1, 1, 96, 96, 513, [(0, 96)]),                            # one chunk shorter than two tiles
+    (2, 2, 192, 64, 1, [(64, 64)]),                            # one tile, one query
+    (6, 3, 448, 64, 300, [(3, 61), (64, 65), (257, 190)]),     # pieces starting mid-chunk, a one-key piece (6 tiles)
 ]
 
 
