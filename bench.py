@@ -328,11 +328,14 @@ def kv_bench(a, bits):
         torch.cuda.synchronize()
         qev = [(E(), E()) for _ in qc]
         dev_ = [(E(), E()) for _ in dc]
+        sev = [E() for _ in range(steps + 1)]  # step boundaries, for the median and minimum step
         start, stop = E(), E()
         start.record(stream)
+        sev[0].record(stream)
         for i in range(steps):
             last = i == steps - 1
             step(qev if last else None, dev_ if last else None)
+            sev[i + 1].record(stream)
         stop.record(stream)
         torch.cuda.synchronize()
         # every quantize call of the run shares ws: its sticky error word is
@@ -342,7 +345,11 @@ def kv_bench(a, bits):
             print(f"bench.py: a quantize call's bounded wait timed out (error word {err}); "
                   "its outputs are invalid, so no result is reported", flush=True)
             sys.exit(3)
+        per = sorted(sev[i].elapsed_time(sev[i + 1]) for i in range(steps))
         return {"ms_step": start.elapsed_time(stop) / steps,
+                "step_ms": {"median": round(per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] +
+                                                                                   per[steps // 2]), 4),
+                            "min": round(per[0], 4), "max": round(per[-1], 4)},
                 "q_call_ms": sum(e0.elapsed_time(e1) for e0, e1 in qev) / len(qev),
                 "d_call_ms": sum(e0.elapsed_time(e1) for e0, e1 in dev_) / len(dev_),
                 "calls_per_step": len(qc), "out": o, "deq": dq, "err": err}
@@ -401,6 +408,7 @@ def kv_bench(a, bits):
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": r["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
