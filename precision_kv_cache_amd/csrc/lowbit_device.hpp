@@ -55,7 +55,16 @@ __host__ __device__ constexpr uint32_t lowbit_pack_bias(bool hi) {
 // magnitude value (k / 2, or k) is the sum minus 2^23, exactly.  The error
 // needs no sign: y has z's sign (R >= 0) and v S is exact, so
 // |fl(z - sign(z) v S)| = fl(|z| - v S) and the squares agree.
-template <int BITS>
+//
+// CLAMP = false drops the saturation where it can never act: for the
+// candidate that maps the block maximum t below the top magnitude (c = 1.0:
+// c_b at 3 bits, c_a at 2 bits), S = E4M3(t) gives t / S <= 1.0625 for a
+// normal S (RNE to 3 mantissa bits) and t / S < 1.5 for a subnormal one
+// (S = k 2^-9, t in [(k - 1/2) 2^-9, (k + 1/2) 2^-9), ties going to even k),
+// and R = fl(1 / S), so every |y| = fl(|z| R) <= fl(t R) stays below 1.5:
+// 2|y| < 3 rounds to at most 3 = the 3-bit top index, |y| < 1.5 to at most
+// 1 = the 2-bit top.  (S = 0 gives R = 0 and y = 0.)
+template <int BITS, bool CLAMP = true>
 __device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S, float R, uint32_t& lo,
                                                   uint32_t& hi) {
   constexpr float kMagic = 8388608.0f;  // 2^23
@@ -66,7 +75,8 @@ __device__ __forceinline__ float lowbit_candidate(const float (&z)[16], float S,
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float y = z[i] * R;
-    const float t = fminf(BITS == 3 ? __builtin_fmaf(fabsf(y), 2.0f, kMagic) : fabsf(y) + kMagic, kMagic + kTop);
+    const float t0 = BITS == 3 ? __builtin_fmaf(fabsf(y), 2.0f, kMagic) : fabsf(y) + kMagic;
+    const float t = CLAMP ? fminf(t0, kMagic + kTop) : t0;
     const float v = BITS == 3 ? __builtin_fmaf(t, 0.5f, -0.5f * kMagic) : t - kMagic;  // k / 2 or k, exact
     const float e = __builtin_fmaf(-v, S, fabsf(z[i]));
     if (i < 8)
@@ -111,6 +121,12 @@ struct LowBitBlock {
 
 template <int BITS, int MODE>
 __device__ __forceinline__ LowBitBlock lowbit_block16(const float (&z)[16], const float2* tab) {
+  // At 3 bits the candidate whose constant is 1.0 (c_b) cannot saturate
+  // (lowbit_candidate) and skips the clamp: 3-bit quantize 1-5 % faster.  The
+  // same holds for c_a at 2 bits, but there the build without it measured
+  // 0.6 % slower, so both 2-bit candidates keep it.
+  constexpr bool kClampA = BITS == 2 || LowBit<BITS>::ca != 1.0f;
+  constexpr bool kClampB = BITS == 2 || LowBit<BITS>::cb != 1.0f;
   const float t = block_absmax(z);
   // both candidate scales in one conversion: byte 0 = E4M3(t / ca), byte 1 = E4M3(t / cb);
   // the division by 1.5 is the IEEE quotient (correctly rounded division)
@@ -122,19 +138,19 @@ __device__ __forceinline__ LowBitBlock lowbit_block16(const float (&z)[16], cons
   lowbit_signs<BITS>(z, slo, shi);
   if (MODE == kModeFixed6) {
     const float2 c = tab[s & 0xffu];
-    (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
+    (void)lowbit_candidate<BITS, kClampA>(z, c.x, c.y, out.lo, out.hi);
     out.scale = s & 0xffu;
     out.useb = 0;
   } else if (MODE == kModeFixed4) {
     const float2 c = tab[s >> 8];
-    (void)lowbit_candidate<BITS>(z, c.x, c.y, out.lo, out.hi);
+    (void)lowbit_candidate<BITS, kClampB>(z, c.x, c.y, out.lo, out.hi);
     out.scale = s >> 8;
     out.useb = 1;
   } else {
     const float2 c0 = tab[s & 0xffu], c1 = tab[s >> 8];
     uint32_t la, ha, lb, hb;
-    const float ea = lowbit_candidate<BITS>(z, c0.x, c0.y, la, ha);
-    const float eb = lowbit_candidate<BITS>(z, c1.x, c1.y, lb, hb);
+    const float ea = lowbit_candidate<BITS, kClampA>(z, c0.x, c0.y, la, ha);
+    const float eb = lowbit_candidate<BITS, kClampB>(z, c1.x, c1.y, lb, hb);
     const bool useb = eb < ea;
     out.lo = useb ? lb : la;
     out.hi = useb ? hb : ha;

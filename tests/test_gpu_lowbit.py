@@ -149,3 +149,30 @@ def test_degenerate_values(bits, path):
         kb = W.bf16_bits(torch.as_tensor(np.asarray(k, np.float32)).to(torch.bfloat16))
         vb = W.bf16_bits(torch.as_tensor(np.asarray(v, np.float32)).to(torch.bfloat16))
         _run(kb, vb, L, bits, O.MODE_4OVER6, path)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["overlap", "two-pass"])
+@pytest.mark.parametrize("bits", [3, 2])
+@pytest.mark.parametrize("mode", [O.MODE_4OVER6, O.MODE_FIXED6, O.MODE_FIXED4])
+def test_block_maxima_across_the_e4m3_range(bits, mode, path):
+    # Block maxima log-uniform over 2^-22 .. 1 of the unit's largest value, so
+    # that the candidate scales cover E4M3's normal and subnormal values and 0
+    # (where a candidate's elements come closest to, or cross, the top
+    # magnitude); a few elements of each block near its maximum.
+    rng = np.random.default_rng(4242 + 10 * bits + mode)
+    H, T, D, L = 2, 256, 128, 128
+    nb = H * T * D // 16
+
+    def tensor():
+        scale = np.exp2(rng.uniform(-22.0, 0.0, nb))[:, None]
+        x = rng.uniform(-1.0, 1.0, (nb, 16))
+        x[:, 0] = np.sign(x[:, 0]) + (x[:, 0] == 0)  # the block maximum, +-1
+        x[:, 1:4] = np.sign(x[:, 1:4]) * rng.uniform(0.6, 1.0, (nb, 3))
+        x = rng.permuted(x, axis=1) * scale
+        x = x.reshape(H, T, D)
+        x[0, 0, 0] = 1.0  # the unit maximum of every chunk
+        x[0, L, 0] = -1.0
+        return W.bf16_bits(torch.as_tensor(x.astype(np.float32)).to(torch.bfloat16))
+
+    say("lowbit block maxima over the E4M3 range, bits", bits, "mode", mode, path)
+    _run(tensor(), tensor(), L, bits, mode, path)
