@@ -52,18 +52,19 @@ constexpr int kHalves = kD / 8;                       // 16-byte halves per row
 constexpr int kSRowsPerPass = kOvThreads / kHalves;   // 16
 constexpr int kQRowsPerPass = kOvThreads / kNB;       // 32
 constexpr int kSBatch = 4;                            // rows in flight per statistics lane
+constexpr int kSBatchSmall = 8;                       // the same in calls of at most kOvAheadUnits units
 constexpr int kQBatch = 2;                            // rows in flight per quantize lane
 constexpr int kReplicaStride = 32;                    // 64-bit words between ready words (256 B)
 constexpr int kWaves = kOvThreads / 64;
-// K channel sums: each lane adds its rows in fp32 runs of kRunBatches
-// batches (kRunBatches * kSBatch = 8 rows) and folds every run into fp64.  A
+// K channel sums: each lane adds its rows in fp32 runs of kRunRows = 8 rows
+// (8 / SB batches of SB rows) and folds every run into fp64.  A
 // run of n rows has at most n - 1 fp32 roundings, each at most 2^-24 of the
 // run's magnitude sum, so the channel sum is within 7 * 2^-24 * sum |K| of
 // the exact one and the rounded mean within 8 * 2^-24 * max(|m|, mean |K|):
 // inside the 1e-6 acceptance of the mean, at a quarter of the per-element
 // issue cost of fp64 adds (the fp32 -> fp64 convert is a half-rate
 // instruction).
-constexpr int kRunBatches = 2;
+constexpr int kRunRows = 8;
 
 __device__ __forceinline__ unsigned long long load64_agent(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -126,11 +127,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const uint16_t* p, u
 // One lane's 16 bytes of rows r, r + 16, ..., r + 112 of a slab: byte
 // voff + sb + 4096 q for row r + 16 q (voff: the lane's offset, sb: the
 // batch's first row, uniform).  With GUARD, only rows below r1.
-template <bool GUARD>
+template <int SB, bool GUARD>
 __device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t sb, int r, int r1,
-                                           uint4 (&a)[kSBatch]) {
+                                           uint4 (&a)[SB]) {
 #pragma unroll
-  for (int q = 0; q < kSBatch; ++q) {
+  for (int q = 0; q < SB; ++q) {
     if (!GUARD || r + q * kSRowsPerPass < r1) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, sb + q * kSRowsPerPass * kD * 2, 0);
       a[q] = make_uint4(v[0], v[1], v[2], v[3]);
@@ -141,12 +142,12 @@ __device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t rs, uint32_t v
 
 // K statistics of one batch: fp32 channel sums of the batch's rows added to
 // the running fp32 run sums r (a lane folds them into fp64 every
-// kRunBatches batches), channel max and min.
-template <bool GUARD>
-__device__ __forceinline__ void k_stats_batch(const uint4 (&a)[kSBatch], int r, int r1, float (&rs)[8],
+// kRunRows rows), channel max and min.
+template <int SB, bool GUARD>
+__device__ __forceinline__ void k_stats_batch(const uint4 (&a)[SB], int r, int r1, float (&rs)[8],
                                               float (&mx)[8], float (&mn)[8]) {
 #pragma unroll
-  for (int q = 0; q < kSBatch; ++q) {
+  for (int q = 0; q < SB; ++q) {
     if (GUARD && r + q * kSRowsPerPass >= r1) continue;
     const uint32_t w[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
 #pragma unroll
@@ -173,10 +174,10 @@ __device__ __forceinline__ void fold_runs(double (&s)[8], float (&rs)[8]) {
 // V statistics of one batch: the largest magnitude, on the bf16 bit
 // patterns (with the sign cleared, the integer order of two bf16 magnitudes
 // is their numeric order), two values per 16-bit lane of am.
-template <bool GUARD>
-__device__ __forceinline__ void v_stats_batch(const uint4 (&a)[kSBatch], int r, int r1, u16x2& am) {
+template <int SB, bool GUARD>
+__device__ __forceinline__ void v_stats_batch(const uint4 (&a)[SB], int r, int r1, u16x2& am) {
 #pragma unroll
-  for (int q = 0; q < kSBatch; ++q) {
+  for (int q = 0; q < SB; ++q) {
     if (GUARD && r + q * kSRowsPerPass >= r1) continue;
     const uint32_t w[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
 #pragma unroll
@@ -192,7 +193,8 @@ __device__ __forceinline__ void v_stats_batch(const uint4 (&a)[kSBatch], int r, 
 // One (unit, head, tile) statistics task.  Lane t reads the 16-byte half
 // t % 16 (channels 8 (t % 16) ..) of rows r0 + t / 16, + 16, + 32, ...
 // K: fp64 channel sums and channel max / min; V: the largest magnitude.
-template <int MODE, int BITS>
+// SB: rows each lane has in flight.
+template <int MODE, int BITS, int SB>
 __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double* shs, uint32_t* shx, float* shw,
                            unsigned* sh_flag) {
   const int c = u % p.nc, tau = u / p.nc;
@@ -203,7 +205,9 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
   const __amdgpu_buffer_rsrc_t rs = slab_rsrc(p.x[tau] + ((size_t)h * p.T + (size_t)c * p.L) * kD, (uint32_t)p.L * kD * 2);
   const uint32_t voff = (uint32_t)(roff * kD + hc * 8) * 2;
   const size_t tile = ((size_t)c * p.H + h) * p.nst + ts;
-  constexpr int kBatchRows = kSBatch * kSRowsPerPass;
+  constexpr int kBatchRows = SB * kSRowsPerPass;
+  constexpr int kRunBatches = kRunRows / SB;
+  static_assert(kRunBatches * SB == kRunRows, "whole batches per fp32 run");
   const int nfull = (r1 - r0) / kBatchRows;  // whole batches: no per-row guard
   const int rrest = r0 + nfull * kBatchRows;
   uint32_t done = 0;
@@ -215,18 +219,17 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
     for (int i = 0; i < 8; ++i) { s[i] = 0.0; run[i] = 0.0f; mx[i] = -INFINITY; mn[i] = INFINITY; }
     // whole batches unguarded (no per-row branch, so the compiler keeps the
     // running max / min as plain v_max3 / v_min3), then one guarded batch
-    uint4 ld[kSBatch];
+    uint4 ld[SB];
     for (int b = 0; b < nfull; ++b) {
-      load_batch<false>(rs, voff, (uint32_t)(r0 + b * kBatchRows) * kD * 2, 0, 0, ld);
-      k_stats_batch<false>(ld, 0, 0, run, mx, mn);
+      load_batch<SB, false>(rs, voff, (uint32_t)(r0 + b * kBatchRows) * kD * 2, 0, 0, ld);
+      k_stats_batch<SB, false>(ld, 0, 0, run, mx, mn);
       if (b % kRunBatches == kRunBatches - 1) fold_runs(s, run);
     }
-    // the open run holds at most kRunBatches - 1 = 1 batch, so the guarded
-    // batch keeps it within kRunBatches batches
-    static_assert(kRunBatches == 2, "the guarded batch joins the open run");
+    // the open run holds at most kRunBatches - 1 batches, so the guarded
+    // batch keeps it within kRunRows rows
     if (rrest + roff < r1) {
-      load_batch<true>(rs, voff, (uint32_t)rrest * kD * 2, rrest + roff, r1, ld);
-      k_stats_batch<true>(ld, rrest + roff, r1, run, mx, mn);
+      load_batch<SB, true>(rs, voff, (uint32_t)rrest * kD * 2, rrest + roff, r1, ld);
+      k_stats_batch<SB, true>(ld, rrest + roff, r1, run, mx, mn);
     }
     fold_runs(s, run);
     // the 4 rows of a wave (lanes hc, hc + 16, hc + 32, hc + 48), in a fixed order
@@ -263,14 +266,14 @@ __device__ void stats_tile(const OverlapParams& p, int u, int h, int ts, double*
     }
   } else {
     u16x2 am = {0, 0};
-    uint4 ld[kSBatch];
+    uint4 ld[SB];
     for (int b = 0; b < nfull; ++b) {
-      load_batch<false>(rs, voff, (uint32_t)(r0 + b * kBatchRows) * kD * 2, 0, 0, ld);
-      v_stats_batch<false>(ld, 0, 0, am);
+      load_batch<SB, false>(rs, voff, (uint32_t)(r0 + b * kBatchRows) * kD * 2, 0, 0, ld);
+      v_stats_batch<SB, false>(ld, 0, 0, am);
     }
     if (rrest + roff < r1) {
-      load_batch<true>(rs, voff, (uint32_t)rrest * kD * 2, rrest + roff, r1, ld);
-      v_stats_batch<true>(ld, rrest + roff, r1, am);
+      load_batch<SB, true>(rs, voff, (uint32_t)rrest * kD * 2, rrest + roff, r1, ld);
+      v_stats_batch<SB, true>(ld, rrest + roff, r1, am);
     }
     uint32_t amw;
     __builtin_memcpy(&amw, &am, 4);
@@ -466,7 +469,13 @@ __global__ __launch_bounds__(kOvThreads) void kv_overlap_kernel(OverlapParams p)
   __shared__ unsigned sh_tally[4 * kWaves];
   const Tile t = decode(p, blockIdx.x);
   if (t.stats) {
-    stats_tile<MODE, BITS>(p, t.u, t.h, t.t, shs, shx, shw, &sh_flag);
+    // calls of few units have little else to overlap the statistics with:
+    // more rows in flight per lane (4-bit only: the low-bit encode would
+    // lose a wave per SIMD to the extra registers)
+    if (BITS == 4 && p.ahead)
+      stats_tile<MODE, BITS, kSBatchSmall>(p, t.u, t.h, t.t, shs, shx, shw, &sh_flag);
+    else
+      stats_tile<MODE, BITS, kSBatch>(p, t.u, t.h, t.t, shs, shx, shw, &sh_flag);
   } else {
     fill_scale_table(sh_tab);
     quant_tile<MODE, BITS>(p, t.u, t.h, t.t, t.q, sh_mean, shw, &sh_flag, sh_tab, sh_tally);
