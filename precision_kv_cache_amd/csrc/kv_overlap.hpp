@@ -13,7 +13,8 @@ constexpr int kOvStatsRows = 512;    // rows per statistics tile
 constexpr int kOvQuantRows = 256;    // rows per quantize tile
 constexpr int kOvDepth = 3;          // segments between a unit's statistics and its quantization
 // Calls of at most this many (chunk, tensor) units quantize with each row's
-// loads issued one row ahead: they have about one round of quantize tiles,
+// loads issued one row ahead, and (at 4 bits) their statistics tiles keep 8
+// rows per lane in flight instead of 4: they have about one round of tiles,
 // so no other workgroup hides a tile's load latency.  Larger calls keep
 // fewer live registers instead.
 constexpr int kOvAheadUnits = 4;
@@ -39,7 +40,7 @@ struct OverlapParams {
                              // caller's word for the call that has no workspace)
   uint32_t* tally;           // [U * nq][4] per-quantize-tile 4/6 choice counts (when choice)
   int choice;
-  int ahead;  // quantize tiles load each row one row ahead (calls of few units, see kOvAheadUnits)
+  int ahead;  // calls of few units (kOvAheadUnits): rows loaded one ahead, 8-row statistics batches
   int H, T, L, nc, nst, nqt, depth;
   unsigned spin_limit;
 };
