@@ -127,6 +127,8 @@ def test_full_cache_layer_sampled(layer, path):
     (24, 1000, 128, 100),  # 10 chunks; every tile of a chunk ragged
     (3, 77, 128, 7),     # 11 chunks of 7 rows: one tile per (chunk, head)
     (600, 32, 128, 32),  # many heads, one short chunk
+    (2, 200, 128, 100),  # a small call (2 chunks): one guarded 8-row statistics batch per lane
+    (1, 1000, 128, 500),  # a small call: three whole 8-row batches, then a guarded one
     (1, 204800, 128, 204800),  # one head, one 204800-row chunk (400 statistics tiles)
 ])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
